@@ -1,0 +1,195 @@
+"""MI355X-native blockwise absmax k-bit codebook quantization.
+
+Thin Python binding over ``libkbit.so`` (C ABI in ``include/kbit.h``).  Every
+step of the quantize / dequantize paths runs in the library's HIP kernels;
+this module only allocates outputs with torch, checks tensor placement and
+forwards raw device pointers and the current HIP stream.  If the library has
+not been built, the first call raises ``ImportError``: there is no fallback.
+
+Entry points carry the C names (``quantize_kbit_bf16_k4``,
+``dequantize_4bit_nested_fp16``, ...) and a few dtype/K-dispatching
+conveniences (``quantize_kbit``, ``dequantize_kbit``,
+``dequantize_4bit_nested``, ``quantize_act_fwht_k4_bf16``).
+"""
+
+import ctypes as ct
+
+import numpy as np
+
+__all__ = [
+    "KbitError", "lib", "codebook_nf", "codebook_fp4", "codebook_lloyd_max_normal",
+    "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested",
+    "quantize_act_fwht_k4_bf16", "n_words", "n_blocks",
+]
+
+_TORCH_NAME = {"fp32": "float32", "fp16": "float16", "bf16": "bfloat16"}
+
+
+class KbitError(RuntimeError):
+    """A libkbit entry point returned a non-zero status."""
+
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded ctypes library (raises ImportError if it was not built)."""
+    from . import _lib
+    return _lib.lib
+
+
+def _check(fn_name, status):
+    if status != 0:
+        raise KbitError(fn_name, status, lib().kbit_strerror(status).decode())
+
+
+def n_blocks(n, blocksize):
+    return -(-n // blocksize)
+
+
+def n_words(n, K):
+    return -(-n // 32) * K
+
+
+# --------------------------------------------------------------------------
+# codebooks (host)
+# --------------------------------------------------------------------------
+def _host_table(fn_name, size, *args):
+    out = np.zeros(size, dtype=np.float32)
+    _check(fn_name, getattr(lib(), fn_name)(*args, out.ctypes.data_as(ct.c_void_p)))
+    return out
+
+
+def codebook_nf(K):
+    return _host_table("kbit_codebook_nf", 1 << K, K)
+
+
+def codebook_fp4():
+    return _host_table("kbit_codebook_fp4", 16)
+
+
+def codebook_lloyd_max_normal(levels=16):
+    return _host_table("kbit_codebook_lloyd_max_normal", levels, levels)
+
+
+def dynamic_map8():
+    return _host_table("kbit_dynamic_map8", 256)
+
+
+# --------------------------------------------------------------------------
+# device entry points
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_name(t):
+    torch = _torch()
+    for name, tn in _TORCH_NAME.items():
+        if t == getattr(torch, tn):
+            return name
+    raise TypeError(f"unsupported element dtype {t}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ct.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ct.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def quantize_kbit(A, codebook, k, blocksize, absmax=None, packed=None):
+    """Quantize A (fp32/fp16/bf16 CUDA tensor, any shape) -> (packed int32, absmax fp32)."""
+    torch = _torch()
+    t = _dtype_name(A.dtype)
+    n = A.numel()
+    if absmax is None:
+        absmax = torch.empty(n_blocks(n, blocksize), dtype=torch.float32, device=A.device)
+    if packed is None:
+        packed = torch.empty(n_words(n, k), dtype=torch.int32, device=A.device)
+    name = f"quantize_kbit_{t}_k{k}"
+    fn = getattr(lib(), name)
+    _check(name, fn(_ptr(codebook), _ptr(A), _ptr(absmax), _ptr(packed), n, blocksize, _stream(A.device)))
+    return packed, absmax
+
+
+def dequantize_kbit(packed, codebook, absmax, k, n, dtype, blocksize, out=None):
+    """Dequantize bit-plane words -> tensor of n elements of ``dtype``."""
+    torch = _torch()
+    t = _dtype_name(dtype)
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=packed.device)
+    name = f"dequantize_kbit_{t}_k{k}"
+    fn = getattr(lib(), name)
+    _check(name, fn(_ptr(packed), _ptr(codebook), _ptr(absmax), _ptr(out), n, blocksize, _stream(packed.device)))
+    return out
+
+
+def dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offset, n, dtype, blocksize,
+                           out=None):
+    """Nested 4-bit dequantize with the scale rebuild fused into the decode."""
+    torch = _torch()
+    t = _dtype_name(dtype)
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=packed.device)
+    name = f"dequantize_4bit_nested_{t}"
+    fn = getattr(lib(), name)
+    _check(name, fn(_ptr(packed), _ptr(codebook16), _ptr(absmax_code), _ptr(qmap2), _ptr(absmax2),
+                    ct.c_float(float(offset)), _ptr(out), n, blocksize, _stream(packed.device)))
+    return out
+
+
+def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=None):
+    """Token norm + sign flip + FWHT + Lloyd-Max assignment of bf16 [rows, 4096]."""
+    torch = _torch()
+    if X.dtype != torch.bfloat16 or X.dim() != 2:
+        raise TypeError("X must be a 2-D bfloat16 tensor")
+    rows, d = X.shape
+    if row_norm is None:
+        row_norm = torch.empty(rows, dtype=torch.float32, device=X.device)
+    if packed is None:
+        packed = torch.empty(n_words(rows * d, 4), dtype=torch.int32, device=X.device)
+    name = "quantize_act_fwht_k4_bf16"
+    _check(name, lib().quantize_act_fwht_k4_bf16(_ptr(X), rows, d, _ptr(sign_bits), _ptr(codebook16),
+                                                  _ptr(row_norm), _ptr(packed), _stream(X.device)))
+    return packed, row_norm
+
+
+def _make_named(fn_name, generic, **fixed):
+    def f(*args, **kw):
+        kw.update(fixed)
+        return generic(*args, **kw)
+    f.__name__ = fn_name
+    f.__doc__ = f"{generic.__doc__} (fixed: {fixed})"
+    return f
+
+
+def _install_named():
+    torch_dt = lambda t: getattr(_torch(), _TORCH_NAME[t])  # noqa: E731
+    g = globals()
+    for t in _TORCH_NAME:
+        for k in (2, 3, 4, 5):
+            g[f"quantize_kbit_{t}_k{k}"] = _make_named(
+                f"quantize_kbit_{t}_k{k}", lambda A, codebook, blocksize, _k=k, **kw:
+                quantize_kbit(A, codebook, _k, blocksize, **kw))
+            g[f"dequantize_kbit_{t}_k{k}"] = _make_named(
+                f"dequantize_kbit_{t}_k{k}", lambda packed, codebook, absmax, n, blocksize, _k=k, _t=t, **kw:
+                dequantize_kbit(packed, codebook, absmax, _k, n, torch_dt(_t), blocksize, **kw))
+        g[f"dequantize_4bit_nested_{t}"] = _make_named(
+            f"dequantize_4bit_nested_{t}",
+            lambda packed, codebook16, absmax_code, qmap2, absmax2, offset, n, blocksize, _t=t, **kw:
+            dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offset, n,
+                                   torch_dt(_t), blocksize, **kw))
+
+
+_install_named()

@@ -1,0 +1,57 @@
+"""ctypes loader for libkbit.so and signatures of every exported symbol.
+
+Argument marshalling only.  If the library is missing the import of this
+module raises, so no caller can silently fall back to another path.
+"""
+
+import ctypes as ct
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkbit.so")
+
+DTYPES = ("fp32", "fp16", "bf16")
+KS = (2, 3, 4, 5)
+
+_p = ct.c_void_p
+_i64 = ct.c_int64
+_i32 = ct.c_int32
+_f32 = ct.c_float
+
+
+def _signatures():
+    """(name, argtypes) for every C entry point declared in include/kbit.h."""
+    sig = [
+        ("kbit_strerror", [ct.c_int]),
+        ("kbit_abi_version", []),
+        ("kbit_codebook_nf", [ct.c_int, _p]),
+        ("kbit_codebook_fp4", [_p]),
+        ("kbit_codebook_lloyd_max_normal", [ct.c_int, _p]),
+        ("kbit_dynamic_map8", [_p]),
+        ("quantize_act_fwht_k4_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p]),
+    ]
+    for t in DTYPES:
+        for k in KS:
+            sig.append((f"quantize_kbit_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
+            sig.append((f"dequantize_kbit_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
+        sig.append((f"dequantize_4bit_nested_{t}", [_p, _p, _p, _p, _p, _f32, _p, _i64, _i32, _p]))
+    return sig
+
+
+SIGNATURES = _signatures()
+
+
+def load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(
+            f"libkbit.so not found at {path}; build it with "
+            "`python -m blockwise_bit_codebook_amd.build` (hipcc, gfx950)")
+    lib = ct.CDLL(path)
+    for name, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ct.c_char_p if name == "kbit_strerror" else ct.c_int
+    return lib
+
+
+lib = load()

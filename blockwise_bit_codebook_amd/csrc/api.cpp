@@ -1,0 +1,168 @@
+// C ABI of libkbit.so: argument validation, device checks and dispatch to
+// the HIP launchers.  Every entry point validates before it launches and
+// reports errors as kbit_status codes; nothing aborts, allocates or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "kbit.h"
+#include "kbit_internal.h"
+
+namespace kbit {
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kMaxDevices = 64;
+
+// Per-device CU count; 0 = not probed, -1 = not a gfx950 device.
+std::atomic<int> g_cus[kMaxDevices];
+
+int probe_device(int dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return -1;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return -1;
+    return prop.multiProcessorCount > 0 ? prop.multiProcessorCount : -1;
+}
+
+// CU count of the current device, or a negative value if it is unusable.
+int current_device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        v = probe_device(dev);
+        g_cus[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int log2_block(int32_t blocksize) {
+    if (blocksize < 32 || blocksize > 4096 || (blocksize & (blocksize - 1)) != 0) return -1;
+    int l = 0;
+    while ((1 << l) < blocksize) ++l;
+    return l;
+}
+
+int map_launch(int hip_status) { return hip_status == 0 ? KBIT_OK : KBIT_ELAUNCH; }
+
+int do_quantize(Dtype t, int K, const float* codebook, const void* A, float* absmax, uint32_t* packed,
+                int64_t n, int32_t blocksize, void* stream) {
+    const int l2b = log2_block(blocksize);
+    if (l2b < 0) return KBIT_EBLOCK;
+    if (n < 0 || n > kMaxElems) return KBIT_EINVAL;
+    if (n == 0) return KBIT_OK;
+    if (!codebook || !A || !absmax || !packed) return KBIT_EINVAL;
+    if (!aligned(A, 16) || !aligned(codebook, 4) || !aligned(absmax, 4) || !aligned(packed, 4))
+        return KBIT_EALIGN;
+    if (current_device_cus() <= 0) return KBIT_EDEVICE;
+    return map_launch(launch_quantize(t, K, codebook, A, absmax, packed, n, l2b, stream));
+}
+
+int do_dequantize(Dtype t, int K, const uint32_t* packed, const float* codebook, const float* absmax,
+                  void* out, int64_t n, int32_t blocksize, void* stream) {
+    const int l2b = log2_block(blocksize);
+    if (l2b < 0) return KBIT_EBLOCK;
+    if (n < 0 || n > kMaxElems) return KBIT_EINVAL;
+    if (n == 0) return KBIT_OK;
+    if (!packed || !codebook || !absmax || !out) return KBIT_EINVAL;
+    if (!aligned(out, 16) || !aligned(codebook, 4) || !aligned(absmax, 4) || !aligned(packed, 4))
+        return KBIT_EALIGN;
+    if (current_device_cus() <= 0) return KBIT_EDEVICE;
+    return map_launch(launch_dequantize(t, K, packed, codebook, absmax, out, n, l2b, stream));
+}
+
+int do_nested(Dtype t, const uint32_t* packed, const float* codebook16, const uint8_t* code,
+              const float* qmap2, const float* absmax2, float offset, void* out, int64_t n,
+              int32_t blocksize, void* stream) {
+    const int l2b = log2_block(blocksize);
+    if (l2b < 0) return KBIT_EBLOCK;
+    if (n < 0 || n > kMaxElems) return KBIT_EINVAL;
+    if (n == 0) return KBIT_OK;
+    if (!packed || !codebook16 || !code || !qmap2 || !absmax2 || !out) return KBIT_EINVAL;
+    if (!aligned(out, 16) || !aligned(codebook16, 4) || !aligned(qmap2, 4) || !aligned(absmax2, 4) ||
+        !aligned(packed, 4))
+        return KBIT_EALIGN;
+    if (current_device_cus() <= 0) return KBIT_EDEVICE;
+    return map_launch(
+        launch_dequantize_nested(t, packed, codebook16, code, qmap2, absmax2, offset, out, n, l2b, stream));
+}
+
+}  // namespace
+
+int device_cu_count() {
+    const int v = current_device_cus();
+    return v > 0 ? v : 1;
+}
+
+}  // namespace kbit
+
+using kbit::Dtype;
+
+extern "C" {
+
+const char* kbit_strerror(int status) {
+    switch (status) {
+        case KBIT_OK: return "ok";
+        case KBIT_EINVAL: return "invalid argument (null pointer, bad size, K or d)";
+        case KBIT_EBLOCK: return "blocksize must be a power of two in [32, 4096]";
+        case KBIT_EALIGN: return "misaligned pointer (element arrays need 16 bytes, others 4)";
+        case KBIT_ELAUNCH: return "kernel launch failed";
+        case KBIT_EDEVICE: return "current device is not a usable gfx950 GPU";
+        default: return "unknown status";
+    }
+}
+
+int kbit_abi_version(void) { return 1; }
+
+#define KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, K)                                                   \
+    int quantize_kbit_##TNAME##_k##K(const float* codebook, const CTYPE* A, float* absmax,          \
+                                     uint32_t* packed, int64_t n, int32_t blocksize, void* stream) { \
+        return kbit::do_quantize(DT, K, codebook, A, absmax, packed, n, blocksize, stream);         \
+    }
+#define KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, K)                                                 \
+    int dequantize_kbit_##TNAME##_k##K(const uint32_t* packed, const float* codebook,               \
+                                       const float* absmax, CTYPE* out, int64_t n,                  \
+                                       int32_t blocksize, void* stream) {                           \
+        return kbit::do_dequantize(DT, K, packed, codebook, absmax, out, n, blocksize, stream);     \
+    }
+#define KBIT_DEFINE_ALL_K(TNAME, CTYPE, DT)                                                         \
+    KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 2) KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 3)             \
+    KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 4) KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 5)             \
+    KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 2) KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 3)         \
+    KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 4) KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 5)
+
+KBIT_DEFINE_ALL_K(fp32, float, Dtype::fp32)
+KBIT_DEFINE_ALL_K(fp16, uint16_t, Dtype::fp16)
+KBIT_DEFINE_ALL_K(bf16, uint16_t, Dtype::bf16)
+
+#define KBIT_DEFINE_NESTED(TNAME, CTYPE, DT)                                                          \
+    int dequantize_4bit_nested_##TNAME(const uint32_t* packed, const float* codebook16,               \
+                                       const uint8_t* absmax_code, const float* qmap2,                \
+                                       const float* absmax2, float offset, CTYPE* out, int64_t n,     \
+                                       int32_t blocksize, void* stream) {                             \
+        return kbit::do_nested(DT, packed, codebook16, absmax_code, qmap2, absmax2, offset, out, n,   \
+                               blocksize, stream);                                                    \
+    }
+KBIT_DEFINE_NESTED(fp32, float, Dtype::fp32)
+KBIT_DEFINE_NESTED(fp16, uint16_t, Dtype::fp16)
+KBIT_DEFINE_NESTED(bf16, uint16_t, Dtype::bf16)
+
+int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const uint32_t* sign_bits,
+                              const float* codebook16, float* row_norm, uint32_t* packed, void* stream) {
+    if (d != 4096) return KBIT_EINVAL;
+    if (rows < 0 || rows > (kbit::kMaxElems >> 12)) return KBIT_EINVAL;
+    if (rows == 0) return KBIT_OK;
+    if (!X || !sign_bits || !codebook16 || !row_norm || !packed) return KBIT_EINVAL;
+    if (!kbit::aligned(X, 16) || !kbit::aligned(sign_bits, 4) || !kbit::aligned(codebook16, 4) ||
+        !kbit::aligned(row_norm, 4) || !kbit::aligned(packed, 4))
+        return KBIT_EALIGN;
+    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
+    return kbit::map_launch(kbit::launch_act_fwht(X, rows, d, sign_bits, codebook16, row_norm, packed, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+// Device helpers shared by the gfx950 kernels of libkbit.
+//
+// Wave64 cross-lane primitives (DPP within a 16-lane row, bpermute across
+// rows), the byte transpose inside a quad of lanes that turns per-lane plane
+// bytes into bit-plane words, and element load/store traits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kbit {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWave * kWavesPerGroup;
+constexpr int kElemsPerLane = 8;                        // one byte of each plane word
+constexpr int kWaveTile = kWave * kElemsPerLane;        // 512 elements = 16 groups of 32
+constexpr int kGroup = 32;
+
+// DPP controls (row = 16 lanes).
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppQuadBcast0 = 0x00;    // quad_perm [0,0,0,0]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i inside each half row
+constexpr int kDppMirror = 0x140;       // lane i <-> 15-i inside each row
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) {
+    const int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
+    const int lane = __lane_id();
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, static_cast<int>(v)));
+}
+
+// Max over aligned runs of `lanes` consecutive lanes (lanes = 4..64, power
+// of two); every lane of the run ends with the run's maximum.  `lanes` is
+// uniform across the wave.
+__device__ __forceinline__ float run_max(float m, int lanes) {
+    m = fmaxf(m, dpp_f32<kDppXor1>(m));
+    m = fmaxf(m, dpp_f32<kDppXor2>(m));
+    if (lanes >= 8) m = fmaxf(m, dpp_f32<kDppHalfMirror>(m));
+    if (lanes >= 16) m = fmaxf(m, dpp_f32<kDppMirror>(m));
+    if (lanes >= 32) m = fmaxf(m, shfl_xor_f32(m, 16));
+    if (lanes >= 64) m = fmaxf(m, shfl_xor_f32(m, 32));
+    return m;
+}
+
+// 4x4 byte transpose inside each quad of lanes: on return lane l holds
+// byte l of the inputs of lanes 0..3 (lane i's byte in byte position i).
+// v_perm_b32 picks bytes 0-3 from its second source and 4-7 from its first.
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t v, int lane) {
+    uint32_t p = dpp_u32<kDppXor1>(v);
+    v = __builtin_amdgcn_perm(p, v, (lane & 1) ? 0x03070105u : 0x06020400u);
+    p = dpp_u32<kDppXor2>(v);
+    v = __builtin_amdgcn_perm(p, v, (lane & 2) ? 0x03020706u : 0x05040100u);
+    return v;
+}
+
+// Bit b (b < 4) of v moved to bit 8*b: the plane bytes of one element.
+__host__ __device__ __forceinline__ uint32_t spread4(uint32_t v) {
+    return (v & 1u) | ((v & 2u) << 7) | ((v & 4u) << 14) | ((v & 8u) << 21);
+}
+
+__device__ __forceinline__ uint32_t delta_swap(uint32_t x, uint32_t m, int d) {
+    uint32_t t = (x ^ (x >> d)) & m;
+    return x ^ t ^ (t << d);
+}
+
+// Plane bytes -> nibbles: input byte j bit s (plane j of element s) becomes
+// output bit 4*s + j, i.e. nibble s is the 4-bit index of element s.  The
+// bit index (j1 j0 s2 s1 s0) is rotated to (s2 s1 s0 j1 j0) by four swaps of
+// index bits: (4,2), (3,1), (2,0), (1,0).
+__device__ __forceinline__ uint32_t planes_to_nibbles(uint32_t p) {
+    p = delta_swap(p, 0x0000F0F0u, 12);
+    p = delta_swap(p, 0x00CC00CCu, 6);
+    p = delta_swap(p, 0x0A0A0A0Au, 3);
+    p = delta_swap(p, 0x22222222u, 1);
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// Element types.  Each trait loads the 8 consecutive elements of one lane
+// (16 bytes for 16-bit types, 32 bytes for fp32) widened exactly to float,
+// and stores 8 floats narrowed with round-to-nearest-even.
+// ---------------------------------------------------------------------------
+typedef float float8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+struct Fp32 {
+    using storage = float;
+    static constexpr int kBytes = 4;
+    __device__ static void load8(const storage* p, float* x) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
+        x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+        x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+        x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+        x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+    }
+    __device__ static float load1(const storage* p) { return *p; }
+    __device__ static void store8(storage* p, const float* v) {
+        uint4 a, b;
+        a.x = __float_as_uint(v[0]); a.y = __float_as_uint(v[1]);
+        a.z = __float_as_uint(v[2]); a.w = __float_as_uint(v[3]);
+        b.x = __float_as_uint(v[4]); b.y = __float_as_uint(v[5]);
+        b.z = __float_as_uint(v[6]); b.w = __float_as_uint(v[7]);
+        *reinterpret_cast<uint4*>(p) = a;
+        *reinterpret_cast<uint4*>(p + 4) = b;
+    }
+    __device__ static void store1(storage* p, float v) { *p = v; }
+};
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    bf16x2 h = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    f16x2 h = __builtin_convertvector(f, f16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+struct Bf16 {
+    using storage = uint16_t;
+    static constexpr int kBytes = 2;
+    __device__ static void load8(const storage* p, float* x) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+    __device__ static float load1(const storage* p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
+    __device__ static void store8(storage* p, const float* v) {
+        uint4 a;
+        a.x = pack_bf16x2(v[0], v[1]); a.y = pack_bf16x2(v[2], v[3]);
+        a.z = pack_bf16x2(v[4], v[5]); a.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(p) = a;
+    }
+    __device__ static void store1(storage* p, float v) {
+        *p = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+    }
+};
+
+struct Fp16 {
+    using storage = uint16_t;
+    static constexpr int kBytes = 2;
+    __device__ static float h2f(uint32_t bits16) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+    }
+    __device__ static void load8(const storage* p, float* x) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = h2f(w[i] & 0xFFFFu);
+            x[2 * i + 1] = h2f(w[i] >> 16);
+        }
+    }
+    __device__ static float load1(const storage* p) { return h2f(*p); }
+    __device__ static void store8(storage* p, const float* v) {
+        uint4 a;
+        a.x = pack_f16x2(v[0], v[1]); a.y = pack_f16x2(v[2], v[3]);
+        a.z = pack_f16x2(v[4], v[5]); a.w = pack_f16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(p) = a;
+    }
+    __device__ static void store1(storage* p, float v) {
+        *p = static_cast<uint16_t>(pack_f16x2(v, 0.0f) & 0xFFFFu);
+    }
+};
+
+}  // namespace kbit

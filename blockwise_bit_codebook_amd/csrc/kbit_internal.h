@@ -1,0 +1,30 @@
+// Internal launcher interface between the C ABI (api.cpp) and the HIP
+// translation units.  No HIP types cross this boundary.
+#pragma once
+
+#include <stdint.h>
+
+namespace kbit {
+
+enum class Dtype : int { fp32 = 0, fp16 = 1, bf16 = 2 };
+
+// Each launcher enqueues its kernel on `stream` and returns 0, or the HIP
+// error code of a failed launch.  Arguments are already validated.
+int launch_quantize(Dtype t, int K, const float* codebook, const void* A, float* absmax,
+                    uint32_t* packed, int64_t n, int log2B, void* stream);
+
+int launch_dequantize(Dtype t, int K, const uint32_t* packed, const float* codebook,
+                      const float* absmax, void* out, int64_t n, int log2B, void* stream);
+
+int launch_dequantize_nested(Dtype t, const uint32_t* packed, const float* codebook16,
+                             const uint8_t* code, const float* qmap2, const float* absmax2,
+                             float offset, void* out, int64_t n, int log2B, void* stream);
+
+int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
+                    const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
+
+// Number of workgroups that fill the current device for a kernel whose
+// per-CU residency is `blocks_per_cu`.  Returns 0 if no device is usable.
+int device_cu_count();
+
+}  // namespace kbit

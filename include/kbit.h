@@ -1,0 +1,200 @@
+/*
+ * kbit.h -- C ABI of libkbit.so: blockwise absmax k-bit codebook
+ * quantization and dequantization on AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (web pages, cited by title and section):
+ *   [QLORA-2] bitsandbytes "compare main...QLORA-2" patch series:
+ *             PATCH 001 "Add k-bit quantization kernels (K=2-5, blocksize=32)"
+ *             (csrc/kernels.cu kQuantizeBlockwise_kbit / kDequantizeBlockwise_kbit,
+ *             csrc/pythonInterface.cpp exports, tests/test_kbit_quantization.py
+ *             reference functions); PATCH 003 (Python API quantize_kbit /
+ *             dequantize_kbit, create_normal_float_codebook).
+ *   [PR2051]  bitsandbytes pull request 2051 "Fuse nested 4-bit scale
+ *             reconstruction on SM103": Summary, Implementation.
+ *   [ORBIT]   orbitquant 0.2.2 -> 0.3.0 package diff: README (W4A4 fast path),
+ *             native-kernels CARD.md (quantize_activations_packed_w4),
+ *             docs methodology audit (epsilon guard, Lloyd-Max codebook).
+ *
+ * Conventions for every entry point
+ *   - Return value: KBIT_OK (0) or a negative kbit_status.  Arguments are
+ *     validated before anything is launched; on error nothing is launched and
+ *     no memory is touched.  A launch failure is reported as KBIT_ELAUNCH.
+ *     Nothing aborts the process.
+ *   - Device pointers are plain device addresses (e.g. torch data_ptr()).
+ *     The caller owns and allocates every buffer with exact sizes; the
+ *     library allocates, frees and keeps no device memory and never
+ *     synchronises.  Inputs are read-only and left unmodified.
+ *   - stream: a hipStream_t cast to void*; NULL means the null stream.  Work
+ *     is enqueued asynchronously on that stream.
+ *   - n == 0 is a no-op returning KBIT_OK (null pointers are then allowed).
+ *   - Element types: fp32 = float; fp16 = IEEE binary16 and bf16 = bfloat16,
+ *     both passed as uint16_t bit patterns.
+ *   - blocksize B: a power of two in [32, 4096].  Block b holds elements
+ *     [b*B, (b+1)*B) of the flattened tensor; the last block may be short.
+ *   - Bit-plane layout (the persisted format, [QLORA-2] PATCH 001
+ *     pack_kbit_ref and the ballot packing of kQuantizeBlockwise_kbit): for
+ *     every group g of 32 consecutive elements there are K uint32 words;
+ *     bit t of word g*K + j is bit j of the K-bit index of element 32*g + t.
+ *     Bits of positions past n are 0.  packed holds ceil(n/32)*K words.
+ *   - Alignment: element arrays (A, out, X) and packed must be 16-byte
+ *     aligned, float/uint8 side arrays 4-byte aligned (codes: 1 byte);
+ *     otherwise KBIT_EALIGN.
+ *   - Floating point: IEEE binary32 with round to nearest even, no fused
+ *     multiply-add, subnormals kept; narrowing to fp16/bf16 rounds to
+ *     nearest even.  Results are bit-identical to the CPU oracle.
+ *   - Limits: n <= 2^40 elements (KBIT_EINVAL beyond).
+ *   - Calls on different streams may run concurrently (no shared state).
+ */
+#ifndef KBIT_H
+#define KBIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KBIT_OK = 0,
+    KBIT_EINVAL = -1,   /* null pointer, negative or too large n, bad K/levels */
+    KBIT_EBLOCK = -2,   /* blocksize not a power of two in [32, 4096]          */
+    KBIT_EALIGN = -3,   /* pointer misaligned for the kernel's vector accesses */
+    KBIT_ELAUNCH = -4,  /* the HIP runtime rejected the launch                 */
+    KBIT_EDEVICE = -5   /* no usable gfx950 device is current                  */
+} kbit_status;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* kbit_strerror(int status);
+
+/* ABI version of this header/library pair. */
+int kbit_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Codebook generation (host, no device access).  Each writes float32 values
+ * sorted ascending into a caller-owned host array.
+ * ---------------------------------------------------------------------- */
+
+/* NF_K codebook, K in 2..5 -> 2^K values in out_host.
+ * [QLORA-2] PATCH 001 tests/test_kbit_quantization.py
+ * create_normal_float_codebook gives levels at the N(0,1) quantiles of the
+ * bin midpoints (2i+1)/(2n), scaled to [-1, 1]; the hot path needs an exact
+ * zero, so the negative side uses that rule at n = 2^K - 1 levels, the
+ * positive side at n = 2^K levels, each side scaled so its extreme is
+ * exactly -1 / +1, plus 0.0.  Computed in extended precision and rounded
+ * once to float32.  KBIT_EINVAL for K outside 2..5 or a null pointer. */
+int kbit_codebook_nf(int K, float* out_host);
+
+/* FP4 (E2M1) codebook scaled to [-1, 1], 16 values:
+ * {-6,-4,-3,-2,-1.5,-1,-0.5,-0, +0,0.5,1,1.5,2,3,4,6} / 6 (float32 division).
+ * Index 7 is -0.0 and index 8 is +0.0.  ([PR2051] Summary names NF4/FP4.) */
+int kbit_codebook_fp4(float* out_host);
+
+/* Lloyd-Max (minimum mean-squared-error) quantizer levels of N(0,1):
+ * levels even in 2..256; fixed point of the centroid/midpoint conditions,
+ * exactly antisymmetric, rounded once to float32.  ([ORBIT] methodology
+ * audit: converged Lloyd-Max codebook.)  KBIT_EINVAL for bad levels. */
+int kbit_codebook_lloyd_max_normal(int levels, float* out_host);
+
+/* 256-entry signed dynamic-tree 8-bit map used by the nested absmax codes:
+ * 0, +1, and +-10^-z * (0.1 + 0.9 (2f+1) / 2^(7-z)) for z = 0..6,
+ * f = 0..2^(6-z)-1, sorted ascending.  ([PR2051] Summary: per-block scales
+ * are 8-bit General8 codes; this table is this library's own construction
+ * from the dynamic tree quantization description.) */
+int kbit_dynamic_map8(float* out_host);
+
+/* ------------------------------------------------------------------------
+ * Blockwise quantize: [QLORA-2] PATCH 001 kQuantizeBlockwise_kbit /
+ * quantize_kbit_ref, generalised to blocksize B.
+ *   absmax[b]  = max |A_e| over block b (stored unclamped)
+ *   x_n        = RN(A_e / max(absmax[b], 1e-8f))        (IEEE division)
+ *   index      = smallest i minimising |RN(x_n - codebook[i])|
+ *   packed     = bit planes of the indices (layout above)
+ * codebook : device, 2^K float32.  Any finite values are accepted; sorted
+ *            codebooks in [-1, 1] whose distinct neighbours differ by at least
+ *            1/64 take the fast classification path, others an exact scan.
+ * A        : device, n elements of the named type.
+ * absmax   : device, ceil(n/B) float32 (output).
+ * packed   : device, ceil(n/32)*K uint32 (output).
+ * --------------------------------------------------------------------- */
+#define KBIT_DECLARE_QUANTIZE(TNAME, CTYPE, K)                                       \
+    int quantize_kbit_##TNAME##_k##K(const float* codebook, const CTYPE* A,           \
+                                     float* absmax, uint32_t* packed, int64_t n,      \
+                                     int32_t blocksize, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Blockwise dequantize: [QLORA-2] PATCH 001 kDequantizeBlockwise_kbit /
+ * dequantize_kbit_ref.
+ *   out_e = RN_T( RN(codebook[index_e] * absmax[e / B]) )
+ * packed   : device, ceil(n/32)*K uint32.
+ * codebook : device, 2^K float32.
+ * absmax   : device, ceil(n/B) float32.
+ * out      : device, n elements of the named type (output).
+ * --------------------------------------------------------------------- */
+#define KBIT_DECLARE_DEQUANTIZE(TNAME, CTYPE, K)                                     \
+    int dequantize_kbit_##TNAME##_k##K(const uint32_t* packed, const float* codebook, \
+                                       const float* absmax, CTYPE* out, int64_t n,    \
+                                       int32_t blocksize, void* stream);
+
+#define KBIT_DECLARE_ALL_K(TNAME, CTYPE)                                              \
+    KBIT_DECLARE_QUANTIZE(TNAME, CTYPE, 2) KBIT_DECLARE_QUANTIZE(TNAME, CTYPE, 3)     \
+    KBIT_DECLARE_QUANTIZE(TNAME, CTYPE, 4) KBIT_DECLARE_QUANTIZE(TNAME, CTYPE, 5)     \
+    KBIT_DECLARE_DEQUANTIZE(TNAME, CTYPE, 2) KBIT_DECLARE_DEQUANTIZE(TNAME, CTYPE, 3) \
+    KBIT_DECLARE_DEQUANTIZE(TNAME, CTYPE, 4) KBIT_DECLARE_DEQUANTIZE(TNAME, CTYPE, 5)
+
+KBIT_DECLARE_ALL_K(fp32, float)
+KBIT_DECLARE_ALL_K(fp16, uint16_t)
+KBIT_DECLARE_ALL_K(bf16, uint16_t)
+
+/* ------------------------------------------------------------------------
+ * Nested (double-quantized) 4-bit dequantize, scale rebuild fused into the
+ * value decode: [PR2051] Summary and Implementation.  Groups of 256 blocks.
+ *   s_b   = RN( RN(qmap2[absmax_code[b]] * absmax2[b / 256]) + offset )
+ *           (a separately rounded multiply, then add; never fused)
+ *   out_e = RN_T( RN(codebook16[index_e] * s_{e / B}) )
+ * packed      : device, ceil(n/32)*4 uint32 (K = 4 bit planes).
+ * codebook16  : device, 16 float32 (NF4 or FP4).
+ * absmax_code : device, ceil(n/B) uint8.
+ * qmap2       : device, 256 float32.
+ * absmax2     : device, ceil(ceil(n/B)/256) float32.
+ * offset      : the fp32 mean offset (by value).
+ * out         : device, n elements of the named type (output).
+ * --------------------------------------------------------------------- */
+#define KBIT_DECLARE_NESTED(TNAME, CTYPE)                                               \
+    int dequantize_4bit_nested_##TNAME(const uint32_t* packed, const float* codebook16, \
+                                       const uint8_t* absmax_code, const float* qmap2,  \
+                                       const float* absmax2, float offset, CTYPE* out,  \
+                                       int64_t n, int32_t blocksize, void* stream);
+KBIT_DECLARE_NESTED(fp32, float)
+KBIT_DECLARE_NESTED(fp16, uint16_t)
+KBIT_DECLARE_NESTED(bf16, uint16_t)
+
+/* ------------------------------------------------------------------------
+ * W4A4-style activation assignment ([ORBIT] README W4A4 fast path and
+ * CARD.md quantize_activations_packed_w4; exact Lloyd-Max centroids, packed
+ * 4-bit output).  Per row r of X (rows x d, bf16, row-major):
+ *   norm_r = RN(sqrt(S)), S = sum of x_i^2 over a perfect binary tree of
+ *            contiguous halves, each addition rounded to fp32;
+ *   u      = x with its sign flipped where bit (i % 32) of sign_bits[i / 32]
+ *            is 1 (one mask shared by all rows);
+ *   u      = unnormalised Walsh-Hadamard transform of length d, natural
+ *            order, stages h = 1, 2, ..., d/2 in that order, every
+ *            butterfly (u_j + u_{j+h}, u_j - u_{j+h}) rounded to fp32;
+ *   z      = RN(u / max(norm_r, 1e-10f));
+ *   index  = smallest i minimising |RN(z - codebook16[i])|.
+ * X          : device, rows*d uint16 (bf16 bits).
+ * sign_bits  : device, d/32 uint32.
+ * codebook16 : device, 16 float32 (e.g. kbit_codebook_lloyd_max_normal(16)).
+ * row_norm   : device, rows float32 (output, unclamped norm).
+ * packed     : device, rows*d/32*4 uint32 (output; K = 4 bit planes of the
+ *              flattened index array, row after row).
+ * d must be 4096 (KBIT_EINVAL otherwise); rows >= 0.
+ * --------------------------------------------------------------------- */
+int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d,
+                              const uint32_t* sign_bits, const float* codebook16,
+                              float* row_norm, uint32_t* packed, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KBIT_H */

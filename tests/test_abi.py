@@ -1,0 +1,107 @@
+"""Host-side checks of libkbit.so: exports, codebook generators, validation.
+
+No compute call is made here; argument errors are detected by the library
+before it touches a device.
+"""
+
+import ctypes as ct
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import codebooks
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kbit.h")
+
+kb = pytest.importorskip("blockwise_bit_codebook_amd")
+
+
+def _lib():
+    return kb.lib()
+
+
+def _declared_functions():
+    out = subprocess.run(["gcc", "-E", "-P", "-x", "c", HEADER], capture_output=True, text=True, check=True).stdout
+    names = re.findall(r"\b(?:int|const char\s*\*)\s+(\w+)\s*\(", out)
+    return sorted(set(names))
+
+
+def test_header_compiles_as_c_and_cpp():
+    for lang in ("c", "c++"):
+        subprocess.run(["gcc", "-fsyntax-only", "-Wall", "-Werror", "-x", lang, HEADER], check=True)
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) == 4 + 2 + 24 + 3 + 1, names
+    nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
+                        capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    from blockwise_bit_codebook_amd import _lib as L
+    assert sorted(n for n, _ in L.SIGNATURES) == names
+
+
+@pytest.mark.parametrize("K", [2, 3, 4, 5])
+def test_nf_generator_equals_oracle(K):
+    assert np.array_equal(kb.codebook_nf(K).view(np.uint32), codebooks.nf(K).view(np.uint32))
+
+
+def test_fp4_generator_equals_oracle():
+    assert np.array_equal(kb.codebook_fp4().view(np.uint32), codebooks.fp4().view(np.uint32))
+
+
+def test_lloyd_max_generator_equals_oracle():
+    assert np.array_equal(kb.codebook_lloyd_max_normal(16).view(np.uint32),
+                          codebooks.lloyd_max_normal(16).view(np.uint32))
+
+
+def test_dynamic_map_generator_equals_oracle():
+    assert np.array_equal(kb.dynamic_map8().view(np.uint32), codebooks.dynamic_map8().view(np.uint32))
+
+
+def test_generator_argument_errors():
+    lib = _lib()
+    buf = np.zeros(64, np.float32)
+    p = buf.ctypes.data_as(ct.c_void_p)
+    assert lib.kbit_codebook_nf(1, p) == -1
+    assert lib.kbit_codebook_nf(6, p) == -1
+    assert lib.kbit_codebook_nf(4, None) == -1
+    assert lib.kbit_codebook_lloyd_max_normal(3, p) == -1
+    assert lib.kbit_codebook_fp4(None) == -1
+    assert lib.kbit_strerror(-2).decode().startswith("blocksize")
+    assert lib.kbit_abi_version() == 1
+
+
+# fake, never dereferenced device addresses
+_A16 = ct.c_void_p(0x10000)
+_A4 = ct.c_void_p(0x20004)
+
+
+def test_validation_codes_before_any_device_access():
+    lib = _lib()
+    q = lib.quantize_kbit_bf16_k4
+    assert q(_A16, _A16, _A16, _A16, 100, 48, None) == -2         # blocksize not power of two
+    assert q(_A16, _A16, _A16, _A16, 100, 16, None) == -2         # too small
+    assert q(_A16, _A16, _A16, _A16, 100, 8192, None) == -2       # too large
+    assert q(_A16, _A16, _A16, _A16, -1, 64, None) == -1          # negative n
+    assert q(_A16, _A16, _A16, _A16, (1 << 40) + 1, 64, None) == -1
+    assert q(_A16, _A16, _A16, _A16, 0, 64, None) == 0            # empty: no-op
+    assert q(None, None, None, None, 0, 64, None) == 0
+    assert q(None, _A16, _A16, _A16, 10, 64, None) == -1          # null codebook
+    assert q(_A16, _A4, _A16, _A16, 10, 64, None) == -3           # A not 16-byte aligned
+    d = lib.dequantize_kbit_fp32_k3
+    assert d(_A16, _A16, _A16, _A4, 10, 32, None) == -3           # out misaligned
+    assert d(_A16, _A16, _A16, None, 10, 32, None) == -1
+    nd = lib.dequantize_4bit_nested_fp16
+    assert nd(_A16, _A16, None, _A16, _A16, ct.c_float(0.0), _A16, 10, 64, None) == -1
+    assert nd(_A16, _A16, _A16, _A16, _A16, ct.c_float(0.0), _A16, 10, 96, None) == -2
+    act = lib.quantize_act_fwht_k4_bf16
+    assert act(_A16, 4, 2048, _A16, _A16, _A16, _A16, None) == -1  # d must be 4096
+    assert act(_A16, 0, 4096, None, None, None, None, None) == 0
+    assert act(_A4, 4, 4096, _A16, _A16, _A16, _A16, None) == -3
