@@ -24,9 +24,12 @@ constexpr int kDppQuadBcast0 = 0x00;    // quad_perm [0,0,0,0]
 constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i inside each half row
 constexpr int kDppMirror = 0x140;       // lane i <-> 15-i inside each row
 
+// Every control used here (quad_perm, row mirrors) reads a lane that
+// exists, so bound_ctrl never applies; setting it lets the compiler fold the
+// move into the consuming VOP2 instruction as a DPP operand.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, false));
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
 }
 
 template <int CTRL>
@@ -95,14 +98,55 @@ __device__ __forceinline__ uint32_t planes_to_nibbles(uint32_t p) {
 // (16 bytes for 16-bit types, 32 bytes for fp32) widened exactly to float,
 // and stores 8 floats narrowed with round-to-nearest-even.
 // ---------------------------------------------------------------------------
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float float8 __attribute__((ext_vector_type(8)));
+
+// 16-byte global load, optionally marked non-temporal (streamed once).
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Largest magnitude (sign bit cleared) of the 8 16-bit values in r[0], as an
+// integer.  For IEEE-style formats the magnitude order of finite values and
+// infinities equals the integer order of their bits, and NaNs sort above.
+__device__ __forceinline__ uint32_t max_mag16x8(const u32x4& r) {
+    auto h = [](uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu); };
+    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(h(r[0]), h(r[1])),
+                                              __builtin_elementwise_max(h(r[2]), h(r[3])));
+    return max(static_cast<uint32_t>(m[0]), static_cast<uint32_t>(m[1]));
+}
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct Fp32 {
     using storage = float;
     static constexpr int kBytes = 4;
+    static constexpr int kVec = 2;  // 16-byte vectors per 8 elements
+    __device__ static void unpack(const u32x4* r, float* x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = __uint_as_float(r[0][i]);
+            x[4 + i] = __uint_as_float(r[1][i]);
+        }
+    }
+    __device__ static uint32_t max_mag(const u32x4* r) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max(r[0][i] & 0x7FFFFFFFu, r[1][i] & 0x7FFFFFFFu));
+        return m;
+    }
+    __device__ static float mag_to_float(uint32_t m) { return __uint_as_float(m); }
+    // Elements e0 .. e0+7 with zeros past n.
+    __device__ static void load_partial(const storage* A, int64_t e0, int64_t n, u32x4* r) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            r[s >> 2][s & 3] = (e0 + s < n) ? __float_as_uint(A[e0 + s]) : 0u;
+    }
     __device__ static void load8(const storage* p, float* x) {
         const uint4 a = *reinterpret_cast<const uint4*>(p);
         const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
@@ -139,6 +183,23 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 struct Bf16 {
     using storage = uint16_t;
     static constexpr int kBytes = 2;
+    static constexpr int kVec = 1;
+    __device__ static void unpack(const u32x4* r, float* x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(r[0][i] << 16);
+            x[2 * i + 1] = __uint_as_float(r[0][i] & 0xFFFF0000u);
+        }
+    }
+    __device__ static uint32_t max_mag(const u32x4* r) { return max_mag16x8(r[0]); }
+    __device__ static void load_partial(const storage* A, int64_t e0, int64_t n, u32x4* r) {
+        uint32_t h[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) h[s] = (e0 + s < n) ? static_cast<uint32_t>(A[e0 + s]) : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[0][i] = h[2 * i] | (h[2 * i + 1] << 16);
+    }
+    __device__ static float mag_to_float(uint32_t m) { return __uint_as_float(m << 16); }
     __device__ static void load8(const storage* p, float* x) {
         const uint4 a = *reinterpret_cast<const uint4*>(p);
         const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -163,9 +224,26 @@ struct Bf16 {
 struct Fp16 {
     using storage = uint16_t;
     static constexpr int kBytes = 2;
+    static constexpr int kVec = 1;
     __device__ static float h2f(uint32_t bits16) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
     }
+    __device__ static void unpack(const u32x4* r, float* x) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = h2f(r[0][i] & 0xFFFFu);
+            x[2 * i + 1] = h2f(r[0][i] >> 16);
+        }
+    }
+    __device__ static uint32_t max_mag(const u32x4* r) { return max_mag16x8(r[0]); }
+    __device__ static void load_partial(const storage* A, int64_t e0, int64_t n, u32x4* r) {
+        uint32_t h[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) h[s] = (e0 + s < n) ? static_cast<uint32_t>(A[e0 + s]) : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[0][i] = h[2 * i] | (h[2 * i + 1] << 16);
+    }
+    __device__ static float mag_to_float(uint32_t m) { return h2f(m); }
     __device__ static void load8(const storage* p, float* x) {
         const uint4 a = *reinterpret_cast<const uint4*>(p);
         const uint32_t w[4] = {a.x, a.y, a.z, a.w};
