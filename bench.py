@@ -5,16 +5,19 @@ blocksize 64) followed by the nested 4-bit dequantize of those planes back to
 bf16 (per-block scales rebuilt from 8-bit codes over groups of 256 plus a
 mean offset), on an 8192 x 8192 weight drawn from N(0, 0.02).  Inputs live in
 HBM before timing starts.  Several buffer sets are rotated so that the
-256 MB last-level cache cannot hold a step's working set.
+256 MB last-level cache cannot hold a step's working set.  Each set's step
+is captured once into a HIP graph and the timed loop replays the graphs.
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (read +
-written by both kernels) divided by the measured time per step, in GB/s.
-Per-kernel throughput comes from HIP events around each launch on the
-stream the kernels run on.  ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload (rank 0, N = 1 only).
+written by both kernels) divided by the wall time per step, in GB/s.
+Per-kernel launch times come from HIP events around graph replays that run
+one kernel back to back over all buffer sets, on the stream the kernels run
+on.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload (N = 1 only).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--sets 4]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--sets 4]
                     [--no-cpu-baseline] [--copy-calibration]
+    python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR   (no GPU)
 """
 
 import argparse
@@ -49,16 +52,125 @@ def algorithmic_bytes(n):
 def parse(argv=None):
     ap = argparse.ArgumentParser(description="k-bit codec hot-path throughput (one GPU)")
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run plain 256 MiB device copies (to scale HBM byte counters)")
+                    help=f"after timing, run {CAL_COPIES} plain device copies of {CAL_BYTES >> 20} MiB "
+                         "(known bytes, to scale HBM byte counters)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="per-dispatch HBM bytes measured with rocprofv3 counters, if present")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarise rocprofv3 output of the profile commands into profiles/")
     return ap.parse_args(argv)
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (CPU only)
+# --------------------------------------------------------------------------
+CAL_BYTES = 192 << 20
+CAL_COPIES = 3
+KERNELS = {
+    # name used in the JSON line: (substring of the HIP kernel name, sources that define it)
+    "quantize_kbit_bf16_k4": ("quantize_kernel<kbit::Bf16, 4",
+                              ["blockwise_bit_codebook_amd/csrc/quantize.hip",
+                               "blockwise_bit_codebook_amd/csrc/device.h"]),
+    "dequantize_4bit_nested_bf16": ("dequantize_nested_kernel<kbit::Bf16",
+                                    ["blockwise_bit_codebook_amd/csrc/dequantize.hip",
+                                     "blockwise_bit_codebook_amd/csrc/device.h"]),
+}
+PROFILE_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o trace -- "
+    "python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline --copy-calibration",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o fetch -- "
+    "python3 $R/bench.py --steps 6 --warmup 2 --no-cpu-baseline --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o write -- "
+    "python3 $R/bench.py --steps 6 --warmup 2 --no-cpu-baseline --copy-calibration",
+    "cd $R && python3 bench.py --summarize gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write",
+]
+
+
+def source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize(trace_dir, fetch_dir, write_dir):
+    """Per-kernel average duration (kernel trace) and HBM bytes per dispatch
+    (FETCH_SIZE / WRITE_SIZE in KiB, each scaled by what the same counter
+    reads for the calibration copies of known size)."""
+    trace = _csv_rows(trace_dir, "kernel_trace.csv")
+    counters = {c: _csv_rows(d, "counter_collection.csv") for c, d in (("FETCH_SIZE", fetch_dir),
+                                                                        ("WRITE_SIZE", write_dir))}
+    scale = {}
+    per_kernel = {}
+    for cname, rows in counters.items():
+        rows = [r for r in rows if r["Counter_Name"] == cname]
+        cal = sorted((r for r in rows if "copyBuffer" in r["Kernel_Name"]), key=lambda r: int(r["Dispatch_Id"]))
+        cal = cal[-CAL_COPIES:]
+        kib = sum(float(r["Counter_Value"]) for r in cal) / len(cal)
+        scale[cname] = (CAL_BYTES / 1024.0) / kib
+        for name, (pat, _) in KERNELS.items():
+            vals = [float(r["Counter_Value"]) for r in rows if pat in r["Kernel_Name"]]
+            per_kernel.setdefault(name, {})[cname] = sum(vals) / len(vals) if vals else None
+    n = ROWS * COLS
+    qb, nb = algorithmic_bytes(n)
+    alg = {"quantize_kbit_bf16_k4": qb, "dequantize_4bit_nested_bf16": nb}
+    out = {"calibration": {"copy_bytes": CAL_BYTES, "copies": CAL_COPIES,
+                           "fetch_scale": round(scale["FETCH_SIZE"], 4),
+                           "write_scale": round(scale["WRITE_SIZE"], 4)},
+           "kernels": {}}
+    lines = ["# rocprofv3 summary: quantize + nested dequantize, 8192x8192 bf16, NF4, blocksize 64", "",
+             "Commands (R = repository root; the counter runs are separate passes):", "", "```"]
+    lines += PROFILE_COMMANDS + ["```", "",
+                                 f"Calibration: the last {CAL_COPIES} device copies of {CAL_BYTES >> 20} MiB each; "
+                                 f"FETCH_SIZE x {scale['FETCH_SIZE']:.3f}, WRITE_SIZE x {scale['WRITE_SIZE']:.3f} "
+                                 "give bytes.", "",
+                                 "| kernel | dispatches | avg us | min us | max us | HBM read MB | HBM write MB "
+                                 "| algorithmic MB | traffic / algorithmic | GB/s (algorithmic) |",
+                                 "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, (pat, srcs) in KERNELS.items():
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if pat in r["Kernel_Name"]]
+        if not durs:
+            continue
+        avg = sum(durs) / len(durs) / 1e3
+        f_kib = per_kernel[name]["FETCH_SIZE"]
+        w_kib = per_kernel[name]["WRITE_SIZE"]
+        rd = f_kib * 1024 * scale["FETCH_SIZE"]
+        wr = w_kib * 1024 * scale["WRITE_SIZE"]
+        out["kernels"][name] = {"avg_us": round(avg, 3), "dispatches": len(durs),
+                                "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
+                                "read_bytes": int(rd), "write_bytes": int(wr), "traffic": int(rd + wr),
+                                "algorithmic_bytes": alg[name], "source_sha256_16": source_digest(srcs)}
+        lines.append(f"| {name} | {len(durs)} | {avg:.2f} | {min(durs) / 1e3:.2f} | {max(durs) / 1e3:.2f} | "
+                     f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {alg[name] / 1e6:.1f} | {(rd + wr) / alg[name]:.3f} | "
+                     f"{alg[name] / (avg * 1e-6) / 1e9:.0f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    md = os.path.join(ROOT, "profiles", "quantize_nested_dequant_8192sq_bf16_b64.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
 
 
 def cpu_baseline(seconds_target):
@@ -90,14 +202,17 @@ def cpu_baseline(seconds_target):
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} elements ({done // COLS} rows of the 8192x8192 bf16 weight) in 1 Mi-element chunks: "
-                  f"quantize + pack + nested encode + nested dequantize, numpy float32, one thread; {el:.1f} s",
+        "sample": f"{done} elements: 1 Mi-element chunks (128 rows) taken in order from the 8192x8192 bf16 "
+                  f"weight, wrapping around; quantize + pack + nested encode + nested dequantize, numpy "
+                  f"float32, one thread; {el:.1f} s",
         "elements_per_s": round(done / el, 1),
     }
 
 
 def main(argv=None):
     args = parse(argv)
+    if args.summarize:
+        return summarize(*args.summarize)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the hot path has no "
               "cross-GPU step to measure here.", file=sys.stderr)
@@ -129,31 +244,68 @@ def main(argv=None):
         })
     torch.cuda.synchronize()
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step(s):
         kb.quantize_kbit(s["A"], cb, K, BLOCK, absmax=s["absmax"], packed=s["packed"])
-        if ev is not None:
-            ev[1].record()
         kb.dequantize_4bit_nested(s["packed"], cb, s["code"], qmap, s["absmax2"], offset, n,
                                   torch.bfloat16, BLOCK, out=s["out"])
-        if ev is not None:
-            ev[2].record()
 
-    for i in range(args.warmup):
-        step(sets[i % args.sets])
+    def quant_only(s):
+        kb.quantize_kbit(s["A"], cb, K, BLOCK, absmax=s["absmax"], packed=s["packed"])
+
+    def nested_only(s):
+        kb.dequantize_4bit_nested(s["packed"], cb, s["code"], qmap, s["absmax2"], offset, n,
+                                  torch.bfloat16, BLOCK, out=s["out"])
+
+    for s_ in sets:                              # eager once per set: per-device setup happens here
+        step(s_)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The step's two launches are captured once per buffer set into a HIP
+    # graph, so the timed loop measures the GPU rather than Python's launch
+    # path (the kernels allocate nothing and take the capture stream).
+    def capture(fn, items):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s_ in items:
+                fn(s_)
+        return g
+
+    g_step = [capture(step, [s_]) for s_ in sets]
+    g_quant = capture(quant_only, sets)          # one launch per set, back to back
+    g_nested = capture(nested_only, sets)
+    for i in range(args.warmup):
+        g_step[i % args.sets].replay()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
-        step(sets[i % args.sets], evs[i])
+        g_step[i % args.sets].replay()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
 
-    tq = [e[0].elapsed_time(e[1]) for e in evs]      # ms
-    tn = [e[1].elapsed_time(e[2]) for e in evs]
+    # Per-kernel launch time: bursts of the same kernel (graph replays),
+    # HIP events on the stream the kernels run on.
+    def burst(g, launches_per_replay, reps):
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / launches_per_replay)
+        return times
+
+    reps = max(3, args.steps // args.sets)
+    tq = burst(g_quant, args.sets, reps)
+    tn = burst(g_nested, args.sets, reps)
     qbytes, nbytes = algorithmic_bytes(n)
     ms_step = wall * 1e3 / args.steps
     value = (qbytes + nbytes) / (ms_step * 1e-3) / 1e9
@@ -163,8 +315,7 @@ def main(argv=None):
         avg = float(ts.mean())
         gbps = nbytes_ / (avg * 1e-3) / 1e9
         return {"avg_us": round(avg * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
-                "p10_us": round(float(np.percentile(ts, 10)) * 1e3, 3),
-                "p90_us": round(float(np.percentile(ts, 90)) * 1e3, 3),
+                "min_us": round(float(ts.min()) * 1e3, 3), "max_us": round(float(ts.max()) * 1e3, 3),
                 "bytes": nbytes_, "GB/s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                 "elements_per_s": round(n / (avg * 1e-3), 1)}
 
@@ -173,18 +324,22 @@ def main(argv=None):
         ("dequantize_4bit_nested_bf16", kn)
     traffic = None
     if os.path.exists(args.traffic_json):
+        # counters taken on a different version of the kernel's source do not count
         try:
             with open(args.traffic_json) as f:
-                traffic = json.load(f).get(dom_name)
-        except (OSError, ValueError):
+                rec = json.load(f)["kernels"].get(dom_name)
+            if rec and rec["source_sha256_16"] == source_digest(KERNELS[dom_name][1]):
+                traffic = rec["traffic"]
+        except (OSError, ValueError, KeyError):
             traffic = None
     roofline = {"kernel": dom_name, "bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": dom["frac_of_hbm_peak"], "traffic": traffic}
 
     if args.copy_calibration:
-        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev)
+        src = torch.zeros(CAL_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(5):
+        torch.cuda.synchronize()
+        for _ in range(CAL_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
 
@@ -198,6 +353,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -28,10 +28,16 @@
 namespace kbit {
 namespace {
 
-// Per-lane block scale: the plain path reads absmax.
+// Per-lane block scale in two steps, so that its global loads can be issued
+// a step ahead: load() gathers what the block's scale is built from,
+// finish() builds it.
 struct PlainScale {
     const float* absmax;
-    __device__ float get(int64_t b) const { return absmax[b]; }
+    struct Raw {
+        float a;
+    };
+    __device__ Raw load(int64_t b) const { return Raw{absmax[b]}; }
+    __device__ float finish(const Raw& r) const { return r.a; }
 };
 
 // Nested scale rebuild.  qmap2 is staged in LDS by the kernel prologue.
@@ -40,72 +46,112 @@ struct NestedScale {
     const float* absmax2;
     float offset;
     const float* qmap_lds;
-    __device__ float get(int64_t b) const {
+    struct Raw {
+        uint32_t code;
+        float a2;
+    };
+    __device__ Raw load(int64_t b) const { return Raw{code[b], absmax2[b >> 8]}; }
+    __device__ float finish(const Raw& r) const {
 #pragma clang fp contract(off)
-        const float q = qmap_lds[code[b]];
-        const float prod = q * absmax2[b >> 8];
+        const float prod = qmap_lds[r.code] * r.a2;
         return prod + offset;
     }
 };
 
-// Loads the K plane words of the lane's group and returns the lane's plane
-// bytes (byte j = plane j, bit t = element t of the lane's 8) and, for K = 5,
-// the plane-4 byte in *p4.
-template <int K>
-__device__ __forceinline__ uint32_t load_plane_bytes(const uint32_t* __restrict__ packed, int64_t g,
-                                                     bool g_ok, int lane, uint32_t* p4) {
+// One lane's share of one wave tile (512 elements = 16 groups of 32): plane
+// word l of its group (l = lane & 3, lanes with l >= K hold 0), for K = 5 the
+// group's plane-4 word (lane l = 0 only), and the raw scale of its block.
+template <int K, class Scale>
+struct TileIn {
+    uint32_t w = 0, w4 = 0;
+    typename Scale::Raw sc;
+};
+
+template <int K, class Scale, bool FULL>
+__device__ __forceinline__ TileIn<K, Scale> load_tile(const uint32_t* __restrict__ packed, const Scale& scale,
+                                                      int64_t tile, int64_t n, int log2B, int lane) {
+    TileIn<K, Scale> in;
+    const int64_t base = tile * kWaveTile;
+    const int64_t g = base / kGroup + (lane >> 2);
+    const int64_t e0 = base + static_cast<int64_t>(lane) * kElemsPerLane;
     const int l = lane & 3;
-    uint32_t w = 0;
-    if (l < K && g_ok) w = packed[g * K + l];
-    const uint32_t p = quad_transpose_bytes(w, lane);
+    const bool g_ok = FULL || g * kGroup < n;
+    if (K == 4 ? g_ok : (l < K && g_ok)) in.w = packed[g * K + l];
     if constexpr (K == 5) {
-        uint32_t w4 = (l == 0 && g_ok) ? packed[g * K + 4] : 0u;
-        w4 = dpp_u32<kDppQuadBcast0>(w4);
-        *p4 = (w4 >> (8 * l)) & 0xFFu;
+        if (l == 0 && g_ok) in.w4 = packed[g * K + 4];
     }
-    return p;
+    in.sc = scale.load((FULL || e0 < n ? e0 : 0) >> log2B);
+    return in;
 }
 
-template <class E, int K, class Scale>
+template <class E, int K, class Scale, bool FULL, bool NTS>
+__device__ __forceinline__ void decode_tile(const TileIn<K, Scale>& in, const Scale& scale, const float* cb_lds,
+                                            const float2* pair_lds, typename E::storage* __restrict__ out,
+                                            int64_t tile, int64_t n, int lane) {
+    const int64_t e0 = tile * kWaveTile + static_cast<int64_t>(lane) * kElemsPerLane;
+    const uint32_t p = quad_transpose_bytes(in.w, lane);
+    const uint32_t nib = planes_to_nibbles(p);
+    const float s = scale.finish(in.sc);
+    float v[kElemsPerLane];
+    if constexpr (K <= 4) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float2 c2 = pair_lds[(nib >> (8 * t)) & 0xFFu];
+            v[2 * t] = c2.x * s;
+            v[2 * t + 1] = c2.y * s;
+        }
+    } else {
+        const uint32_t p4 = (dpp_u32<kDppQuadBcast0>(in.w4) >> (8 * (lane & 3))) & 0xFFu;
+#pragma unroll
+        for (int t = 0; t < kElemsPerLane; ++t) {
+            const uint32_t idx = ((nib >> (4 * t)) & 15u) | (((p4 >> t) & 1u) << 4);
+            v[t] = cb_lds[idx] * s;
+        }
+    }
+    if (FULL) {
+        E::template store8<NTS>(out + e0, v);
+    } else {
+#pragma unroll
+        for (int t = 0; t < kElemsPerLane; ++t)
+            if (e0 + t < n) E::store1(out + e0 + t, v[t]);
+    }
+}
+
+// Steps of U wave tiles: the step's plane words and scale inputs are loaded
+// together, the next step's loads are issued before this step's stores, and
+// full steps run without branches (so the store queue never has to drain
+// before the next loads are used).  Remaining tiles go one at a time.
+template <class E, int K, class Scale, int U, bool NTS>
 __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packed, const float* cb_lds,
-                                              const float2* pair_lds, Scale scale,
-                                              typename E::storage* __restrict__ out, int64_t n,
-                                              int log2B) {
+                                              const float2* pair_lds, const Scale& scale,
+                                              typename E::storage* __restrict__ out, int64_t n, int log2B) {
     const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerGroup;
+    const int64_t nfull = n / (static_cast<int64_t>(kWaveTile) * U);  // full steps
+    int64_t st = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    if (st < nfull) {
+        TileIn<K, Scale> cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = load_tile<K, Scale, true>(packed, scale, st * U + u, n, log2B, lane);
+        for (; st < nfull; st += nwaves) {
+            const int64_t sn = min(st + nwaves, nfull - 1);
+            TileIn<K, Scale> nxt[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) nxt[u] = load_tile<K, Scale, true>(packed, scale, sn * U + u, n, log2B, lane);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                decode_tile<E, K, Scale, true, NTS>(cur[u], scale, cb_lds, pair_lds, out, st * U + u, n, lane);
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+    }
+    // tiles after the last full step: one wave tile per wave
     const int64_t ntiles = (n + kWaveTile - 1) / kWaveTile;
-    const int64_t ngroups = (n + kGroup - 1) / kGroup;
-    for (int64_t tile = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + (threadIdx.x >> 6);
-         tile < ntiles; tile += nwaves) {
-        const int64_t base = tile * kWaveTile;
-        const int64_t g = base / kGroup + (lane >> 2);
-        const int64_t e0 = base + lane * kElemsPerLane;
-        uint32_t p4 = 0;
-        const uint32_t p = load_plane_bytes<K>(packed, g, g < ngroups, lane, &p4);
-        const float s = (e0 < n) ? scale.get(e0 >> log2B) : 0.0f;
-        const uint32_t nib = planes_to_nibbles(p);
-        float v[kElemsPerLane];
-        if constexpr (K <= 4) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float2 c2 = pair_lds[(nib >> (8 * t)) & 0xFFu];
-                v[2 * t] = c2.x * s;
-                v[2 * t + 1] = c2.y * s;
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < kElemsPerLane; ++t) {
-                const uint32_t idx = ((nib >> (4 * t)) & 15u) | (((p4 >> t) & 1u) << 4);
-                v[t] = cb_lds[idx] * s;
-            }
-        }
-        if (base + kWaveTile <= n) {
-            E::store8(out + e0, v);
-        } else {
-#pragma unroll
-            for (int t = 0; t < kElemsPerLane; ++t)
-                if (e0 + t < n) E::store1(out + e0 + t, v[t]);
-        }
+    for (int64_t t = nfull * U + static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave; t < ntiles;
+         t += nwaves) {
+        const TileIn<K, Scale> in = load_tile<K, Scale, false>(packed, scale, t, n, log2B, lane);
+        decode_tile<E, K, Scale, false, false>(in, scale, cb_lds, pair_lds, out, t, n, lane);
     }
 }
 
@@ -122,6 +168,9 @@ __device__ __forceinline__ void stage_codebook(const float* __restrict__ cb, flo
     }
 }
 
+constexpr int kSteps = 4;      // wave tiles per step
+constexpr bool kNtStore = true;
+
 template <class E, int K>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ cb, const float* __restrict__ absmax,
@@ -130,10 +179,11 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
     __shared__ float2 pair_lds[256];
     stage_codebook<K>(cb, cb_lds, pair_lds);
     __syncthreads();
-    dequant_tiles<E, K>(packed, cb_lds, pair_lds, PlainScale{absmax}, out, n, log2B);
+    dequant_tiles<E, K, PlainScale, kSteps, kNtStore>(packed, cb_lds, pair_lds, PlainScale{absmax}, out, n,
+                                                       log2B);
 }
 
-template <class E>
+template <class E, int U = kSteps, bool NTS = kNtStore>
 __global__ __launch_bounds__(kThreads) void dequantize_nested_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ cb, const uint8_t* __restrict__ code,
     const float* __restrict__ qmap2, const float* __restrict__ absmax2, float offset,
@@ -144,8 +194,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_nested_kernel(
     stage_codebook<4>(cb, cb_lds, pair_lds);
     qmap_lds[threadIdx.x] = qmap2[threadIdx.x];
     __syncthreads();
-    dequant_tiles<E, 4>(packed, cb_lds, pair_lds, NestedScale{code, absmax2, offset, qmap_lds}, out, n,
-                        log2B);
+    dequant_tiles<E, 4, NestedScale, U, NTS>(packed, cb_lds, pair_lds,
+                                                        NestedScale{code, absmax2, offset, qmap_lds}, out, n,
+                                                        log2B);
 }
 
 template <class E, int K>
@@ -153,19 +204,19 @@ int launch_plain(const uint32_t* packed, const float* cb, const float* absmax, v
                  int log2B, void* stream) {
     auto kern = dequantize_kernel<E, K>;
     static int blocks_per_cu = 0;
-    const int64_t grid = persistent_grid(kern, blocks_per_cu, (n + kWaveTile - 1) / kWaveTile);
+    const int64_t grid = persistent_grid(kern, blocks_per_cu, (n + kWaveTile * kSteps - 1) / (kWaveTile * kSteps));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), packed, cb, absmax,
                        static_cast<typename E::storage*>(out), n, log2B);
     return static_cast<int>(hipGetLastError());
 }
 
-template <class E>
+template <class E, int U = kSteps, bool NTS = kNtStore>
 int launch_nested(const uint32_t* packed, const float* cb, const uint8_t* code, const float* qmap2,
                   const float* absmax2, float offset, void* out, int64_t n, int log2B, void* stream) {
-    auto kern = dequantize_nested_kernel<E>;
+    auto kern = dequantize_nested_kernel<E, U, NTS>;
     static int blocks_per_cu = 0;
-    const int64_t grid = persistent_grid(kern, blocks_per_cu, (n + kWaveTile - 1) / kWaveTile);
+    const int64_t grid = persistent_grid(kern, blocks_per_cu, (n + kWaveTile * U - 1) / (kWaveTile * U));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), packed, cb, code, qmap2, absmax2, offset,
                        static_cast<typename E::storage*>(out), n, log2B);

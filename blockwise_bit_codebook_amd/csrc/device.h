@@ -108,6 +108,14 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
     if constexpr (NT) return __builtin_nontemporal_load(q);
     else return *q;
 }
+
+// 16-byte global store, optionally marked non-temporal (written once).
+template <bool NT>
+__device__ __forceinline__ void store16(void* p, const u32x4& v) {
+    u32x4* q = reinterpret_cast<u32x4*>(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
@@ -156,25 +164,30 @@ struct Fp32 {
         x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
     }
     __device__ static float load1(const storage* p) { return *p; }
+    template <bool NT = false>
     __device__ static void store8(storage* p, const float* v) {
-        uint4 a, b;
-        a.x = __float_as_uint(v[0]); a.y = __float_as_uint(v[1]);
-        a.z = __float_as_uint(v[2]); a.w = __float_as_uint(v[3]);
-        b.x = __float_as_uint(v[4]); b.y = __float_as_uint(v[5]);
-        b.z = __float_as_uint(v[6]); b.w = __float_as_uint(v[7]);
-        *reinterpret_cast<uint4*>(p) = a;
-        *reinterpret_cast<uint4*>(p + 4) = b;
+        const u32x4 a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        const u32x4 b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+        store16<NT>(p, a);
+        store16<NT>(p + 4, b);
     }
     __device__ static void store1(storage* p, float v) { *p = v; }
 };
 
+// The narrowing converts below must see an fp32 value that has already been
+// rounded: without the empty asm the compiler may fold a preceding fp32
+// multiply into the conversion (v_fma_mix*), rounding once instead of twice.
+__device__ __forceinline__ void fence_f32(float& a, float& b) { asm("" : "+v"(a), "+v"(b)); }
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    fence_f32(lo, hi);
     f32x2 f = {lo, hi};
     bf16x2 h = __builtin_convertvector(f, bf16x2);
     return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    fence_f32(lo, hi);
     f32x2 f = {lo, hi};
     f16x2 h = __builtin_convertvector(f, f16x2);
     return __builtin_bit_cast(uint32_t, h);
@@ -210,11 +223,10 @@ struct Bf16 {
         }
     }
     __device__ static float load1(const storage* p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
+    template <bool NT = false>
     __device__ static void store8(storage* p, const float* v) {
-        uint4 a;
-        a.x = pack_bf16x2(v[0], v[1]); a.y = pack_bf16x2(v[2], v[3]);
-        a.z = pack_bf16x2(v[4], v[5]); a.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(p) = a;
+        store16<NT>(p, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                             pack_bf16x2(v[6], v[7])});
     }
     __device__ static void store1(storage* p, float v) {
         *p = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
@@ -254,11 +266,10 @@ struct Fp16 {
         }
     }
     __device__ static float load1(const storage* p) { return h2f(*p); }
+    template <bool NT = false>
     __device__ static void store8(storage* p, const float* v) {
-        uint4 a;
-        a.x = pack_f16x2(v[0], v[1]); a.y = pack_f16x2(v[2], v[3]);
-        a.z = pack_f16x2(v[4], v[5]); a.w = pack_f16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(p) = a;
+        store16<NT>(p, u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
+                             pack_f16x2(v[6], v[7])});
     }
     __device__ static void store1(storage* p, float v) {
         *p = static_cast<uint16_t>(pack_f16x2(v, 0.0f) & 0xFFFFu);

@@ -1,0 +1,66 @@
+"""The hot path captured into a HIP graph (as the benchmark runs it) gives, on
+every replay, exactly what eager launches give.  Outputs are cleared between
+replays, with eager work and synchronisations in between."""
+
+import numpy as np
+import pytest
+
+import blockwise_bit_codebook_amd as kb
+from blockwise_bit_codebook_amd import synth
+from oracle import codebooks, kbit, nested
+from tests.gpu_util import bits, case, np_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager_and_oracle():
+    import torch
+    B, K = 64, 4
+    x = synth.weight(1024, 1024, "bf16", seed=synth.SEED_WEIGHT_SHAPES, extra=synth.TAIL_EXTRA)
+    n = x.size
+    nb = kb.n_blocks(n, B)
+    cb = to_dev(codebooks.nf(K))
+    q = codebooks.dynamic_map8()
+    qmap = to_dev(q)
+    code_np, a2_np, off = synth.nested_state_synthetic(nb, seed=3)
+    A = to_dev(x, "bf16")
+    code, a2 = to_dev(code_np), to_dev(a2_np)
+    packed = torch.empty(kb.n_words(n, K), dtype=torch.int32, device="cuda")
+    absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
+    out = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        kb.quantize_kbit(A, cb, K, B, absmax=absmax, packed=packed)
+        kb.dequantize_4bit_nested(packed, cb, code, qmap, a2, off, n, torch.bfloat16, B, out=out)
+
+    case("graph: eager reference")
+    step()
+    torch.cuda.synchronize()
+    ref = (bits(packed), bits(absmax), bits(out))
+
+    # the oracle agrees with the eager run
+    from oracle import numerics
+    want_w, want_a = kbit.quantize_packed(numerics.widen(x, "bf16"), codebooks.nf(K), K, B)
+    assert np.array_equal(ref[0], want_w)
+    assert np.array_equal(ref[1], np_bits(want_a))
+    idx = kbit.unpack(want_w, K, n)
+    assert np.array_equal(ref[2], np_bits(nested.dequantize(idx, code_np, a2_np, off, q, codebooks.nf(K), B,
+                                                            "bf16")))
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    scratch = torch.empty_like(packed)
+    for r in range(4):
+        case(f"graph: replay {r}")
+        packed.zero_()
+        absmax.zero_()
+        out.zero_()
+        kb.quantize_kbit(A, cb, K, B, packed=scratch)     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(packed), ref[0]), r
+        assert np.array_equal(bits(absmax), ref[1]), r
+        assert np.array_equal(bits(out), ref[2]), r
