@@ -36,12 +36,13 @@
  *     every group g of 32 consecutive elements there are K uint32 words;
  *     bit t of word g*K + j is bit j of the K-bit index of element 32*g + t.
  *     Bits of positions past n are 0.  packed holds ceil(n/32)*K words.
- *   - Alignment: element arrays (A, out, X) and packed must be 16-byte
- *     aligned, float/uint8 side arrays 4-byte aligned (codes: 1 byte);
- *     otherwise KBIT_EALIGN.
+ *   - Alignment: element arrays (A, out, X) must be 16-byte aligned;
+ *     packed, sign_bits and the float arrays 4-byte aligned; absmax_code
+ *     (bytes) has no requirement.  Otherwise KBIT_EALIGN.
  *   - Floating point: IEEE binary32 with round to nearest even, no fused
  *     multiply-add, subnormals kept; narrowing to fp16/bf16 rounds to
- *     nearest even.  Results are bit-identical to the CPU oracle.
+ *     nearest even.  Every result is the one the definitions above fix,
+ *     bit for bit (no tolerance).
  *   - Limits: n <= 2^40 elements (KBIT_EINVAL beyond).
  *   - Calls on different streams may run concurrently (no shared state).
  */

@@ -21,7 +21,8 @@ All values are computed in float64 and rounded once to float32.
     FP4 (E2M1) magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6} with both signs, divided
     by 6 in float32 (one rounding of the exact rational).  Index order: the
     eight negatives (-6 .. -0) then the eight positives (+0 .. +6).  The FP4
-    format is named by [PR2051] Summary; its values are this build's reading.
+    format is named by [PR2051] Summary, which prints no table; the values and
+    their order are a reading of that name (standard E2M1 magnitudes).
 
 ``lloyd_max_normal(L)``
     The L-level minimum-MSE (Lloyd-Max) quantizer of N(0,1), found by the
