@@ -66,14 +66,17 @@ struct Tables {
     u32x4 master[kBuckets];
     float code_lo[kBuckets];        // codes of the two candidate indices
     float code_hi[kBuckets];
+    float code[32];                 // the codebook (exact path)
     int fail;
 };
 
+// First-index nearest code by a full scan.  c is the codebook in LDS; the
+// loop stays rolled so that the rare exact path keeps no codebook registers.
 template <int C>
-__device__ __forceinline__ uint32_t nearest_scan(const float (&c)[C], float xn) {
+__device__ __forceinline__ uint32_t nearest_scan(const float* c, float xn) {
     uint32_t best = 0;
     float bd = fabsf(xn - c[0]);
-#pragma unroll
+#pragma unroll 1
     for (int i = 1; i < C; ++i) {
         const float d = fabsf(xn - c[i]);
         if (d < bd) {
@@ -84,6 +87,9 @@ __device__ __forceinline__ uint32_t nearest_scan(const float (&c)[C], float xn) 
     return best;
 }
 
+// The fast path's precondition: values in [-1, 1] (so no NaN) and
+// non-decreasing.  Prologue only: the register copy of the codebook dies
+// before the main loop.
 template <int C>
 __device__ __forceinline__ bool codebook_is_sorted_unit(const float (&c)[C]) {
     bool ok = true;
@@ -135,7 +141,7 @@ __device__ bool build_entry(const float (&c)[1 << K], int j, u32x4& e, float& cl
     clo = c[0];
     chi = c[0];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
+    for (int i = 1; i < C; ++i) {
         if (static_cast<uint32_t>(i) == below) clo = c[i];
         if (static_cast<uint32_t>(i) == above) chi = c[i];
     }
@@ -156,15 +162,17 @@ __device__ __forceinline__ void shift_down8(float (&y)[8]) {
     for (int i = 0; i < 7; ++i) y[i] = y[i + 1];
 }
 
+// c: the codebook in LDS (this path is rare; registers stay free for the
+// fast path).
 template <int K>
-__device__ __forceinline__ Codes classify_exact(const float (&c)[1 << K], const float (&x)[8], float s) {
+__device__ __forceinline__ Codes classify_exact(const float* c, const float (&x)[8], float s) {
     Codes r;
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = x[i];
 #pragma unroll 1
     for (int t = 0; t < 8; ++t) {
-        const uint32_t idx = nearest_scan(c, y[0] / s);
+        const uint32_t idx = nearest_scan<1 << K>(c, y[0] / s);
         r.acc |= spread4(idx & 15u) << t;
         if constexpr (K == 5) r.acc4 |= ((idx >> 4) & 1u) << t;
         shift_down8(y);
@@ -224,15 +232,15 @@ __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, flo
 // and store the quad's plane words.  FULL: all 512 elements of the wave row
 // are below n (no masking, every store unconditional).
 template <class E, int K, bool FULL>
-__device__ __forceinline__ void encode_row(const float (&c)[1 << K], bool fast, const Tables& T, const char* tab,
+__device__ __forceinline__ void encode_row(bool fast, const Tables& T, const char* tab,
                                            uint32_t lane_off, int lane, const float (&x)[8], float m,
                                            int64_t row_base, int64_t n, uint32_t* __restrict__ packed) {
-    const float s = (m < kAbsmaxEps) ? kAbsmaxEps : m;  // NaN stays NaN (exact path)
+    const float s = __builtin_elementwise_maximum(m, kAbsmaxEps);  // NaN stays NaN (exact path)
     Codes cd;
     if (fast && !__builtin_amdgcn_ballot_w64(!(s < kMaxFastScale))) {
         cd = classify_fast<K>(x, s, __builtin_amdgcn_rcpf(s) * kSlope, tab, T, lane_off);
     } else {
-        cd = classify_exact<K>(c, x, s);
+        cd = classify_exact<K>(T.code, x, s);
     }
     bool live = true;
     if constexpr (!FULL) {
@@ -243,7 +251,8 @@ __device__ __forceinline__ void encode_row(const float (&c)[1 << K], bool fast, 
         live = row_base + (lane >> 2) * kGroup < n;
     }
     const uint32_t word = quad_transpose_bytes(cd.acc, lane);
-    uint32_t* dst = packed + (row_base / kGroup) * K + (lane >> 2) * K;
+    uint32_t* dst_row = packed + (row_base / kGroup) * K;  // wave-uniform
+    uint32_t* dst = dst_row + (lane >> 2) * K;
     const int l = lane & 3;
     if (K == 4 ? live : (l < K && live)) dst[l] = word;
     if constexpr (K == 5) {
@@ -254,29 +263,55 @@ __device__ __forceinline__ void encode_row(const float (&c)[1 << K], bool fast, 
     }
 }
 
+// The 8 elements of lane offset `off` from a wave-uniform row pointer; for
+// partial rows `rem` is the number of valid elements from `p` on (elements
+// past it read as 0).
 template <class E, bool NT>
-__device__ __forceinline__ void load_row(const typename E::storage* __restrict__ A, int64_t e0, int64_t n, bool full,
+__device__ __forceinline__ void load_row(const typename E::storage* __restrict__ p, int off, int64_t rem, bool full,
                                          u32x4 (&raw)[E::kVec]) {
     if (full) {
 #pragma unroll
-        for (int v = 0; v < E::kVec; ++v) raw[v] = load16<NT>(A + e0 + v * (16 / E::kBytes));
+        for (int v = 0; v < E::kVec; ++v) raw[v] = load16<NT>(p + off + v * (16 / E::kBytes));
     } else {
-        E::load_partial(A, e0, n, raw);
+        E::load_partial(p, off, rem, raw);
     }
 }
 
+// Max of |x| over the lane's 8 values and then over aligned runs of LANES
+// lanes (4..64).  IEEE maximum (v_maximum3_f32) propagates NaN; across lanes
+// the max is taken on the bits, which order non-negative floats (and put
+// NaN above infinity) exactly as their values.
+template <int LANES>
+__device__ __forceinline__ float block_max_abs(const float (&x)[8]);
+
 // Max magnitude over aligned runs of `lanes` lanes (4..64), as an integer.
-__device__ __forceinline__ uint32_t run_max_u32(uint32_t m, int lanes) {
+template <int LANES>
+__device__ __forceinline__ uint32_t run_max_u32(uint32_t m) {
     m = max(m, dpp_u32<kDppXor1>(m));
     m = max(m, dpp_u32<kDppXor2>(m));
-    if (lanes >= 8) m = max(m, dpp_u32<kDppHalfMirror>(m));
-    if (lanes >= 16) m = max(m, dpp_u32<kDppMirror>(m));
-    if (lanes >= 32) m = max(m, shfl_xor_u32(m, 16));
-    if (lanes >= 64) m = max(m, shfl_xor_u32(m, 32));
+    if constexpr (LANES >= 8) m = max(m, dpp_u32<kDppHalfMirror>(m));
+    if constexpr (LANES >= 16) m = max(m, dpp_u32<kDppMirror>(m));
+    if constexpr (LANES >= 32) m = max(m, shfl_xor_u32(m, 16));
+    if constexpr (LANES >= 64) m = max(m, shfl_xor_u32(m, 32));
     return m;
 }
 
-template <class E, int K, bool WIDE, int ROWS, bool PF, bool NT, int THREADS>
+
+__device__ __forceinline__ float lane_max_abs(const float (&x)[8]) {
+    auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+    const float a = mx(mx(fabsf(x[0]), fabsf(x[1])), fabsf(x[2]));
+    const float b = mx(mx(fabsf(x[3]), fabsf(x[4])), fabsf(x[5]));
+    return mx(mx(fabsf(x[6]), fabsf(x[7])), mx(a, b));
+}
+
+template <int LANES>
+__device__ __forceinline__ float block_max_abs(const float (&x)[8]) {
+    return __uint_as_float(run_max_u32<LANES>(__float_as_uint(lane_max_abs(x))));
+}
+
+// LOG2B = log2(B) for B <= 512 (blocks inside a wave row); LOG2B = 0 for
+// B = 1024..4096 (blocks spanning rows; log2B from the argument).
+template <class E, int K, int LOG2B, int ROWS, bool NT, int THREADS, int PFD>
 __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restrict__ cb,
                                                              const typename E::storage* __restrict__ A,
                                                              float* __restrict__ absmax,
@@ -286,11 +321,30 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     constexpr int kWaves_ = THREADS / kWave;
     __shared__ Tables T;
 
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves_;
+
+    // Row-tile geometry (B <= 512) and the wave's first loads, issued before
+    // the table build so that their latency overlaps it.
+    constexpr int kStep = kWaveTile * ROWS;
+    const int64_t nfull = LOG2B != 0 ? n / kStep : 0;
+    const int lane_e = lane * kElemsPerLane;
+    int64_t st = static_cast<int64_t>(blockIdx.x) * kWaves_ + wave;
+    u32x4 ra[ROWS][kV], rb[ROWS][kV];
+    auto load_full = [&](int64_t i, u32x4 (&r)[ROWS][kV]) {
+        const typename E::storage* src = A + i * kStep;  // wave-uniform
+#pragma unroll
+        for (int u = 0; u < ROWS; ++u) load_row<E, NT>(src + u * kWaveTile, lane_e, n, true, r[u]);
+    };
+    if (LOG2B != 0 && st < nfull) load_full(st, ra);
+
     float c[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) c[i] = cb[i];
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
+    if (threadIdx.x < C) T.code[threadIdx.x] = c[threadIdx.x];
     __syncthreads();
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
@@ -307,27 +361,19 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     }
     __syncthreads();
 
-    const int lane = __lane_id();
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
     const char* tab = reinterpret_cast<const char*>(T.row);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves_;
 
-    if constexpr (!WIDE) {
+    if constexpr (LOG2B != 0) {
+        static_assert(LOG2B >= 5 && LOG2B <= 9, "rows hold whole blocks of 32..512");
         // Steps of ROWS wave rows (512 elements each); blocks of B <= 512
-        // lie inside a row.  Full steps run with the next step's rows in
-        // flight (the prefetch index is clamped so the load is always
-        // issued); the one partial step, if any, goes last.
-        constexpr int kStep = kWaveTile * ROWS;
-        const int lpb = (1 << log2B) >> 3;
+        // lie inside a row.  Full steps alternate between two register
+        // buffers: the next step's rows load while this step's are
+        // classified (the prefetch index is clamped, so the load is always
+        // issued and the loop has no data-dependent branches).  The one
+        // partial step, if any, goes last.
+        constexpr int kLpb = (1 << LOG2B) / kElemsPerLane;  // lanes per block
         const int64_t nsteps = (n + kStep - 1) / kStep;
-        const int64_t nfull = n / kStep;
-        const int64_t lane_e = static_cast<int64_t>(lane) * kElemsPerLane;
-        int64_t st = static_cast<int64_t>(blockIdx.x) * kWaves_ + wave;
-        auto load_step = [&](int64_t i, bool full, u32x4 (&r)[ROWS][kV]) {
-#pragma unroll
-            for (int u = 0; u < ROWS; ++u) load_row<E, NT>(A, i * kStep + u * kWaveTile + lane_e, n, full, r[u]);
-        };
         auto do_step = [&](int64_t i, const u32x4 (&r)[ROWS][kV], auto full_tag) {
             constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
@@ -335,33 +381,49 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
                 const int64_t base = i * kStep + u * kWaveTile;
                 float x[8];
                 E::unpack(r[u], x);
-                const float m = E::mag_to_float(run_max_u32(E::max_mag(r[u]), lpb));
-                const int64_t e0 = base + lane_e;
-                if (kFull || ((lane & (lpb - 1)) == 0 && e0 < n)) absmax[e0 >> log2B] = m;
-                encode_row<E, K, kFull>(c, fast, T, tab, lane_off, lane, x, m, base, n, packed);
+                const float m = block_max_abs<kLpb>(x);
+                float* am = absmax + (base >> LOG2B);  // wave-uniform
+                if (kFull || ((lane & (kLpb - 1)) == 0 && base + lane_e < n)) am[lane_e >> LOG2B] = m;
+                encode_row<E, K, kFull>(fast, T, tab, lane_off, lane, x, m, base, n, packed);
             }
         };
         if (st < nfull) {
-            u32x4 raw[ROWS][kV];
-            load_step(st, true, raw);
-            for (; st < nfull; st += nwaves) {
-                u32x4 nxt[ROWS][kV];
-                if constexpr (PF) load_step(min(st + nwaves, nfull - 1), true, nxt);
-                do_step(st, raw, std::true_type{});
-                if constexpr (PF) {
-#pragma unroll
-                    for (int u = 0; u < ROWS; ++u)
-#pragma unroll
-                        for (int v = 0; v < kV; ++v) raw[u][v] = nxt[u][v];
-                } else if (st + nwaves < nfull) {
-                    load_step(st + nwaves, true, raw);
+            if constexpr (PFD == 1) {
+                while (true) {
+                    load_full(min(st + nwaves, nfull - 1), rb);
+                    do_step(st, ra, std::true_type{});
+                    st += nwaves;
+                    if (st >= nfull) break;
+                    load_full(min(st + nwaves, nfull - 1), ra);
+                    do_step(st, rb, std::true_type{});
+                    st += nwaves;
+                    if (st >= nfull) break;
+                }
+            } else {
+                // two steps in flight: three buffers in rotation
+                u32x4 rc[ROWS][kV];
+                load_full(min(st + nwaves, nfull - 1), rb);
+                while (true) {
+                    load_full(min(st + 2 * nwaves, nfull - 1), rc);
+                    do_step(st, ra, std::true_type{});
+                    st += nwaves;
+                    if (st >= nfull) break;
+                    load_full(min(st + 2 * nwaves, nfull - 1), ra);
+                    do_step(st, rb, std::true_type{});
+                    st += nwaves;
+                    if (st >= nfull) break;
+                    load_full(min(st + 2 * nwaves, nfull - 1), rb);
+                    do_step(st, rc, std::true_type{});
+                    st += nwaves;
+                    if (st >= nfull) break;
                 }
             }
         }
         if (st == nfull && nfull < nsteps) {
-            u32x4 raw[ROWS][kV];
-            load_step(st, false, raw);
-            do_step(st, raw, std::false_type{});
+            u32x4 r[ROWS][kV];
+#pragma unroll
+            for (int u = 0; u < ROWS; ++u) load_row<E, false>(A + st * kStep + u * kWaveTile, lane_e, n - (st * kStep + u * kWaveTile), false, r[u]);
+            do_step(st, r, std::false_type{});
         }
     } else {
         // One block of B = 1024..4096 per step: max over its rows, then
@@ -370,44 +432,47 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
         const int64_t nblocks = (n + (1LL << log2B) - 1) >> log2B;
         for (int64_t b = static_cast<int64_t>(blockIdx.x) * kWaves_ + wave; b < nblocks; b += nwaves) {
             const int64_t base = b << log2B;
-            uint32_t mb = 0;
+            float ml = 0.0f;
             for (int u = 0; u < rows; ++u) {
-                const int64_t e0 = base + u * kWaveTile + lane * kElemsPerLane;
+                const int64_t rb = base + u * kWaveTile;
                 u32x4 raw[kV];
-                load_row<E, false>(A, e0, n, e0 + kElemsPerLane <= n, raw);
-                mb = max(mb, E::max_mag(raw));
+                load_row<E, false>(A + rb, lane * kElemsPerLane, n - rb, rb + kWaveTile <= n, raw);
+                float x[8];
+                E::unpack(raw, x);
+                ml = __builtin_elementwise_maximum(ml, lane_max_abs(x));
             }
-            mb = run_max_u32(mb, kWave);
-            const float m = E::mag_to_float(mb);
+            const float m = __uint_as_float(run_max_u32<kWave>(__float_as_uint(ml)));
             if (lane == 0) absmax[b] = m;
             for (int u = 0; u < rows; ++u) {
                 const int64_t rb = base + u * kWaveTile;
                 if (rb >= n) break;
-                const int64_t e0 = rb + lane * kElemsPerLane;
                 u32x4 raw[kV];
-                load_row<E, false>(A, e0, n, e0 + kElemsPerLane <= n, raw);
+                load_row<E, false>(A + rb, lane * kElemsPerLane, n - rb, rb + kWaveTile <= n, raw);
                 float x[8];
                 E::unpack(raw, x);
-                encode_row<E, K, false>(c, fast, T, tab, lane_off, lane, x, m, rb, n, packed);
+                encode_row<E, K, false>(fast, T, tab, lane_off, lane, x, m, rb, n, packed);
             }
         }
     }
 }
 
-template <class E, int K, bool WIDE, int ROWS = 1, bool PF = true, bool NT = false, int THREADS = kQThreads>
+// grid_mult > 1 launches that many times the resident number of
+// workgroups (each then walks fewer steps).
+template <class E, int K, int LOG2B, int ROWS = 1, bool NT = true, int THREADS = kQThreads, int PFD = 1>
 int launch_cfg(const float* cb, const void* A, float* absmax, uint32_t* packed, int64_t n, int log2B,
-               void* stream) {
-    auto kern = quantize_kernel<E, K, WIDE, ROWS, PF, NT, THREADS>;
+               void* stream, int grid_mult = 1) {
+    auto kern = quantize_kernel<E, K, LOG2B, ROWS, NT, THREADS, PFD>;
     static int blocks_per_cu = 0;
     if (blocks_per_cu == 0) {
         int b = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, THREADS, 0) != hipSuccess || b < 1) b = 1;
         blocks_per_cu = b;
     }
-    const int64_t units = WIDE ? ((n + (1LL << log2B) - 1) >> log2B) : (n + kWaveTile * ROWS - 1) / (kWaveTile * ROWS);
+    const int64_t units = LOG2B == 0 ? ((n + (1LL << log2B) - 1) >> log2B)
+                                     : (n + kWaveTile * ROWS - 1) / (kWaveTile * ROWS);
     constexpr int waves = THREADS / kWave;
     int64_t grid = (units + waves - 1) / waves;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu * grid_mult;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(THREADS), 0,
@@ -419,11 +484,19 @@ int launch_cfg(const float* cb, const void* A, float* absmax, uint32_t* packed, 
 template <class E, int K>
 int launch_k(const float* cb, const void* A, float* absmax, uint32_t* packed, int64_t n, int log2B,
              void* stream) {
-    if (log2B > 9) return launch_cfg<E, K, true>(cb, A, absmax, packed, n, log2B, stream);
     // Two wave rows per step for bf16 (32 bytes per lane in flight plus the
     // prefetched step) where that still fits 64 VGPRs; one row otherwise.
-    constexpr int kRows = (std::is_same<E, Bf16>::value && K <= 4) ? 2 : 1;
-    return launch_cfg<E, K, false, kRows, true, true>(cb, A, absmax, packed, n, log2B, stream);
+    // K = 5 needs about 80 VGPRs: 512-thread groups keep 6 waves per SIMD.
+    constexpr int R = (std::is_same<E, Bf16>::value && K <= 4) ? 2 : 1;
+    constexpr int TH = K == 5 ? 512 : kQThreads;
+    switch (log2B) {
+        case 5: return launch_cfg<E, K, 5, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 6: return launch_cfg<E, K, 6, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 7: return launch_cfg<E, K, 7, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 8: return launch_cfg<E, K, 8, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 9: return launch_cfg<E, K, 9, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        default: return launch_cfg<E, K, 0, 1, false, TH>(cb, A, absmax, packed, n, log2B, stream);
+    }
 }
 
 template <class E>
