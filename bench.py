@@ -5,15 +5,18 @@ blocksize 64) followed by the nested 4-bit dequantize of those planes back to
 bf16 (per-block scales rebuilt from 8-bit codes over groups of 256 plus a
 mean offset), on an 8192 x 8192 weight drawn from N(0, 0.02).  Inputs live in
 HBM before timing starts.  Several buffer sets are rotated so that the
-256 MB last-level cache cannot hold a step's working set.  Each set's step
-is captured once into a HIP graph and the timed loop replays the graphs.
+256 MB last-level cache cannot hold a step's working set.  One step per
+buffer set is captured into a single HIP graph and the timed loop replays
+it (steps must be a multiple of the number of sets).
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (read +
 written by both kernels) divided by the wall time per step, in GB/s.
-Per-kernel launch times come from HIP events around graph replays that run
-one kernel back to back over all buffer sets, on the stream the kernels run
-on.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload (N = 1 only).
+Per-kernel launch times (the ``roofline`` object) come from HIP events
+around eager bursts of one kernel over all buffer sets, on the stream the
+kernels run on.  The same line also reports the FP4 codebook, warm-cache
+numbers and the W4A4 activation path (4096 x 4096 bf16) as side
+measurements.  ``cpu_baseline`` times the CPU oracle on a bounded sample of
+the same workload (N = 1 only).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--sets 4]
                     [--no-cpu-baseline] [--copy-calibration]
@@ -56,6 +59,9 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-act", action="store_true", help="skip the activation-path timing")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the NF4 step and its two kernels (what the profiles cover)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help=f"after timing, run {CAL_COPIES} plain device copies of {CAL_BYTES >> 20} MiB "
@@ -84,11 +90,11 @@ KERNELS = {
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o trace -- "
-    "python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline --copy-calibration",
+    "python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline --headline-only --copy-calibration",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o fetch -- "
-    "python3 $R/bench.py --steps 6 --warmup 2 --no-cpu-baseline --copy-calibration",
+    "python3 $R/bench.py --steps 8 --warmup 4 --no-cpu-baseline --headline-only --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o write -- "
-    "python3 $R/bench.py --steps 6 --warmup 2 --no-cpu-baseline --copy-calibration",
+    "python3 $R/bench.py --steps 8 --warmup 4 --no-cpu-baseline --headline-only --copy-calibration",
     "cd $R && python3 bench.py --summarize gpurun_out/prof_trace gpurun_out/prof_fetch gpurun_out/prof_write",
 ]
 
@@ -209,10 +215,65 @@ def cpu_baseline(seconds_target):
     }
 
 
+ACT_ROWS = ACT_D = 4096
+ACT_FLOPS_PER_ELEM = 15          # 12 butterfly add/sub + square + add (norm tree) + divide
+VALU_FP32_PEAK_TFLOPS = 157.3    # 256 CUs x 4 SIMDs x 32 fp32 lanes (packed) x 2 x 2.4 GHz
+
+
+def act_bytes(rows=ACT_ROWS, d=ACT_D):
+    """Algorithmic bytes of one activation-path launch: bf16 in, sign mask,
+    16 centroids, 4 bit-planes per 32 and one fp32 norm per row out."""
+    n = rows * d
+    return 2 * n + d // 8 + 64 + (n // 32) * 4 * 4 + 4 * rows
+
+
+def bench_act(torch, kb, synth, dev, reps, sets=12):
+    """Timing of the W4A4 activation assignment on 4096 x 4096 bf16
+    (rows N(0,1) x 10^U(-1,1), shared sign mask, Lloyd-Max-16)."""
+    x, signs = synth.activations_bf16(ACT_ROWS, ACT_D)
+    cbl = torch.from_numpy(kb.codebook_lloyd_max_normal(16)).to(dev)
+    sg = torch.from_numpy(signs.view(np.int32)).to(dev)
+    x0 = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    bufs = [(x0 if i == 0 else x0.clone(),
+             torch.empty(ACT_ROWS, dtype=torch.float32, device=dev),
+             torch.empty(kb.n_words(ACT_ROWS * ACT_D, 4), dtype=torch.int32, device=dev)) for i in range(sets)]
+    torch.cuda.synchronize()
+
+    def run(b):
+        kb.quantize_act_fwht_k4_bf16(b[0], sg, cbl, row_norm=b[1], packed=b[2])
+
+    for _ in range(3):
+        for b in bufs:
+            run(b)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        for b in bufs:
+            run(b)
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    ts = np.array([ev[r].elapsed_time(ev[r + 1]) / sets for r in range(reps)])
+    avg = float(ts.mean())
+    nbytes = act_bytes()
+    flops = ACT_FLOPS_PER_ELEM * ACT_ROWS * ACT_D
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    tflops = flops / (avg * 1e-3) / 1e12
+    return {"workload": "4096 x 4096 bf16 activations, Lloyd-Max-16, K=4 planes, 12 rotated buffer sets",
+            "avg_us": round(avg * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
+            "bytes": nbytes, "GB/s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "algorithmic_flops": flops, "TFLOP/s": round(tflops, 3),
+            "frac_of_fp32_valu_peak": round(tflops / VALU_FP32_PEAK_TFLOPS, 4),
+            "rows_per_s": round(ACT_ROWS / (avg * 1e-3), 1)}
+
+
 def main(argv=None):
     args = parse(argv)
     if args.summarize:
         return summarize(*args.summarize)
+    if args.steps % args.sets:
+        print(f"--steps ({args.steps}) must be a multiple of --sets ({args.sets})", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the hot path has no "
               "cross-GPU step to measure here.", file=sys.stderr)
@@ -260,9 +321,9 @@ def main(argv=None):
         step(s_)
     torch.cuda.synchronize()
 
-    # The step's two launches are captured once per buffer set into a HIP
-    # graph, so the timed loop measures the GPU rather than Python's launch
-    # path (the kernels allocate nothing and take the capture stream).
+    # The steps are captured into a HIP graph, so the timed loop measures the
+    # GPU rather than Python's launch path (the kernels allocate nothing and
+    # take the capture stream).
     def capture(fn, items):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -270,11 +331,11 @@ def main(argv=None):
                 fn(s_)
         return g
 
-    g_step = [capture(step, [s_]) for s_ in sets]
-    g_quant = capture(quant_only, sets)          # one launch per set, back to back
-    g_nested = capture(nested_only, sets)
-    for i in range(args.warmup):
-        g_step[i % args.sets].replay()
+    # One graph holds one step per buffer set (quantize, nested dequantize,
+    # then the next set), so a replay is args.sets steps.
+    g_steps = capture(step, sets)
+    for i in range(-(-args.warmup // args.sets)):
+        g_steps.replay()
     torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -282,44 +343,65 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        g_step[i % args.sets].replay()
+    for i in range(args.steps // args.sets):
+        g_steps.replay()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
 
-    # Per-kernel launch time: bursts of the same kernel (graph replays),
-    # HIP events on the stream the kernels run on.
-    def burst(g, launches_per_replay, reps):
-        times = []
-        for _ in range(reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / launches_per_replay)
-        return times
+    # Per-kernel launch time: eager bursts of one kernel over all buffer
+    # sets, HIP events on the stream the kernels run on (torch's current
+    # stream, which the binding passes to every launch).
+    def burst(fn, reps, warm=3):
+        for _ in range(warm):
+            for s_ in sets:
+                fn(s_)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for r in range(reps):
+            for s_ in sets:
+                fn(s_)
+            ev[r + 1].record()
+        torch.cuda.synchronize()
+        return [ev[r].elapsed_time(ev[r + 1]) / len(sets) for r in range(reps)]
 
-    reps = max(3, args.steps // args.sets)
-    tq = burst(g_quant, args.sets, reps)
-    tn = burst(g_nested, args.sets, reps)
+    reps = max(5, args.steps // args.sets)
+    tq = burst(quant_only, reps)
+    tn = burst(nested_only, reps)
     qbytes, nbytes = algorithmic_bytes(n)
     ms_step = wall * 1e3 / args.steps
     value = (qbytes + nbytes) / (ms_step * 1e-3) / 1e9
 
-    def kstats(ts, nbytes_):
+    def kstats(ts, nbytes_, elems=n):
         ts = np.array(ts)
         avg = float(ts.mean())
         gbps = nbytes_ / (avg * 1e-3) / 1e9
         return {"avg_us": round(avg * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
                 "min_us": round(float(ts.min()) * 1e3, 3), "max_us": round(float(ts.max()) * 1e3, 3),
                 "bytes": nbytes_, "GB/s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                "elements_per_s": round(n / (avg * 1e-3), 1)}
+                "elements_per_s": round(elems / (avg * 1e-3), 1)}
 
     kq, kn = kstats(tq, qbytes), kstats(tn, nbytes)
+
+    # The same two kernels with the FP4 codebook, and warm numbers (one
+    # buffer set over and over, so the last-level cache holds most of it).
+    fp4 = warm = act = None
+    if not args.headline_only:
+        cb_nf = cb
+        cb = torch.from_numpy(kb.codebook_fp4()).to(dev)
+        fp4 = {"quantize_kbit_bf16_k4": kstats(burst(quant_only, reps), qbytes),
+               "dequantize_4bit_nested_bf16": kstats(burst(nested_only, reps), nbytes)}
+        cb = cb_nf
+        warm_sets, sets = sets, sets[:1]
+        warm = {"quantize_kbit_bf16_k4": kstats(burst(quant_only, reps), qbytes),
+                "dequantize_4bit_nested_bf16": kstats(burst(nested_only, reps), nbytes),
+                "note": "same buffer set every launch (warm cache); not the headline number"}
+        sets = warm_sets
+        if not args.no_act:
+            act = bench_act(torch, kb, synth, dev, reps)
+
     dom_name, dom = ("quantize_kbit_bf16_k4", kq) if kq["avg_us"] >= kn["avg_us"] else \
         ("dequantize_4bit_nested_bf16", kn)
     traffic = None
@@ -365,6 +447,9 @@ def main(argv=None):
                    "buffer_sets": args.sets, "step_bytes": qbytes + nbytes},
         "quantize": kq,
         "nested_dequantize": kn,
+        "fp4_codebook": fp4,
+        "warm": warm,
+        "act_fwht": act,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -20,20 +20,25 @@
 //     lanes.  Blocks of 1024..4096 span 2..8 wave tiles: the wave reduces
 //     over them first and re-reads them (from L2) to classify.
 //   * Nearest code without a division per element.  For a sorted codebook
-//     the first-index argmin rule is a step function of x_n that can change
-//     only near the midpoints of distinct neighbouring codes.  Each element
-//     computes q = fma(x, 0.99*rcp(s), 2.99 + 2^-10), an approximation of an
-//     affine image of x_n that lies in (2, 4), so bits 16..22 of q (its top 7
-//     mantissa bits) pick one of 128 equal buckets.  A bucket's table entry
-//     holds the one midpoint whose window [t - d, t + d] (d = 2^-18) meets
-//     the bucket, and the bit-plane bytes of the indices on either side.
-//     Outside the window the comparison q >= t decides exactly as the
-//     definition does (the combined error of q, t and the roundings in the
-//     definition is below 2^-20); inside it the element is redone exactly
-//     (IEEE division, then the two candidate codes compared as the
-//     definition compares them).  Codebooks that are unsorted, leave
-//     [-1, 1], or put two windows into one bucket, and blocks whose scale is
-//     not finite or above 2^125, take the exact path: division and the full
+//     whose distinct neighbours are at least 2^-16 apart, the first-index
+//     argmin rule picks, between two neighbouring codes c_lo < c_hi, the
+//     upper one exactly when x_n >= u for one fp32 value u (the rule is
+//     monotone in x_n).  The prologue finds each u by bisecting the fp32
+//     values between the two codes with the rule itself, and turns it
+//     into a test on x and s: RN(x/s) >= u  <=>  x - M*s > 0, with M the
+//     midpoint of u and its fp32 predecessor, nudged by a few fp64 ulps to
+//     encode the round-to-even direction of an exact tie.  M*s has at most
+//     49 significant bits, so one fp64 fma gives the sign of x - M*s
+//     exactly, and the nudge is far below the smallest nonzero |x - M*s|.
+//     To know which threshold to test, each element computes
+//     q = fma(x, 0.99*rcp(s), 2.99 + 2^-10), an approximation of an affine
+//     image of x_n inside (2, 4); bits 16..22 of q pick one of 128 buckets.
+//     A bucket's entry holds the M of the one threshold whose window
+//     [t - 2^-18, t + 2^-18] (in q) meets the bucket (q's error is below
+//     2^-21) and the plane bytes of the indices on either side.  Codebooks
+//     that are unsorted, leave [-1, 1], have close distinct neighbours, or
+//     put two windows into one bucket, and blocks whose scale is not finite
+//     or above 2^125, take the exact path: IEEE division and the full
 //     first-index scan.
 //   * The table sits in LDS with each bucket row replicated 16 times (16
 //     bytes per copy), and lane l reads copy l mod 16: the 16 lanes served
@@ -57,19 +62,17 @@ constexpr int kCopies = 16;
 constexpr float kAbsmaxEps = 1e-8f;
 constexpr float kSlope = 0.99f;                          // q = kBase + kSlope * x_n
 constexpr float kBase = 2.0f + kSlope + 0x1p-10f;        // keeps q inside (2, 4)
-constexpr float kDelta = 0x1p-18f;                       // decision window half-width in q
-constexpr float kSentinel = 8.0f;                        // a threshold q never reaches
+constexpr float kDelta = 0x1p-18f;                       // bucket window half-width in q
+constexpr float kMinGap = 0x1p-16f;                      // closest distinct neighbours (fast path)
 constexpr float kMaxFastScale = 0x1p125f;
 
 struct Tables {
-    u32x4 row[kBuckets * kCopies];  // {t - d, t + d, planes(below), planes(above)} per copy
+    u32x4 row[kBuckets * kCopies];  // {M (fp64 bits), planes(below), planes(above)} per copy
     u32x4 master[kBuckets];
-    float code_lo[kBuckets];        // codes of the two candidate indices
-    float code_hi[kBuckets];
+    uint64_t mid[32];               // per threshold i (between codes i-1 and i): M as fp64 bits
     float code[32];                 // the codebook (exact path)
     int fail;
 };
-
 // First-index nearest code by a full scan.  c is the codebook in LDS; the
 // loop stays rolled so that the rare exact path keeps no codebook registers.
 template <int C>
@@ -87,32 +90,72 @@ __device__ __forceinline__ uint32_t nearest_scan(const float* c, float xn) {
     return best;
 }
 
-// The fast path's precondition: values in [-1, 1] (so no NaN) and
-// non-decreasing.  Prologue only: the register copy of the codebook dies
-// before the main loop.
+// The fast path's precondition: values in [-1, 1] (so no NaN), non-
+// decreasing, and distinct neighbours at least kMinGap apart (so that no
+// third code can tie with the two around a threshold).  Prologue only: the
+// register copy of the codebook dies before the main loop.
 template <int C>
 __device__ __forceinline__ bool codebook_is_sorted_unit(const float (&c)[C]) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < C; ++i) ok = ok && (c[i] >= -1.0f) && (c[i] <= 1.0f);
 #pragma unroll
-    for (int i = 1; i < C; ++i) ok = ok && (c[i] >= c[i - 1]);
+    for (int i = 1; i < C; ++i) ok = ok && ((c[i] == c[i - 1]) || (c[i] - c[i - 1] >= kMinGap));
     return ok;
 }
 
-// Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)).  For K = 5 the least
-// significant bits of the two window bounds carry plane 4 of the two
-// indices (moving a bound by one ulp of q, 2^-22, leaves the window far
-// wider than the error it covers).  Returns false if two windows meet the
-// bucket.
+// fp32 values in the order of their keys: key(-0) + 1 = key(+0).
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The definition's choice between neighbouring codes lo < hi (lower index
+// wins ties).
+__device__ __forceinline__ bool upper_wins(float xn, float lo, float hi) {
+    return fabsf(xn - hi) < fabsf(xn - lo);
+}
+
+// fp64 bits of M for the threshold between codes lo < hi: RN(x/s) >= u
+// <=> x - M*s > 0 (s > 0).  The choice is monotone in x_n on [lo, hi], so u
+// is found by bisection over the fp32 values in between (at most 32 steps;
+// near a midpoint of 0 it can lie far from the midpoint, where the rounded
+// distances tie).  Returns false if the bracket is not as expected.
+__device__ bool threshold_mid(float lo, float hi, uint64_t& bits) {
+    uint32_t L = order_key(lo), R = order_key(hi);
+    if (upper_wins(lo, lo, hi) || !upper_wins(hi, lo, hi)) return false;
+    while (R - L > 1u) {
+        const uint32_t m = L + (R - L) / 2u;
+        if (upper_wins(from_key(m), lo, hi)) R = m;
+        else L = m;
+    }
+    const float u = from_key(R);
+    const double M = (static_cast<double>(u) + static_cast<double>(from_key(L))) * 0.5;  // exact
+    // An exact tie x/s == M rounds to the even one of pred(u), u: to u means
+    // "upper" at equality, so M moves down by 4 fp64 ulps; otherwise it moves
+    // up (or stays).  Bits 1:0 stay free for the plane-4 flags of K = 5.
+    const bool tie_up = static_cast<float>(M) == u;
+    uint64_t b = static_cast<uint64_t>(__double_as_longlong(M));
+    if (M > 0.0) b = tie_up ? b - 4u : b;
+    else b = tie_up ? b + 4u : b - 4u;
+    bits = b & ~static_cast<uint64_t>(3u);
+    return true;
+}
+
+// Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
+// threshold whose window meets the bucket (mid[i] from the prologue), the
+// plane bytes of the indices below and above it, and for K = 5 their plane-4
+// bits in bits 0 and 1 of M.  Returns false if two windows meet the bucket.
 template <int K>
-__device__ bool build_entry(const float (&c)[1 << K], int j, u32x4& e, float& clo, float& chi) {
+__device__ bool build_entry(const float (&c)[1 << K], const uint64_t* mid, int j, u32x4& e) {
     constexpr int C = 1 << K;
     const float lo = 2.0f + static_cast<float>(j) * (2.0f / kBuckets);
     const float hi = lo + (2.0f / kBuckets);
     uint32_t below = 0;
     int cand = -1;
-    float cand_t = kSentinel;
     bool ok = true;
 #pragma unroll
     for (int i = 1; i < C; ++i) {
@@ -121,30 +164,15 @@ __device__ bool build_entry(const float (&c)[1 << K], int j, u32x4& e, float& cl
             if (t + kDelta <= lo) {
                 below = i;
             } else if (t - kDelta < hi) {
-                if (cand < 0) {
-                    cand = i;
-                    cand_t = t;
-                } else {
-                    ok = false;
-                }
+                if (cand < 0) cand = i;
+                else ok = false;
             }
         }
     }
     const uint32_t above = cand < 0 ? below : static_cast<uint32_t>(cand);
-    uint32_t tlo = __float_as_uint(cand < 0 ? kSentinel : cand_t - kDelta);
-    uint32_t thi = __float_as_uint(cand < 0 ? kSentinel : cand_t + kDelta);
-    if constexpr (K == 5) {
-        tlo = (tlo & ~1u) | ((below >> 4) & 1u);
-        thi = (thi & ~1u) | ((above >> 4) & 1u);
-    }
-    e = u32x4{tlo, thi, spread4(below & 15u), spread4(above & 15u)};
-    clo = c[0];
-    chi = c[0];
-#pragma unroll
-    for (int i = 1; i < C; ++i) {
-        if (static_cast<uint32_t>(i) == below) clo = c[i];
-        if (static_cast<uint32_t>(i) == above) chi = c[i];
-    }
+    uint64_t m = cand < 0 ? 0u : mid[cand];
+    if constexpr (K == 5) m |= ((below >> 4) & 1u) | (((above >> 4) & 1u) << 1);
+    e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), spread4(below & 15u), spread4(above & 15u)};
     return ok;
 }
 
@@ -187,43 +215,19 @@ __device__ __forceinline__ uint32_t entry_addr(float q, uint32_t lane_off) {
 
 template <int K>
 __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, float r, const char* tab,
-                                               const Tables& T, uint32_t lane_off) {
+                                               uint32_t lane_off) {
     Codes out;
-    bool near = false;
+    const double s64 = static_cast<double>(s);
     // Elements 7..0: each step shifts the accumulated plane bits up by one,
     // so element t ends at bit t of every plane byte.
 #pragma unroll
     for (int t = 7; t >= 0; --t) {
         const float q = __builtin_fmaf(x[t], r, kBase);
         const u32x4 e = *reinterpret_cast<const u32x4*>(tab + entry_addr(q, lane_off));
-        const bool clo = q >= __uint_as_float(e[0]);
-        const bool chi = q >= __uint_as_float(e[1]);
-        near = near | (clo != chi);
-        out.acc = (out.acc << 1) | (chi ? e[3] : e[2]);
-        if constexpr (K == 5) out.acc4 = (out.acc4 << 1) | ((chi ? e[1] : e[0]) & 1u);
-    }
-    if (__builtin_amdgcn_ballot_w64(near)) {
-        // Redo the elements inside a window exactly: only the two codes on
-        // either side of the window's midpoint can be nearest there.  One
-        // element per iteration keeps this rare path's registers low.
-        float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = x[i];
-#pragma unroll 1
-        for (int t = 0; t < 8; ++t) {
-            const float xt = y[0];
-            shift_down8(y);
-            const float q = __builtin_fmaf(xt, r, kBase);
-            const uint32_t a = entry_addr(q, lane_off);
-            const u32x4 e = *reinterpret_cast<const u32x4*>(tab + a);
-            if ((q >= __uint_as_float(e[0])) != (q >= __uint_as_float(e[1]))) {
-                const uint32_t j = a >> 8;
-                const float xn = xt / s;
-                const bool up = fabsf(xn - T.code_hi[j]) < fabsf(xn - T.code_lo[j]);
-                out.acc = (out.acc & ~(0x01010101u << t)) | ((up ? e[3] : e[2]) << t);
-                if constexpr (K == 5) out.acc4 = (out.acc4 & ~(1u << t)) | (((up ? e[1] : e[0]) & 1u) << t);
-            }
-        }
+        const double M = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(e[1]) << 32) | e[0]));
+        const bool up = __builtin_fma(-M, s64, static_cast<double>(x[t])) > 0.0;
+        out.acc = (out.acc << 1) | (up ? e[3] : e[2]);
+        if constexpr (K == 5) out.acc4 = (out.acc4 << 1) | ((e[0] >> (up ? 1 : 0)) & 1u);
     }
     return out;
 }
@@ -238,7 +242,7 @@ __device__ __forceinline__ void encode_row(bool fast, const Tables& T, const cha
     const float s = __builtin_elementwise_maximum(m, kAbsmaxEps);  // NaN stays NaN (exact path)
     Codes cd;
     if (fast && !__builtin_amdgcn_ballot_w64(!(s < kMaxFastScale))) {
-        cd = classify_fast<K>(x, s, __builtin_amdgcn_rcpf(s) * kSlope, tab, T, lane_off);
+        cd = classify_fast<K>(x, s, __builtin_amdgcn_rcpf(s) * kSlope, tab, lane_off);
     } else {
         cd = classify_exact<K>(T.code, x, s);
     }
@@ -344,15 +348,18 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     for (int i = 0; i < C; ++i) c[i] = cb[i];
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
-    if (threadIdx.x < C) T.code[threadIdx.x] = c[threadIdx.x];
+    if (threadIdx.x < C) {
+        T.code[threadIdx.x] = c[threadIdx.x];
+        const int i = threadIdx.x;
+        uint64_t m = 0;
+        if (fast && i > 0 && c[i] != c[i - 1] && !threshold_mid(c[i - 1], c[i], m)) T.fail = 1;
+        T.mid[i] = m;
+    }
     __syncthreads();
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
-        float lo, hi;
-        if (!build_entry<K>(c, threadIdx.x, e, lo, hi)) T.fail = 1;
+        if (!build_entry<K>(c, T.mid, threadIdx.x, e)) T.fail = 1;
         T.master[threadIdx.x] = e;
-        T.code_lo[threadIdx.x] = lo;
-        T.code_hi[threadIdx.x] = hi;
     }
     __syncthreads();
     fast = fast && (T.fail == 0);
