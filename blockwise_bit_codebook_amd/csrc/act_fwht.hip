@@ -13,30 +13,67 @@
 //           unnormalised natural-order Hadamard butterfly, each output
 //           rounded to fp32
 //   z     = RN(u / max(norm, 1e-10f));  idx = first-index argmin |RN(z - c_i)|
+//   packed: 4 bit-plane words per 32 elements along the row.
 //
-// How: one workgroup of 256 threads per row; thread t owns the 16
-// contiguous elements [16t, 16t+16).  The norm tree is thread-local for the
+// How: a workgroup of 512 threads works on two rows at a time (256 threads
+// per row, 16 elements per thread).  The norm tree is thread-local for the
 // 4 lowest levels, DPP/bpermute across lanes for the next 6 (pairing
 // contiguous halves, so every partial is the same tree node as in the
-// definition) and LDS across the 4 waves.  Butterfly stages h <= 8 run in
-// registers; stages h >= 16 exchange whole 16-element runs through LDS.
-// Every butterfly within a stage is independent, so the result does not
-// depend on the order in which a stage's butterflies run.
+// definition) and LDS across the 4 waves of the row.  The 12 butterfly
+// stages run in registers as three 16-point passes over the index bits
+// 0-3, 4-7 and 8-11: between passes the row goes through LDS (padded by 16
+// floats per 256 so that the strided reads are conflict-free) and each
+// thread picks up the 16 elements that differ in the next 4 bits.  Every
+// butterfly of a stage is independent and the stages keep their order, so
+// the result is the definition's.  The row then goes back to contiguous
+// order for the assignment, which uses the exact switching-point test of
+// threshold.h (q clamped into [2, 4); |z| <= 64 always, since
+// |u| <= sqrt(4096)*norm): one LDS entry read and one fp64 fma per element.
+// Rows whose norm is not finite, and codebooks that do not qualify, take
+// the exact path (IEEE division and the full scan).
 #include "device.h"
 #include "kbit_internal.h"
 #include "launch.h"
+#include "threshold.h"
 
 namespace kbit {
 namespace {
 
 constexpr int kD = 4096;
-constexpr int kPer = kD / kThreads;  // 16 elements per thread
+constexpr int kRowThreads = 256;
+constexpr int kPer = kD / kRowThreads;  // 16 elements per thread
+constexpr int kSlotsDefault = 2;        // rows in flight per workgroup
 constexpr float kActEps = 1e-10f;
+constexpr float kZRange = 4.0f;                      // thresholds must lie inside (-4, 4)
+constexpr float kActSlope = 0.99f / kZRange;         // q = kActBase + kActSlope * z
+constexpr float kActBase = 3.0f + 0x1p-10f;
+constexpr float kActMinGap = 0x1p-12f;               // |z| <= 64: distances round at <= 2^-17
+constexpr float kQMax = 0x1.fffffep+1f;              // largest float below 4
+constexpr int kBufFloats = kD + (kD / 256) * 16;     // padded row buffer
 
-__device__ __forceinline__ uint32_t nearest16(const float (&c)[16], float z) {
+__device__ __forceinline__ int pad(int e) { return e + ((e >> 8) << 4); }
+
+using ActTables = ThresholdTables<16>;
+
+// In-register 16-point butterfly passes: stages h = 1, 2, 4, 8 of v's index.
+__device__ __forceinline__ void fwht16(float (&v)[kPer]) {
+#pragma unroll
+    for (int h = 1; h < kPer; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if ((j & h) == 0) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t nearest16_lds(const float* c, float z) {
     uint32_t best = 0;
     float bd = fabsf(z - c[0]);
-#pragma unroll
+#pragma unroll 1
     for (int i = 1; i < 16; ++i) {
         const float d = fabsf(z - c[i]);
         if (d < bd) {
@@ -47,114 +84,216 @@ __device__ __forceinline__ uint32_t nearest16(const float (&c)[16], float z) {
     return best;
 }
 
-__global__ __launch_bounds__(kThreads) void act_fwht_kernel(const uint16_t* __restrict__ X, int64_t rows,
-                                                            const uint32_t* __restrict__ sign_bits,
-                                                            const float* __restrict__ cb,
-                                                            float* __restrict__ row_norm,
-                                                            uint32_t* __restrict__ packed) {
-    __shared__ float4 buf[kD / 4];
-    __shared__ float wave_sum[kWavesPerGroup];
-    __shared__ alignas(16) uint8_t idx_lds[kD];
+template <int kSlots>
+__global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const uint16_t* __restrict__ X, int64_t rows,
+                                                               const uint32_t* __restrict__ sign_bits,
+                                                               const float* __restrict__ cb,
+                                                               float* __restrict__ row_norm,
+                                                               uint32_t* __restrict__ packed) {
+    constexpr int kActThreads = kRowThreads * kSlots;
+    __shared__ ActTables T;
+    __shared__ alignas(16) float buf[kSlots][kBufFloats];
+    __shared__ float wave_sum[kSlots][kRowThreads / kWave];
 
+    const int slot = threadIdx.x / kRowThreads;
+    const int t = threadIdx.x % kRowThreads;
+    const int lane = __lane_id();
+    const int wave = t / kWave;
+
+    // ---- table build (once per workgroup) ---------------------------------
     float c[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = cb[i];
+    bool fast = true;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) fast = fast && (c[i] == c[i - 1] || c[i] - c[i - 1] >= kActMinGap);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        const float m = (c[i - 1] + c[i]) * 0.5f;
+        fast = fast && (c[i] == c[i - 1] || (m > -0.97f * kZRange && m < 0.97f * kZRange));
+    }
+    if (threadIdx.x == 0) T.fail = 0;
+    if (threadIdx.x < 16) {
+        const int i = threadIdx.x;
+        T.code[i] = c[i];
+        uint64_t m = 0;
+        if (fast && i > 0 && c[i] != c[i - 1] && !threshold_mid(c[i - 1], c[i], m)) T.fail = 1;
+        T.mid[i] = m;
+    }
+    __syncthreads();
+    if (fast && threadIdx.x < kBuckets) {
+        u32x4 e;
+        if (!build_entry<16, false>(c, T.mid, threadIdx.x, kActSlope, kActBase, e)) T.fail = 1;
+        T.master[threadIdx.x] = e;
+    }
+    __syncthreads();
+    fast = fast && (T.fail == 0);
+    if (fast) {
+        for (int i = threadIdx.x; i < kBuckets * kCopies; i += kActThreads) T.row[i] = T.master[i / kCopies];
+    }
+    __syncthreads();
 
-    const int t = threadIdx.x;
-    const int lane = __lane_id();
-    const int wave = t >> 6;
+    const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
+    const char* tab = reinterpret_cast<const char*>(T.row);
+    // Sign flips as XOR masks on the raw bf16 words: element 2i is the low
+    // half of word i (sign bit 15), element 2i+1 the high half (bit 31).
     const uint32_t signs = (sign_bits[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+    uint32_t flip[kPer / 2];
+#pragma unroll
+    for (int i = 0; i < kPer / 2; ++i)
+        flip[i] = (((signs >> (2 * i)) & 1u) << 15) | (((signs >> (2 * i + 1)) & 1u) << 31);
+    const int hi4 = t >> 4, lo4 = t & 15;
 
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const uint16_t* xr = X + row * kD + t * kPer;
-        float u[kPer];
+    // Every thread runs the same number of iterations (barriers inside);
+    // a slot past the last row computes on zeros and stores nothing.
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kSlots; base < rows;
+         base += static_cast<int64_t>(gridDim.x) * kSlots) {
+        const int64_t row = base + slot;
+        const bool valid = row < rows;
+        float* rb = buf[slot];
+        float* ws = wave_sum[slot];
+        float v[kPer];
         {
-            const uint4 a = *reinterpret_cast<const uint4*>(xr);
-            const uint4 b = *reinterpret_cast<const uint4*>(xr + 8);
-            const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+            if (valid) {
+                const uint16_t* xr = X + row * kD + t * kPer;
+                a = *reinterpret_cast<const uint4*>(xr);
+                b = *reinterpret_cast<const uint4*>(xr + 8);
+            }
+            const uint32_t w[8] = {a.x ^ flip[0], a.y ^ flip[1], a.z ^ flip[2], a.w ^ flip[3],
+                                   b.x ^ flip[4], b.y ^ flip[5], b.z ^ flip[6], b.w ^ flip[7]};
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                u[2 * i] = __uint_as_float(w[i] << 16);
-                u[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+                v[2 * i] = __uint_as_float(w[i] << 16);
+                v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
             }
+            // --- norm: tree over contiguous halves (a flipped sign does not
+            // change a square) ----------------------------------------------
+            float q[kPer];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) q[i] = v[i] * v[i];
+#pragma unroll
+            for (int wd = kPer; wd > 1; wd >>= 1)
+#pragma unroll
+                for (int i = 0; i < wd / 2; ++i) q[i] = q[2 * i] + q[2 * i + 1];
+            float S = q[0];
+            S = S + dpp_f32<kDppXor1>(S);
+            S = S + dpp_f32<kDppXor2>(S);
+            S = S + dpp_f32<kDppHalfMirror>(S);
+            S = S + dpp_f32<kDppMirror>(S);
+            S = S + shfl_xor_f32(S, 16);
+            S = S + shfl_xor_f32(S, 32);
+            if (lane == 0) ws[wave] = S;
         }
-        // --- norm: tree over contiguous halves -------------------------
-        float q[kPer];
+        // --- pass 1 (bits 0-3), to LDS -----------------------------------------
+        fwht16(v);
+        {
+            float4* p = reinterpret_cast<float4*>(rb + pad(t * kPer));
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) q[i] = u[i] * u[i];
-#pragma unroll
-        for (int w = kPer; w > 1; w >>= 1)
-#pragma unroll
-            for (int i = 0; i < w / 2; ++i) q[i] = q[2 * i] + q[2 * i + 1];
-        float S = q[0];
-        S = S + dpp_f32<kDppXor1>(S);
-        S = S + dpp_f32<kDppXor2>(S);
-        S = S + dpp_f32<kDppHalfMirror>(S);
-        S = S + dpp_f32<kDppMirror>(S);
-        S = S + shfl_xor_f32(S, 16);
-        S = S + shfl_xor_f32(S, 32);
-        if (lane == 0) wave_sum[wave] = S;
-        // --- sign flip and in-register stages h = 1, 2, 4, 8 ------------
-#pragma unroll
-        for (int i = 0; i < kPer; ++i)
-            if ((signs >> i) & 1u) u[i] = -u[i];
-#pragma unroll
-        for (int h = 1; h < kPer; h <<= 1) {
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                if ((j & h) == 0) {
-                    const float a = u[j], b = u[j + h];
-                    u[j] = a + b;
-                    u[j + h] = a - b;
-                }
-            }
+            for (int k = 0; k < 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
         }
-        __syncthreads();  // wave_sum visible; buf free
-        const float norm = sqrtf((wave_sum[0] + wave_sum[1]) + (wave_sum[2] + wave_sum[3]));
-        // --- stages h = 16 .. 2048 through LDS --------------------------
-#pragma unroll 1
-        for (int hp = 1; hp < kThreads; hp <<= 1) {  // partner thread distance h / 16
+        __syncthreads();
+        const float norm = sqrtf((ws[0] + ws[1]) + (ws[2] + ws[3]));
+        // --- pass 2 (bits 4-7): elements hi4*256 + i*16 + lo4 ---------------
+        {
+            const int b0 = pad(hi4 * 256 + lo4);
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                buf[t * 4 + k] = make_float4(u[4 * k], u[4 * k + 1], u[4 * k + 2], u[4 * k + 3]);
-            __syncthreads();
-            const int p = t ^ hp;
-            const bool low = (t & hp) == 0;
+            for (int i = 0; i < kPer; ++i) v[i] = rb[b0 + i * 16];
+            fwht16(v);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) rb[b0 + i * 16] = v[i];
+        }
+        __syncthreads();
+        // --- pass 3 (bits 8-11): elements i*256 + t --------------------------
+        {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) v[i] = rb[i * 272 + t];
+            fwht16(v);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) rb[i * 272 + t] = v[i];
+        }
+        __syncthreads();
+        // --- back to contiguous order: elements 16t .. 16t+15 ---------------
+        {
+            const float4* p = reinterpret_cast<const float4*>(rb + pad(t * kPer));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float4 o = buf[p * 4 + k];
-                const float ov[4] = {o.x, o.y, o.z, o.w};
+                const float4 f = p[k];
+                v[4 * k] = f.x;
+                v[4 * k + 1] = f.y;
+                v[4 * k + 2] = f.z;
+                v[4 * k + 3] = f.w;
+            }
+        }
+        // --- assignment: two 8-element plane accumulators -------------------
+        const float den = fmaxf(norm, kActEps);
+        uint32_t acc[2] = {0u, 0u};
+        if (fast && __builtin_amdgcn_ballot_w64(!(norm < __builtin_inff())) == 0) {
+            const float r = __builtin_amdgcn_rcpf(den) * kActSlope;
+            const double d64 = static_cast<double>(den);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float self = u[4 * k + m];
-                    u[4 * k + m] = low ? (self + ov[m]) : (ov[m] - self);
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int k = 7; k >= 0; --k) {
+                    const float z = v[8 * h + k];
+                    const float q = __builtin_amdgcn_fmed3f(__builtin_fmaf(z, r, kActBase), 2.0f, kQMax);
+                    const Decision d = decide(z, q, d64, tab, lane_off);
+                    acc[h] = (acc[h] << 1) | (d.up ? d.e[3] : d.e[2]);
                 }
             }
-            __syncthreads();
-        }
-        // --- divide and assign -----------------------------------------
-        const float den = fmaxf(norm, kActEps);
+        } else {
+            // one element per iteration (rare path): rotate a copy so that
+            // the element in use is always y[0]
+            float y[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) idx_lds[t * kPer + i] = static_cast<uint8_t>(nearest16(c, u[i] / den));
-        if (t == 0) row_norm[row] = norm;
-        __syncthreads();
-        // --- pack: chunk k = 8 elements, lanes of a quad share a group --
+            for (int i = 0; i < kPer; ++i) y[i] = v[i];
+#pragma unroll 1
+            for (int k = 0; k < kPer; ++k) {
+                acc[k >> 3] |= spread4(nearest16_lds(T.code, y[0] / den)) << (k & 7);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int chunk = half * kThreads + t;
-            const uint2 b8 = *reinterpret_cast<const uint2*>(&idx_lds[chunk * 8]);
-            uint32_t acc = 0;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                acc |= spread4((b8.x >> (8 * s)) & 15u) << s;
-                acc |= spread4((b8.y >> (8 * s)) & 15u) << (s + 4);
+                for (int i = 0; i < kPer - 1; ++i) y[i] = y[i + 1];
             }
-            const uint32_t word = quad_transpose_bytes(acc, lane);
-            const int64_t g = row * (kD / kGroup) + (chunk >> 2);
-            packed[g * 4 + (lane & 3)] = word;
         }
-        __syncthreads();  // idx_lds reused by the next row
+        // --- pack: lanes 2g, 2g+1 hold the 32 elements of group g ------------
+        {
+            // per lane: plane j's 16 bits = [acc0 byte j, acc1 byte j]
+            const uint32_t h01 = __builtin_amdgcn_perm(acc[1], acc[0], 0x05010400u);
+            const uint32_t h23 = __builtin_amdgcn_perm(acc[1], acc[0], 0x07030602u);
+            const bool odd = (t & 1) != 0;
+            const uint32_t mine = odd ? h23 : h01;
+            const uint32_t recv = dpp_u32<kDppXor1>(odd ? h01 : h23);
+            const uint32_t lo = odd ? recv : mine, hi = odd ? mine : recv;  // even lane's half first
+            const uint2 words = make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05040100u),
+                                           __builtin_amdgcn_perm(hi, lo, 0x07060302u));
+            if (valid) {
+                uint32_t* dst = packed + row * (kD / kGroup) * 4 + (t >> 1) * 4 + (t & 1) * 2;
+                dst[0] = words.x;
+                dst[1] = words.y;
+                if (t == 0) row_norm[row] = norm;
+            }
+        }
+        __syncthreads();  // the row buffer and wave sums are reused
     }
+}
+
+template <int kSlots>
+int launch_act_slots(const uint16_t* X, int64_t rows, const uint32_t* sign_bits, const float* codebook16,
+                     float* row_norm, uint32_t* packed, void* stream) {
+    constexpr int kActThreads = kRowThreads * kSlots;
+    auto kern = act_fwht_kernel<kSlots>;
+    static int blocks_per_cu = 0;
+    if (blocks_per_cu == 0) {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, kActThreads, 0) != hipSuccess || b < 1) b = 1;
+        blocks_per_cu = b;
+    }
+    int64_t grid = (rows + kSlots - 1) / kSlots;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kActThreads), 0,
+                       static_cast<hipStream_t>(stream), X, rows, sign_bits, codebook16, row_norm, packed);
+    return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace
@@ -162,11 +301,7 @@ __global__ __launch_bounds__(kThreads) void act_fwht_kernel(const uint16_t* __re
 int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream) {
     (void)d;
-    static int blocks_per_cu = 0;
-    int64_t grid = persistent_grid(act_fwht_kernel, blocks_per_cu, rows * kWavesPerGroup);
-    hipLaunchKernelGGL(act_fwht_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), X, rows, sign_bits, codebook16, row_norm, packed);
-    return static_cast<int>(hipGetLastError());
+    return launch_act_slots<kSlotsDefault>(X, rows, sign_bits, codebook16, row_norm, packed, stream);
 }
 
 }  // namespace kbit

@@ -50,6 +50,7 @@
 //     tile's load in flight while the current one is classified.
 #include "device.h"
 #include "kbit_internal.h"
+#include "threshold.h"
 
 #include <type_traits>
 
@@ -57,22 +58,13 @@ namespace kbit {
 namespace {
 
 constexpr int kQThreads = 1024;
-constexpr int kBuckets = 128;
-constexpr int kCopies = 16;
 constexpr float kAbsmaxEps = 1e-8f;
 constexpr float kSlope = 0.99f;                          // q = kBase + kSlope * x_n
 constexpr float kBase = 2.0f + kSlope + 0x1p-10f;        // keeps q inside (2, 4)
-constexpr float kDelta = 0x1p-18f;                       // bucket window half-width in q
 constexpr float kMinGap = 0x1p-16f;                      // closest distinct neighbours (fast path)
 constexpr float kMaxFastScale = 0x1p125f;
 
-struct Tables {
-    u32x4 row[kBuckets * kCopies];  // {M (fp64 bits), planes(below), planes(above)} per copy
-    u32x4 master[kBuckets];
-    uint64_t mid[32];               // per threshold i (between codes i-1 and i): M as fp64 bits
-    float code[32];                 // the codebook (exact path)
-    int fail;
-};
+using Tables = ThresholdTables<32>;
 // First-index nearest code by a full scan.  c is the codebook in LDS; the
 // loop stays rolled so that the rare exact path keeps no codebook registers.
 template <int C>
@@ -101,78 +93,6 @@ __device__ __forceinline__ bool codebook_is_sorted_unit(const float (&c)[C]) {
     for (int i = 0; i < C; ++i) ok = ok && (c[i] >= -1.0f) && (c[i] <= 1.0f);
 #pragma unroll
     for (int i = 1; i < C; ++i) ok = ok && ((c[i] == c[i - 1]) || (c[i] - c[i - 1] >= kMinGap));
-    return ok;
-}
-
-// fp32 values in the order of their keys: key(-0) + 1 = key(+0).
-__device__ __forceinline__ uint32_t order_key(float v) {
-    const uint32_t b = __float_as_uint(v);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float from_key(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// The definition's choice between neighbouring codes lo < hi (lower index
-// wins ties).
-__device__ __forceinline__ bool upper_wins(float xn, float lo, float hi) {
-    return fabsf(xn - hi) < fabsf(xn - lo);
-}
-
-// fp64 bits of M for the threshold between codes lo < hi: RN(x/s) >= u
-// <=> x - M*s > 0 (s > 0).  The choice is monotone in x_n on [lo, hi], so u
-// is found by bisection over the fp32 values in between (at most 32 steps;
-// near a midpoint of 0 it can lie far from the midpoint, where the rounded
-// distances tie).  Returns false if the bracket is not as expected.
-__device__ bool threshold_mid(float lo, float hi, uint64_t& bits) {
-    uint32_t L = order_key(lo), R = order_key(hi);
-    if (upper_wins(lo, lo, hi) || !upper_wins(hi, lo, hi)) return false;
-    while (R - L > 1u) {
-        const uint32_t m = L + (R - L) / 2u;
-        if (upper_wins(from_key(m), lo, hi)) R = m;
-        else L = m;
-    }
-    const float u = from_key(R);
-    const double M = (static_cast<double>(u) + static_cast<double>(from_key(L))) * 0.5;  // exact
-    // An exact tie x/s == M rounds to the even one of pred(u), u: to u means
-    // "upper" at equality, so M moves down by 4 fp64 ulps; otherwise it moves
-    // up (or stays).  Bits 1:0 stay free for the plane-4 flags of K = 5.
-    const bool tie_up = static_cast<float>(M) == u;
-    uint64_t b = static_cast<uint64_t>(__double_as_longlong(M));
-    if (M > 0.0) b = tie_up ? b - 4u : b;
-    else b = tie_up ? b + 4u : b - 4u;
-    bits = b & ~static_cast<uint64_t>(3u);
-    return true;
-}
-
-// Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
-// threshold whose window meets the bucket (mid[i] from the prologue), the
-// plane bytes of the indices below and above it, and for K = 5 their plane-4
-// bits in bits 0 and 1 of M.  Returns false if two windows meet the bucket.
-template <int K>
-__device__ bool build_entry(const float (&c)[1 << K], const uint64_t* mid, int j, u32x4& e) {
-    constexpr int C = 1 << K;
-    const float lo = 2.0f + static_cast<float>(j) * (2.0f / kBuckets);
-    const float hi = lo + (2.0f / kBuckets);
-    uint32_t below = 0;
-    int cand = -1;
-    bool ok = true;
-#pragma unroll
-    for (int i = 1; i < C; ++i) {
-        if (c[i] != c[i - 1]) {
-            const float t = kBase + ((c[i - 1] + c[i]) * 0.5f) * kSlope;
-            if (t + kDelta <= lo) {
-                below = i;
-            } else if (t - kDelta < hi) {
-                if (cand < 0) cand = i;
-                else ok = false;
-            }
-        }
-    }
-    const uint32_t above = cand < 0 ? below : static_cast<uint32_t>(cand);
-    uint64_t m = cand < 0 ? 0u : mid[cand];
-    if constexpr (K == 5) m |= ((below >> 4) & 1u) | (((above >> 4) & 1u) << 1);
-    e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), spread4(below & 15u), spread4(above & 15u)};
     return ok;
 }
 
@@ -208,10 +128,6 @@ __device__ __forceinline__ Codes classify_exact(const float* c, const float (&x)
     return r;
 }
 
-__device__ __forceinline__ uint32_t entry_addr(float q, uint32_t lane_off) {
-    // byte 1 <- bits 16..23 of q (bucket; bit 23 is 0 for q in [2, 4)), byte 0 <- lane offset
-    return __builtin_amdgcn_perm(lane_off, __float_as_uint(q), 0x0C0C0204u);
-}
 
 template <int K>
 __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, float r, const char* tab,
@@ -222,12 +138,9 @@ __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, flo
     // so element t ends at bit t of every plane byte.
 #pragma unroll
     for (int t = 7; t >= 0; --t) {
-        const float q = __builtin_fmaf(x[t], r, kBase);
-        const u32x4 e = *reinterpret_cast<const u32x4*>(tab + entry_addr(q, lane_off));
-        const double M = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(e[1]) << 32) | e[0]));
-        const bool up = __builtin_fma(-M, s64, static_cast<double>(x[t])) > 0.0;
-        out.acc = (out.acc << 1) | (up ? e[3] : e[2]);
-        if constexpr (K == 5) out.acc4 = (out.acc4 << 1) | ((e[0] >> (up ? 1 : 0)) & 1u);
+        const Decision d = decide(x[t], __builtin_fmaf(x[t], r, kBase), s64, tab, lane_off);
+        out.acc = (out.acc << 1) | (d.up ? d.e[3] : d.e[2]);
+        if constexpr (K == 5) out.acc4 = (out.acc4 << 1) | ((d.e[0] >> (d.up ? 1 : 0)) & 1u);
     }
     return out;
 }
@@ -358,7 +271,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     __syncthreads();
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
-        if (!build_entry<K>(c, T.mid, threadIdx.x, e)) T.fail = 1;
+        if (!build_entry<C, K == 5>(c, T.mid, threadIdx.x, kSlope, kBase, e)) T.fail = 1;
         T.master[threadIdx.x] = e;
     }
     __syncthreads();

@@ -1,0 +1,134 @@
+// Exact nearest-code decisions without a per-element division, shared by
+// the blockwise quantizer and the activation assignment.
+//
+// For a sorted codebook whose distinct neighbours are far apart compared
+// with the rounding of the distances involved, the first-index argmin of
+// |RN(v - c_i)| picks, between neighbouring codes lo < hi, the upper one
+// exactly when v >= u for one fp32 value u (the rule is monotone in v).
+// With v = RN(x/s), s > 0:  v >= u  <=>  x - M*s > 0,  where M is the
+// midpoint of u and its fp32 predecessor (nudged by a few fp64 ulps for the
+// round-to-even direction of an exact tie).  M*s has at most 49 significant
+// bits, so one fp64 fma gives the sign exactly.
+//
+// Which threshold applies is found from q = fma(x, slope*rcp(s), base), an
+// approximation of base + slope*v inside [2, 4): bits 16..22 of q pick one
+// of 128 buckets, and a bucket's 16-byte entry holds the M of the one
+// threshold whose window [t - 2^-18, t + 2^-18] meets it (t = base +
+// slope*midpoint; the error of q is far below 2^-18) and the plane bytes of
+// the indices on either side of it.  Each bucket row is replicated 16 times
+// in LDS and lane l reads copy l mod 16, so the 16 lanes served per LDS
+// cycle never share a bank; one v_perm_b32 forms the address.
+#pragma once
+
+#include "device.h"
+
+namespace kbit {
+
+constexpr int kBuckets = 128;
+constexpr int kCopies = 16;
+constexpr float kDelta = 0x1p-18f;  // bucket window half-width in q
+
+// Bucket rows, their master copy, and the per-threshold M (fp64 bits).
+template <int C>
+struct ThresholdTables {
+    u32x4 row[kBuckets * kCopies];  // {M, planes(below), planes(above)} per copy
+    u32x4 master[kBuckets];
+    uint64_t mid[C];                // mid[i]: threshold between codes i-1 and i
+    float code[C];                  // the codebook (exact path)
+    int fail;
+};
+
+// fp32 values in the order of their keys: key(-0) + 1 = key(+0).
+__device__ __forceinline__ uint32_t order_key(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The definition's choice between neighbouring codes lo < hi (lower index
+// wins ties).
+__device__ __forceinline__ bool upper_wins(float xn, float lo, float hi) {
+    return fabsf(xn - hi) < fabsf(xn - lo);
+}
+
+// fp64 bits of M for the threshold between codes lo < hi: RN(x/s) >= u
+// <=> x - M*s > 0 (s > 0).  The choice is monotone in x_n on [lo, hi], so u
+// is found by bisection over the fp32 values in between (at most 32 steps;
+// near a midpoint of 0 it can lie far from the midpoint, where the rounded
+// distances tie).  Returns false if the bracket is not as expected.
+__device__ inline bool threshold_mid(float lo, float hi, uint64_t& bits) {
+    uint32_t L = order_key(lo), R = order_key(hi);
+    if (upper_wins(lo, lo, hi) || !upper_wins(hi, lo, hi)) return false;
+    while (R - L > 1u) {
+        const uint32_t m = L + (R - L) / 2u;
+        if (upper_wins(from_key(m), lo, hi)) R = m;
+        else L = m;
+    }
+    const float u = from_key(R);
+    const double M = (static_cast<double>(u) + static_cast<double>(from_key(L))) * 0.5;  // exact
+    // An exact tie x/s == M rounds to the even one of pred(u), u: to u means
+    // "upper" at equality, so M moves down by 4 fp64 ulps; otherwise it moves
+    // up (or stays).  Bits 1:0 stay free for the plane-4 flags of K = 5.
+    const bool tie_up = static_cast<float>(M) == u;
+    uint64_t b = static_cast<uint64_t>(__double_as_longlong(M));
+    if (M > 0.0) b = tie_up ? b - 4u : b;
+    else b = tie_up ? b + 4u : b - 4u;
+    bits = b & ~static_cast<uint64_t>(3u);
+    return true;
+}
+
+// Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
+// threshold whose window meets the bucket (mid[i] from threshold_mid), the
+// plane bytes of the indices below and above it, and with PLANE4 their
+// plane-4 bits in bits 0 and 1 of M.  Returns false if two windows meet
+// the bucket.
+template <int C, bool PLANE4>
+__device__ bool build_entry(const float (&c)[C], const uint64_t* mid, int j, float slope, float base,
+                            u32x4& e) {
+    const float lo = 2.0f + static_cast<float>(j) * (2.0f / kBuckets);
+    const float hi = lo + (2.0f / kBuckets);
+    uint32_t below = 0;
+    int cand = -1;
+    bool ok = true;
+#pragma unroll
+    for (int i = 1; i < C; ++i) {
+        if (c[i] != c[i - 1]) {
+            const float t = base + ((c[i - 1] + c[i]) * 0.5f) * slope;
+            if (t + kDelta <= lo) {
+                below = i;
+            } else if (t - kDelta < hi) {
+                if (cand < 0) cand = i;
+                else ok = false;
+            }
+        }
+    }
+    const uint32_t above = cand < 0 ? below : static_cast<uint32_t>(cand);
+    uint64_t m = cand < 0 ? 0u : mid[cand];
+    if constexpr (PLANE4) m |= ((below >> 4) & 1u) | (((above >> 4) & 1u) << 1);
+    e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), spread4(below & 15u), spread4(above & 15u)};
+    return ok;
+}
+
+// Byte address of the lane's copy of q's bucket entry: byte 1 <- bits
+// 16..23 of q (bucket; bit 23 is 0 for q in [2, 4)), byte 0 <- lane offset.
+__device__ __forceinline__ uint32_t entry_addr(float q, uint32_t lane_off) {
+    return __builtin_amdgcn_perm(lane_off, __float_as_uint(q), 0x0C0C0204u);
+}
+
+// The entry for q and the exact decision "upper code" for x against scale
+// s64 (= s as fp64).
+struct Decision {
+    u32x4 e;
+    bool up;
+};
+__device__ __forceinline__ Decision decide(float x, float q, double s64, const char* tab, uint32_t lane_off) {
+    Decision d;
+    d.e = *reinterpret_cast<const u32x4*>(tab + entry_addr(q, lane_off));
+    const double M = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(d.e[1]) << 32) | d.e[0]));
+    d.up = __builtin_fma(-M, s64, static_cast<double>(x)) > 0.0;
+    return d;
+}
+
+}  // namespace kbit
