@@ -7,9 +7,11 @@ forwards raw device pointers and the current HIP stream.  If the library has
 not been built, the first call raises ``ImportError``: there is no fallback.
 
 Entry points carry the C names (``quantize_kbit_bf16_k4``,
-``dequantize_4bit_nested_fp16``, ...) and a few dtype/K-dispatching
-conveniences (``quantize_kbit``, ``dequantize_kbit``,
-``dequantize_4bit_nested``, ``quantize_act_fwht_k4_bf16``).
+``quantize_kbit_e4m4_bf16_k4``, ``dequantize_4bit_nested_fp16``, ...) and a
+few dtype/K-dispatching conveniences (``quantize_kbit``, ``dequantize_kbit``,
+``dequantize_4bit_nested``, ``quantize_act_fwht_k4_bf16``).  The block scales
+are fp32 absmax values or, with ``absmax_format="e4m4"``, one E4M4 byte per
+block (uint8 tensor).
 """
 
 import ctypes as ct
@@ -108,28 +110,48 @@ def _stream(device):
     return ct.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def quantize_kbit(A, codebook, k, blocksize, absmax=None, packed=None):
-    """Quantize A (fp32/fp16/bf16 CUDA tensor, any shape) -> (packed int32, absmax fp32)."""
+def _scale_infix(absmax_format):
+    if absmax_format == "fp32":
+        return ""
+    if absmax_format == "e4m4":
+        return "e4m4_"
+    raise ValueError(f"absmax_format must be 'fp32' or 'e4m4', got {absmax_format!r}")
+
+
+def quantize_kbit(A, codebook, k, blocksize, absmax=None, packed=None, absmax_format="fp32"):
+    """Quantize A (fp32/fp16/bf16 CUDA tensor, any shape) -> (packed int32, absmax).
+
+    absmax is fp32, or uint8 E4M4 codes with ``absmax_format="e4m4"``."""
     torch = _torch()
     t = _dtype_name(A.dtype)
     n = A.numel()
+    infix = _scale_infix(absmax_format)
     if absmax is None:
-        absmax = torch.empty(n_blocks(n, blocksize), dtype=torch.float32, device=A.device)
+        absmax = torch.empty(n_blocks(n, blocksize), dtype=torch.uint8 if infix else torch.float32,
+                             device=A.device)
     if packed is None:
         packed = torch.empty(n_words(n, k), dtype=torch.int32, device=A.device)
-    name = f"quantize_kbit_{t}_k{k}"
+    name = f"quantize_kbit_{infix}{t}_k{k}"
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(codebook), _ptr(A), _ptr(absmax), _ptr(packed), n, blocksize, _stream(A.device)))
     return packed, absmax
 
 
 def dequantize_kbit(packed, codebook, absmax, k, n, dtype, blocksize, out=None):
-    """Dequantize bit-plane words -> tensor of n elements of ``dtype``."""
+    """Dequantize bit-plane words -> tensor of n elements of ``dtype``.
+
+    absmax: fp32 scales, or uint8 E4M4 codes (selects the E4M4 entry point)."""
     torch = _torch()
     t = _dtype_name(dtype)
+    if absmax.dtype == torch.uint8:
+        infix = "e4m4_"
+    elif absmax.dtype == torch.float32:
+        infix = ""
+    else:
+        raise TypeError(f"absmax must be float32 or uint8 (E4M4), got {absmax.dtype}")
     if out is None:
         out = torch.empty(n, dtype=dtype, device=packed.device)
-    name = f"dequantize_kbit_{t}_k{k}"
+    name = f"dequantize_kbit_{infix}{t}_k{k}"
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(packed), _ptr(codebook), _ptr(absmax), _ptr(out), n, blocksize, _stream(packed.device)))
     return out
@@ -185,6 +207,13 @@ def _install_named():
             g[f"dequantize_kbit_{t}_k{k}"] = _make_named(
                 f"dequantize_kbit_{t}_k{k}", lambda packed, codebook, absmax, n, blocksize, _k=k, _t=t, **kw:
                 dequantize_kbit(packed, codebook, absmax, _k, n, torch_dt(_t), blocksize, **kw))
+            g[f"quantize_kbit_e4m4_{t}_k{k}"] = _make_named(
+                f"quantize_kbit_e4m4_{t}_k{k}", lambda A, codebook, blocksize, _k=k, **kw:
+                quantize_kbit(A, codebook, _k, blocksize, absmax_format="e4m4", **kw))
+            g[f"dequantize_kbit_e4m4_{t}_k{k}"] = _make_named(
+                f"dequantize_kbit_e4m4_{t}_k{k}",
+                lambda packed, codebook, absmax_e4m4, n, blocksize, _k=k, _t=t, **kw:
+                dequantize_kbit(packed, codebook, absmax_e4m4, _k, n, torch_dt(_t), blocksize, **kw))
         g[f"dequantize_4bit_nested_{t}"] = _make_named(
             f"dequantize_4bit_nested_{t}",
             lambda packed, codebook16, absmax_code, qmap2, absmax2, offset, n, blocksize, _t=t, **kw:

@@ -34,6 +34,8 @@ def _signatures():
         for k in KS:
             sig.append((f"quantize_kbit_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
             sig.append((f"dequantize_kbit_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
+            sig.append((f"quantize_kbit_e4m4_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
+            sig.append((f"dequantize_kbit_e4m4_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
         sig.append((f"dequantize_4bit_nested_{t}", [_p, _p, _p, _p, _p, _f32, _p, _i64, _i32, _p]))
     return sig
 

@@ -50,30 +50,33 @@ int log2_block(int32_t blocksize) {
 
 int map_launch(int hip_status) { return hip_status == 0 ? KBIT_OK : KBIT_ELAUNCH; }
 
-int do_quantize(Dtype t, int K, const float* codebook, const void* A, float* absmax, uint32_t* packed,
-                int64_t n, int32_t blocksize, void* stream) {
+// fp32 scales need 4-byte alignment, E4M4 bytes none.
+bool scale_aligned(ScaleFmt f, const void* absmax) { return f == ScaleFmt::e4m4 || aligned(absmax, 4); }
+
+int do_quantize(Dtype t, ScaleFmt f, int K, const float* codebook, const void* A, void* absmax,
+                uint32_t* packed, int64_t n, int32_t blocksize, void* stream) {
     const int l2b = log2_block(blocksize);
     if (l2b < 0) return KBIT_EBLOCK;
     if (n < 0 || n > kMaxElems) return KBIT_EINVAL;
     if (n == 0) return KBIT_OK;
     if (!codebook || !A || !absmax || !packed) return KBIT_EINVAL;
-    if (!aligned(A, 16) || !aligned(codebook, 4) || !aligned(absmax, 4) || !aligned(packed, 4))
+    if (!aligned(A, 16) || !aligned(codebook, 4) || !scale_aligned(f, absmax) || !aligned(packed, 4))
         return KBIT_EALIGN;
     if (current_device_cus() <= 0) return KBIT_EDEVICE;
-    return map_launch(launch_quantize(t, K, codebook, A, absmax, packed, n, l2b, stream));
+    return map_launch(launch_quantize(t, f, K, codebook, A, absmax, packed, n, l2b, stream));
 }
 
-int do_dequantize(Dtype t, int K, const uint32_t* packed, const float* codebook, const float* absmax,
-                  void* out, int64_t n, int32_t blocksize, void* stream) {
+int do_dequantize(Dtype t, ScaleFmt f, int K, const uint32_t* packed, const float* codebook,
+                  const void* absmax, void* out, int64_t n, int32_t blocksize, void* stream) {
     const int l2b = log2_block(blocksize);
     if (l2b < 0) return KBIT_EBLOCK;
     if (n < 0 || n > kMaxElems) return KBIT_EINVAL;
     if (n == 0) return KBIT_OK;
     if (!packed || !codebook || !absmax || !out) return KBIT_EINVAL;
-    if (!aligned(out, 16) || !aligned(codebook, 4) || !aligned(absmax, 4) || !aligned(packed, 4))
+    if (!aligned(out, 16) || !aligned(codebook, 4) || !scale_aligned(f, absmax) || !aligned(packed, 4))
         return KBIT_EALIGN;
     if (current_device_cus() <= 0) return KBIT_EDEVICE;
-    return map_launch(launch_dequantize(t, K, packed, codebook, absmax, out, n, l2b, stream));
+    return map_launch(launch_dequantize(t, f, K, packed, codebook, absmax, out, n, l2b, stream));
 }
 
 int do_nested(Dtype t, const uint32_t* packed, const float* codebook16, const uint8_t* code,
@@ -102,6 +105,7 @@ int device_cu_count() {
 }  // namespace kbit
 
 using kbit::Dtype;
+using kbit::ScaleFmt;
 
 extern "C" {
 
@@ -117,24 +121,44 @@ const char* kbit_strerror(int status) {
     }
 }
 
-int kbit_abi_version(void) { return 1; }
+int kbit_abi_version(void) { return 2; }
 
 #define KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, K)                                                   \
     int quantize_kbit_##TNAME##_k##K(const float* codebook, const CTYPE* A, float* absmax,          \
                                      uint32_t* packed, int64_t n, int32_t blocksize, void* stream) { \
-        return kbit::do_quantize(DT, K, codebook, A, absmax, packed, n, blocksize, stream);         \
+        return kbit::do_quantize(DT, ScaleFmt::f32, K, codebook, A, absmax, packed, n, blocksize,   \
+                                 stream);                                                           \
     }
 #define KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, K)                                                 \
     int dequantize_kbit_##TNAME##_k##K(const uint32_t* packed, const float* codebook,               \
                                        const float* absmax, CTYPE* out, int64_t n,                  \
                                        int32_t blocksize, void* stream) {                           \
-        return kbit::do_dequantize(DT, K, packed, codebook, absmax, out, n, blocksize, stream);     \
+        return kbit::do_dequantize(DT, ScaleFmt::f32, K, packed, codebook, absmax, out, n,          \
+                                   blocksize, stream);                                              \
+    }
+#define KBIT_DEFINE_QUANTIZE_E4M4(TNAME, CTYPE, DT, K)                                              \
+    int quantize_kbit_e4m4_##TNAME##_k##K(const float* codebook, const CTYPE* A,                    \
+                                          uint8_t* absmax_e4m4, uint32_t* packed, int64_t n,        \
+                                          int32_t blocksize, void* stream) {                        \
+        return kbit::do_quantize(DT, ScaleFmt::e4m4, K, codebook, A, absmax_e4m4, packed, n,        \
+                                 blocksize, stream);                                                \
+    }
+#define KBIT_DEFINE_DEQUANTIZE_E4M4(TNAME, CTYPE, DT, K)                                            \
+    int dequantize_kbit_e4m4_##TNAME##_k##K(const uint32_t* packed, const float* codebook,          \
+                                            const uint8_t* absmax_e4m4, CTYPE* out, int64_t n,      \
+                                            int32_t blocksize, void* stream) {                      \
+        return kbit::do_dequantize(DT, ScaleFmt::e4m4, K, packed, codebook, absmax_e4m4, out, n,    \
+                                   blocksize, stream);                                              \
     }
 #define KBIT_DEFINE_ALL_K(TNAME, CTYPE, DT)                                                         \
     KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 2) KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 3)             \
     KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 4) KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, 5)             \
     KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 2) KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 3)         \
-    KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 4) KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 5)
+    KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 4) KBIT_DEFINE_DEQUANTIZE(TNAME, CTYPE, DT, 5)         \
+    KBIT_DEFINE_QUANTIZE_E4M4(TNAME, CTYPE, DT, 2) KBIT_DEFINE_QUANTIZE_E4M4(TNAME, CTYPE, DT, 3)   \
+    KBIT_DEFINE_QUANTIZE_E4M4(TNAME, CTYPE, DT, 4) KBIT_DEFINE_QUANTIZE_E4M4(TNAME, CTYPE, DT, 5)   \
+    KBIT_DEFINE_DEQUANTIZE_E4M4(TNAME, CTYPE, DT, 2) KBIT_DEFINE_DEQUANTIZE_E4M4(TNAME, CTYPE, DT, 3) \
+    KBIT_DEFINE_DEQUANTIZE_E4M4(TNAME, CTYPE, DT, 4) KBIT_DEFINE_DEQUANTIZE_E4M4(TNAME, CTYPE, DT, 5)
 
 KBIT_DEFINE_ALL_K(fp32, float, Dtype::fp32)
 KBIT_DEFINE_ALL_K(fp16, uint16_t, Dtype::fp16)

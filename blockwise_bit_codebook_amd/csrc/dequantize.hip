@@ -11,6 +11,8 @@
 //          The scale rebuild is a separately rounded multiply then add
 //          (this file is compiled with -ffp-contract=off and the two
 //          operations are kept apart explicitly).
+//   E4M4   ([QLORA-2] PATCH 005): the plain formula with absmax[b] decoded
+//          from one E4M4 byte per block (exact).
 //
 // How: a lane owns 8 consecutive elements of one 32-element group.  Lane l
 // of each quad loads plane word l of its group (K = 4: one coalesced dword
@@ -22,6 +24,7 @@
 // (bf16/fp16) or 32 bytes (fp32).  K = 5 adds a fifth plane byte and looks
 // codes up one by one.
 #include "device.h"
+#include "e4m4.h"
 #include "kbit_internal.h"
 #include "launch.h"
 
@@ -38,6 +41,16 @@ struct PlainScale {
     };
     __device__ Raw load(int64_t b) const { return Raw{absmax[b]}; }
     __device__ float finish(const Raw& r) const { return r.a; }
+};
+
+// One E4M4 byte per block.
+struct E4m4Scale {
+    const uint8_t* code;
+    struct Raw {
+        uint32_t c;
+    };
+    __device__ Raw load(int64_t b) const { return Raw{code[b]}; }
+    __device__ float finish(const Raw& r) const { return e4m4_decode(r.c); }
 };
 
 // Nested scale rebuild.  qmap2 is staged in LDS by the kernel prologue.
@@ -171,16 +184,16 @@ __device__ __forceinline__ void stage_codebook(const float* __restrict__ cb, flo
 constexpr int kSteps = 4;      // wave tiles per step
 constexpr bool kNtStore = true;
 
-template <class E, int K>
-__global__ __launch_bounds__(kThreads) void dequantize_kernel(
-    const uint32_t* __restrict__ packed, const float* __restrict__ cb, const float* __restrict__ absmax,
-    typename E::storage* __restrict__ out, int64_t n, int log2B) {
+template <class E, int K, class Scale>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint32_t* __restrict__ packed,
+                                                              const float* __restrict__ cb, Scale scale,
+                                                              typename E::storage* __restrict__ out, int64_t n,
+                                                              int log2B) {
     __shared__ float cb_lds[32];
     __shared__ float2 pair_lds[256];
     stage_codebook<K>(cb, cb_lds, pair_lds);
     __syncthreads();
-    dequant_tiles<E, K, PlainScale, kSteps, kNtStore>(packed, cb_lds, pair_lds, PlainScale{absmax}, out, n,
-                                                       log2B);
+    dequant_tiles<E, K, Scale, kSteps, kNtStore>(packed, cb_lds, pair_lds, scale, out, n, log2B);
 }
 
 template <class E, int U = kSteps, bool NTS = kNtStore>
@@ -199,14 +212,14 @@ __global__ __launch_bounds__(kThreads) void dequantize_nested_kernel(
                                                         log2B);
 }
 
-template <class E, int K>
-int launch_plain(const uint32_t* packed, const float* cb, const float* absmax, void* out, int64_t n,
-                 int log2B, void* stream) {
-    auto kern = dequantize_kernel<E, K>;
+template <class E, int K, class Scale>
+int launch_plain(const uint32_t* packed, const float* cb, Scale scale, void* out, int64_t n, int log2B,
+                 void* stream) {
+    auto kern = dequantize_kernel<E, K, Scale>;
     static int blocks_per_cu = 0;
     const int64_t grid = persistent_grid(kern, blocks_per_cu, (n + kWaveTile * kSteps - 1) / (kWaveTile * kSteps));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), packed, cb, absmax,
+                       static_cast<hipStream_t>(stream), packed, cb, scale,
                        static_cast<typename E::storage*>(out), n, log2B);
     return static_cast<int>(hipGetLastError());
 }
@@ -223,26 +236,36 @@ int launch_nested(const uint32_t* packed, const float* cb, const uint8_t* code, 
     return static_cast<int>(hipGetLastError());
 }
 
-template <class E>
-int launch_plain_k(int K, const uint32_t* packed, const float* cb, const float* absmax, void* out,
-                   int64_t n, int log2B, void* stream) {
+template <class E, class Scale>
+int launch_plain_k(int K, const uint32_t* packed, const float* cb, Scale scale, void* out, int64_t n,
+                   int log2B, void* stream) {
     switch (K) {
-        case 2: return launch_plain<E, 2>(packed, cb, absmax, out, n, log2B, stream);
-        case 3: return launch_plain<E, 3>(packed, cb, absmax, out, n, log2B, stream);
-        case 4: return launch_plain<E, 4>(packed, cb, absmax, out, n, log2B, stream);
-        default: return launch_plain<E, 5>(packed, cb, absmax, out, n, log2B, stream);
+        case 2: return launch_plain<E, 2>(packed, cb, scale, out, n, log2B, stream);
+        case 3: return launch_plain<E, 3>(packed, cb, scale, out, n, log2B, stream);
+        case 4: return launch_plain<E, 4>(packed, cb, scale, out, n, log2B, stream);
+        default: return launch_plain<E, 5>(packed, cb, scale, out, n, log2B, stream);
+    }
+}
+
+template <class Scale>
+int launch_plain_t(Dtype t, int K, const uint32_t* packed, const float* cb, Scale scale, void* out,
+                   int64_t n, int log2B, void* stream) {
+    switch (t) {
+        case Dtype::fp32: return launch_plain_k<Fp32>(K, packed, cb, scale, out, n, log2B, stream);
+        case Dtype::fp16: return launch_plain_k<Fp16>(K, packed, cb, scale, out, n, log2B, stream);
+        default: return launch_plain_k<Bf16>(K, packed, cb, scale, out, n, log2B, stream);
     }
 }
 
 }  // namespace
 
-int launch_dequantize(Dtype t, int K, const uint32_t* packed, const float* codebook,
-                      const float* absmax, void* out, int64_t n, int log2B, void* stream) {
-    switch (t) {
-        case Dtype::fp32: return launch_plain_k<Fp32>(K, packed, codebook, absmax, out, n, log2B, stream);
-        case Dtype::fp16: return launch_plain_k<Fp16>(K, packed, codebook, absmax, out, n, log2B, stream);
-        default: return launch_plain_k<Bf16>(K, packed, codebook, absmax, out, n, log2B, stream);
-    }
+int launch_dequantize(Dtype t, ScaleFmt f, int K, const uint32_t* packed, const float* codebook,
+                      const void* absmax, void* out, int64_t n, int log2B, void* stream) {
+    if (f == ScaleFmt::e4m4)
+        return launch_plain_t(t, K, packed, codebook, E4m4Scale{static_cast<const uint8_t*>(absmax)}, out, n,
+                              log2B, stream);
+    return launch_plain_t(t, K, packed, codebook, PlainScale{static_cast<const float*>(absmax)}, out, n, log2B,
+                          stream);
 }
 
 int launch_dequantize_nested(Dtype t, const uint32_t* packed, const float* codebook16,

@@ -8,13 +8,16 @@ namespace kbit {
 
 enum class Dtype : int { fp32 = 0, fp16 = 1, bf16 = 2 };
 
+// Storage of the per-block scales: fp32 absmax, or one E4M4 byte per block.
+enum class ScaleFmt : int { f32 = 0, e4m4 = 1 };
+
 // Each launcher enqueues its kernel on `stream` and returns 0, or the HIP
 // error code of a failed launch.  Arguments are already validated.
-int launch_quantize(Dtype t, int K, const float* codebook, const void* A, float* absmax,
+int launch_quantize(Dtype t, ScaleFmt f, int K, const float* codebook, const void* A, void* absmax,
                     uint32_t* packed, int64_t n, int log2B, void* stream);
 
-int launch_dequantize(Dtype t, int K, const uint32_t* packed, const float* codebook,
-                      const float* absmax, void* out, int64_t n, int log2B, void* stream);
+int launch_dequantize(Dtype t, ScaleFmt f, int K, const uint32_t* packed, const float* codebook,
+                      const void* absmax, void* out, int64_t n, int log2B, void* stream);
 
 int launch_dequantize_nested(Dtype t, const uint32_t* packed, const float* codebook16,
                              const uint8_t* code, const float* qmap2, const float* absmax2,

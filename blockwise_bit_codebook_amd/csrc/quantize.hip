@@ -45,10 +45,14 @@
 //     in one LDS cycle hit 16 different 16-byte bank groups whatever their
 //     buckets, so a ds_read_b128 per element runs without bank conflicts.
 //     One v_perm_b32 forms the address (bucket byte of q, lane byte).
+//   * The block scale is stored as the fp32 absmax or, for the E4M4
+//     entry points ([QLORA-2] PATCH 005), as its one-byte E4M4 code; the
+//     indices come from the fp32 absmax either way.
 //   * Persistent grid of 1024-thread workgroups (16 waves, at most 64 VGPRs
 //     so two groups share a CU); each wave walks its tiles with the next
 //     tile's load in flight while the current one is classified.
 #include "device.h"
+#include "e4m4.h"
 #include "kbit_internal.h"
 #include "threshold.h"
 
@@ -226,12 +230,22 @@ __device__ __forceinline__ float block_max_abs(const float (&x)[8]) {
     return __uint_as_float(run_max_u32<LANES>(__float_as_uint(lane_max_abs(x))));
 }
 
+// Block scale output: the fp32 absmax itself, or its E4M4 byte.
+struct F32Scale {
+    using type = float;
+    __device__ static float encode(float m) { return m; }
+};
+struct E4m4Scale {
+    using type = uint8_t;
+    __device__ static uint8_t encode(float m) { return static_cast<uint8_t>(e4m4_encode(m)); }
+};
+
 // LOG2B = log2(B) for B <= 512 (blocks inside a wave row); LOG2B = 0 for
 // B = 1024..4096 (blocks spanning rows; log2B from the argument).
-template <class E, int K, int LOG2B, int ROWS, bool NT, int THREADS, int PFD>
+template <class E, class S, int K, int LOG2B, int ROWS, bool NT, int THREADS, int PFD>
 __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restrict__ cb,
                                                              const typename E::storage* __restrict__ A,
-                                                             float* __restrict__ absmax,
+                                                             typename S::type* __restrict__ absmax,
                                                              uint32_t* __restrict__ packed, int64_t n, int log2B) {
     constexpr int C = 1 << K;
     constexpr int kV = E::kVec;
@@ -302,8 +316,8 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
                 float x[8];
                 E::unpack(r[u], x);
                 const float m = block_max_abs<kLpb>(x);
-                float* am = absmax + (base >> LOG2B);  // wave-uniform
-                if (kFull || ((lane & (kLpb - 1)) == 0 && base + lane_e < n)) am[lane_e >> LOG2B] = m;
+                typename S::type* am = absmax + (base >> LOG2B);  // wave-uniform
+                if (kFull || ((lane & (kLpb - 1)) == 0 && base + lane_e < n)) am[lane_e >> LOG2B] = S::encode(m);
                 encode_row<E, K, kFull>(fast, T, tab, lane_off, lane, x, m, base, n, packed);
             }
         };
@@ -362,7 +376,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
                 ml = __builtin_elementwise_maximum(ml, lane_max_abs(x));
             }
             const float m = __uint_as_float(run_max_u32<kWave>(__float_as_uint(ml)));
-            if (lane == 0) absmax[b] = m;
+            if (lane == 0) absmax[b] = S::encode(m);
             for (int u = 0; u < rows; ++u) {
                 const int64_t rb = base + u * kWaveTile;
                 if (rb >= n) break;
@@ -378,10 +392,11 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
 
 // grid_mult > 1 launches that many times the resident number of
 // workgroups (each then walks fewer steps).
-template <class E, int K, int LOG2B, int ROWS = 1, bool NT = true, int THREADS = kQThreads, int PFD = 1>
-int launch_cfg(const float* cb, const void* A, float* absmax, uint32_t* packed, int64_t n, int log2B,
+template <class E, class S, int K, int LOG2B, int ROWS = 1, bool NT = true, int THREADS = kQThreads,
+          int PFD = 1>
+int launch_cfg(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
                void* stream, int grid_mult = 1) {
-    auto kern = quantize_kernel<E, K, LOG2B, ROWS, NT, THREADS, PFD>;
+    auto kern = quantize_kernel<E, S, K, LOG2B, ROWS, NT, THREADS, PFD>;
     static int blocks_per_cu = 0;
     if (blocks_per_cu == 0) {
         int b = 0;
@@ -397,12 +412,13 @@ int launch_cfg(const float* cb, const void* A, float* absmax, uint32_t* packed, 
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(THREADS), 0,
                        static_cast<hipStream_t>(stream), cb,
-                       static_cast<const typename E::storage*>(A), absmax, packed, n, log2B);
+                       static_cast<const typename E::storage*>(A), static_cast<typename S::type*>(absmax),
+                       packed, n, log2B);
     return static_cast<int>(hipGetLastError());
 }
 
-template <class E, int K>
-int launch_k(const float* cb, const void* A, float* absmax, uint32_t* packed, int64_t n, int log2B,
+template <class E, class S, int K>
+int launch_k(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
              void* stream) {
     // Two wave rows per step for bf16 (32 bytes per lane in flight plus the
     // prefetched step) where that still fits 64 VGPRs; one row otherwise.
@@ -410,35 +426,42 @@ int launch_k(const float* cb, const void* A, float* absmax, uint32_t* packed, in
     constexpr int R = (std::is_same<E, Bf16>::value && K <= 4) ? 2 : 1;
     constexpr int TH = K == 5 ? 512 : kQThreads;
     switch (log2B) {
-        case 5: return launch_cfg<E, K, 5, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 6: return launch_cfg<E, K, 6, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 7: return launch_cfg<E, K, 7, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 8: return launch_cfg<E, K, 8, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 9: return launch_cfg<E, K, 9, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        default: return launch_cfg<E, K, 0, 1, false, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 5: return launch_cfg<E, S, K, 5, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 6: return launch_cfg<E, S, K, 6, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 7: return launch_cfg<E, S, K, 7, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 8: return launch_cfg<E, S, K, 8, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 9: return launch_cfg<E, S, K, 9, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
+        default: return launch_cfg<E, S, K, 0, 1, false, TH>(cb, A, absmax, packed, n, log2B, stream);
     }
 }
 
-template <class E>
-int launch_t(int K, const float* cb, const void* A, float* absmax, uint32_t* packed, int64_t n,
+template <class E, class S>
+int launch_t(int K, const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n,
              int log2B, void* stream) {
     switch (K) {
-        case 2: return launch_k<E, 2>(cb, A, absmax, packed, n, log2B, stream);
-        case 3: return launch_k<E, 3>(cb, A, absmax, packed, n, log2B, stream);
-        case 4: return launch_k<E, 4>(cb, A, absmax, packed, n, log2B, stream);
-        default: return launch_k<E, 5>(cb, A, absmax, packed, n, log2B, stream);
+        case 2: return launch_k<E, S, 2>(cb, A, absmax, packed, n, log2B, stream);
+        case 3: return launch_k<E, S, 3>(cb, A, absmax, packed, n, log2B, stream);
+        case 4: return launch_k<E, S, 4>(cb, A, absmax, packed, n, log2B, stream);
+        default: return launch_k<E, S, 5>(cb, A, absmax, packed, n, log2B, stream);
+    }
+}
+
+template <class S>
+int launch_s(Dtype t, int K, const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n,
+             int log2B, void* stream) {
+    switch (t) {
+        case Dtype::fp32: return launch_t<Fp32, S>(K, cb, A, absmax, packed, n, log2B, stream);
+        case Dtype::fp16: return launch_t<Fp16, S>(K, cb, A, absmax, packed, n, log2B, stream);
+        default: return launch_t<Bf16, S>(K, cb, A, absmax, packed, n, log2B, stream);
     }
 }
 
 }  // namespace
 
-int launch_quantize(Dtype t, int K, const float* codebook, const void* A, float* absmax,
+int launch_quantize(Dtype t, ScaleFmt f, int K, const float* codebook, const void* A, void* absmax,
                     uint32_t* packed, int64_t n, int log2B, void* stream) {
-    switch (t) {
-        case Dtype::fp32: return launch_t<Fp32>(K, codebook, A, absmax, packed, n, log2B, stream);
-        case Dtype::fp16: return launch_t<Fp16>(K, codebook, A, absmax, packed, n, log2B, stream);
-        default: return launch_t<Bf16>(K, codebook, A, absmax, packed, n, log2B, stream);
-    }
+    if (f == ScaleFmt::e4m4) return launch_s<E4m4Scale>(t, K, codebook, A, absmax, packed, n, log2B, stream);
+    return launch_s<F32Scale>(t, K, codebook, A, absmax, packed, n, log2B, stream);
 }
 
 }  // namespace kbit

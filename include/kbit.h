@@ -37,8 +37,9 @@
  *     bit t of word g*K + j is bit j of the K-bit index of element 32*g + t.
  *     Bits of positions past n are 0.  packed holds ceil(n/32)*K words.
  *   - Alignment: element arrays (A, out, X) must be 16-byte aligned;
- *     packed, sign_bits and the float arrays 4-byte aligned; absmax_code
- *     (bytes) has no requirement.  Otherwise KBIT_EALIGN.
+ *     packed, sign_bits and the float arrays 4-byte aligned; the byte
+ *     arrays (absmax_code, absmax_e4m4) have no requirement.  Otherwise
+ *     KBIT_EALIGN.
  *   - Floating point: IEEE binary32 with round to nearest even, no fused
  *     multiply-add, subnormals kept; narrowing to fp16/bf16 rounds to
  *     nearest even.  Every result is the one the definitions above fix,
@@ -110,9 +111,11 @@ int kbit_dynamic_map8(float* out_host);
  *   x_n        = RN(A_e / max(absmax[b], 1e-8f))        (IEEE division)
  *   index      = smallest i minimising |RN(x_n - codebook[i])|
  *   packed     = bit planes of the indices (layout above)
- * codebook : device, 2^K float32.  Any finite values are accepted; sorted
+ * codebook : device, 2^K float32.  Any finite values are accepted.  Sorted
  *            codebooks in [-1, 1] whose distinct neighbours differ by at least
- *            1/64 take the fast classification path, others an exact scan.
+ *            2^-16 are classified against precomputed exact thresholds;
+ *            others (and blocks whose scale is not finite or exceeds 2^125)
+ *            by the full first-index scan.  Results are the same either way.
  * A        : device, n elements of the named type.
  * absmax   : device, ceil(n/B) float32 (output).
  * packed   : device, ceil(n/32)*K uint32 (output).
@@ -145,6 +148,40 @@ int kbit_dynamic_map8(float* out_host);
 KBIT_DECLARE_ALL_K(fp32, float)
 KBIT_DECLARE_ALL_K(fp16, uint16_t)
 KBIT_DECLARE_ALL_K(bf16, uint16_t)
+
+/* ------------------------------------------------------------------------
+ * One-byte E4M4 block scales: [QLORA-2] PATCH 005 "Add vectorized dequant
+ * kernel and E4M4 uint8 absmax" (functional.py encode_absmax_e4m4 /
+ * decode_absmax_e4m4, quantize_kbit(absmax_format="e4m4")).
+ *   code = e << 4 | m, bias 11:  e > 0 -> 2^(e-11) * (1 + m/16),
+ *                                e = 0 -> m * 2^-14  (0x00 = 0).
+ *   encode(a): a <= 0 or NaN -> 0; +inf -> 0xF0; a < 2^-10 ->
+ *     m = RNE(a * 2^14) clamped to 15; otherwise e = min(E + 11, 15) with E
+ *     the binary exponent of a, m = the fraction of a rounded to 4 bits
+ *     (half to even) and clamped to 15 (never carried into e).  Scales of
+ *     2^5 and above are outside the format: e stays 15 and m is taken from
+ *     a's own exponent, as the page's encoder does.
+ * quantize_kbit_e4m4_*: indices exactly as quantize_kbit_* (from the fp32
+ *   absmax); absmax_e4m4[b] = encode(absmax[b]).  absmax_e4m4: device,
+ *   ceil(n/B) uint8 (output).  Other arguments as quantize_kbit_*.
+ * dequantize_kbit_e4m4_*: out_e = RN_T( RN(codebook[index_e] *
+ *   decode(absmax_e4m4[e / B])) ).  absmax_e4m4: device, ceil(n/B) uint8.
+ *   Other arguments as dequantize_kbit_*.
+ * --------------------------------------------------------------------- */
+#define KBIT_DECLARE_E4M4(TNAME, CTYPE, K)                                                   \
+    int quantize_kbit_e4m4_##TNAME##_k##K(const float* codebook, const CTYPE* A,             \
+                                          uint8_t* absmax_e4m4, uint32_t* packed, int64_t n, \
+                                          int32_t blocksize, void* stream);                  \
+    int dequantize_kbit_e4m4_##TNAME##_k##K(const uint32_t* packed, const float* codebook,   \
+                                            const uint8_t* absmax_e4m4, CTYPE* out,          \
+                                            int64_t n, int32_t blocksize, void* stream);
+#define KBIT_DECLARE_E4M4_ALL_K(TNAME, CTYPE)                                   \
+    KBIT_DECLARE_E4M4(TNAME, CTYPE, 2) KBIT_DECLARE_E4M4(TNAME, CTYPE, 3)       \
+    KBIT_DECLARE_E4M4(TNAME, CTYPE, 4) KBIT_DECLARE_E4M4(TNAME, CTYPE, 5)
+
+KBIT_DECLARE_E4M4_ALL_K(fp32, float)
+KBIT_DECLARE_E4M4_ALL_K(fp16, uint16_t)
+KBIT_DECLARE_E4M4_ALL_K(bf16, uint16_t)
 
 /* ------------------------------------------------------------------------
  * Nested (double-quantized) 4-bit dequantize, scale rebuild fused into the

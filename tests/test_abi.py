@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 3 + 1, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 1, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -75,7 +75,7 @@ def test_generator_argument_errors():
     assert lib.kbit_codebook_lloyd_max_normal(3, p) == -1
     assert lib.kbit_codebook_fp4(None) == -1
     assert lib.kbit_strerror(-2).decode().startswith("blocksize")
-    assert lib.kbit_abi_version() == 1
+    assert lib.kbit_abi_version() == 2
 
 
 # fake, never dereferenced device addresses
@@ -101,6 +101,15 @@ def test_validation_codes_before_any_device_access():
     nd = lib.dequantize_4bit_nested_fp16
     assert nd(_A16, _A16, None, _A16, _A16, ct.c_float(0.0), _A16, 10, 64, None) == -1
     assert nd(_A16, _A16, _A16, _A16, _A16, ct.c_float(0.0), _A16, 10, 96, None) == -2
+    qe = lib.quantize_kbit_e4m4_fp16_k2
+    _B1 = ct.c_void_p(0x30001)                                     # byte-aligned only
+    assert qe(_A16, _A16, _B1, _A16, 10, 48, None) == -2
+    assert qe(_A16, _A4, _B1, _A16, 10, 32, None) == -3           # A misaligned
+    assert qe(_A16, _A16, None, _A16, 10, 32, None) == -1
+    de = lib.dequantize_kbit_e4m4_bf16_k5
+    assert de(_A16, _A16, _B1, _A4, 10, 64, None) == -3           # out misaligned
+    assert de(_A16, _A16, None, _A16, 10, 64, None) == -1
+    assert de(None, None, None, None, 0, 64, None) == 0
     act = lib.quantize_act_fwht_k4_bf16
     assert act(_A16, 4, 2048, _A16, _A16, _A16, _A16, None) == -1  # d must be 4096
     assert act(_A16, 0, 4096, None, None, None, None, None) == 0

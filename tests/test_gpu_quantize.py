@@ -26,9 +26,13 @@ def _cb(name, K):
         return codebooks.nf_pages_rule(K)
     if name == "linspace":
         return np.linspace(-1, 1, 1 << K).astype(np.float32)
-    if name == "dense":      # distinct neighbours closer than 1/64: exact path everywhere
+    if name == "dense":      # close distinct neighbours (1e-3), still on the threshold path
         c = codebooks.nf(K).copy()
         c[1] = c[0] + np.float32(1e-3)
+        return c
+    if name == "denser":     # neighbours 2^-20 apart (below the threshold path's 2^-16): full scan
+        c = codebooks.nf(K).copy()
+        c[1] = c[0] + np.float32(2.0 ** -20)
         return c
     if name == "unsorted":
         c = codebooks.nf(K).copy()[::-1].copy()
@@ -74,7 +78,8 @@ def test_block_sizes(dtype, B):
 
 
 @pytest.mark.parametrize("cbname,K", [("fp4", 4), ("pages", 4), ("pages", 2), ("linspace", 3), ("linspace", 5),
-                                      ("nf", 5), ("dense", 4), ("unsorted", 3), ("wide", 4)])
+                                      ("nf", 5), ("dense", 4), ("denser", 4), ("unsorted", 3),
+                                      ("wide", 4)])
 def test_codebooks(cbname, K):
     x = synth.normal(50000, seed=7, dtype="bf16")
     check_quantize(x, "bf16", _cb(cbname, K), K, 64, cbname)
