@@ -12,10 +12,11 @@ it (steps must be a multiple of the number of sets).
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (read +
 written by both kernels) divided by the wall time per step, in GB/s.
 Per-kernel launch times (the ``roofline`` object) come from HIP events
-around eager bursts of one kernel over all buffer sets, on the stream the
-kernels run on.  The same line also reports the FP4 codebook, warm-cache
-numbers and the W4A4 activation path (4096 x 4096 bf16) as side
-measurements.  ``cpu_baseline`` times the CPU oracle on a bounded sample of
+around eager launches of one kernel over all buffer sets, the kernels taken
+in round robin, on the stream the kernels run on.  The same line also reports, as side measurements, the
+quantize / dequantize pair with one-byte E4M4 block scales and the plain
+fp32-scale dequantize on the same tensor, the FP4 codebook, warm-cache
+numbers and the W4A4 activation path (4096 x 4096 bf16).  ``cpu_baseline`` times the CPU oracle on a bounded sample of
 the same workload (N = 1 only).
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--sets 4]
@@ -44,12 +45,25 @@ GROUP2 = 256
 
 
 def algorithmic_bytes(n):
-    """Bytes each kernel must move at minimum (read + write)."""
+    """Bytes each kernel of the step must move at minimum (read + write)."""
+    b = kernel_bytes(n)
+    return b["quantize_kbit_bf16_k4"], b["dequantize_4bit_nested_bf16"]
+
+
+def kernel_bytes(n):
+    """Minimum bytes read + written per launch, by kernel: bf16 elements,
+    K bit planes per 32 elements, per-block scales (4 bytes fp32, 1 byte
+    E4M4 or nested code), group absmax, tables."""
     nb = -(-n // BLOCK)
-    ng32 = -(-n // 32)
-    quant = 2 * n + 4 * ng32 * K + 4 * nb
-    nested = 4 * ng32 * K + nb + 4 * (-(-nb // GROUP2)) + 2 * n + 4 * 256 + 4 * 16
-    return quant, nested
+    planes = 4 * (-(-n // 32)) * K
+    tables = 4 * (1 << K)
+    return {
+        "quantize_kbit_bf16_k4": 2 * n + planes + 4 * nb + tables,
+        "dequantize_4bit_nested_bf16": planes + nb + 4 * (-(-nb // GROUP2)) + 2 * n + 4 * 256 + tables,
+        "quantize_kbit_e4m4_bf16_k4": 2 * n + planes + nb + tables,
+        "dequantize_kbit_e4m4_bf16_k4": planes + nb + 2 * n + tables,
+        "dequantize_kbit_bf16_k4": planes + 4 * nb + 2 * n + tables,
+    }
 
 
 def parse(argv=None):
@@ -58,6 +72,8 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
+    ap.add_argument("--rr-reps", type=int, default=0,
+                    help="rounds of the per-kernel timing (default: steps / sets, at least 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-act", action="store_true", help="skip the activation-path timing")
     ap.add_argument("--headline-only", action="store_true",
@@ -78,19 +94,27 @@ def parse(argv=None):
 # --------------------------------------------------------------------------
 CAL_BYTES = 192 << 20
 CAL_COPIES = 3
+_Q_SRC = ["blockwise_bit_codebook_amd/csrc/quantize.hip", "blockwise_bit_codebook_amd/csrc/device.h",
+          "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/e4m4.h"]
+_D_SRC = ["blockwise_bit_codebook_amd/csrc/dequantize.hip", "blockwise_bit_codebook_amd/csrc/device.h",
+          "blockwise_bit_codebook_amd/csrc/e4m4.h"]
 KERNELS = {
-    # name used in the JSON line: (substring of the HIP kernel name, sources that define it)
-    "quantize_kbit_bf16_k4": ("quantize_kernel<kbit::Bf16, 4",
-                              ["blockwise_bit_codebook_amd/csrc/quantize.hip",
-                               "blockwise_bit_codebook_amd/csrc/device.h"]),
-    "dequantize_4bit_nested_bf16": ("dequantize_nested_kernel<kbit::Bf16",
-                                    ["blockwise_bit_codebook_amd/csrc/dequantize.hip",
-                                     "blockwise_bit_codebook_amd/csrc/device.h"]),
+    # name used in the JSON line: (substrings that all appear in the HIP kernel's demangled name,
+    # sources that define it)
+    "quantize_kbit_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "F32Scale, 4,"), _Q_SRC),
+    "dequantize_4bit_nested_bf16": (("::dequantize_nested_kernel<kbit::Bf16",), _D_SRC),
+    "quantize_kbit_e4m4_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "E4m4Scale, 4,"), _Q_SRC),
+    "dequantize_kbit_e4m4_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "E4m4Scale>"), _D_SRC),
+    "dequantize_kbit_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "PlainScale>"), _D_SRC),
 }
+
+
+def _matches(pat, name):
+    return all(p in name for p in pat)
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o trace -- "
-    "python3 $R/bench.py --steps 20 --warmup 5 --no-cpu-baseline --headline-only --copy-calibration",
+    "python3 $R/bench.py --steps 200 --warmup 10 --rr-reps 5 --no-cpu-baseline --headline-only --copy-calibration",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o fetch -- "
     "python3 $R/bench.py --steps 8 --warmup 4 --no-cpu-baseline --headline-only --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o write -- "
@@ -134,16 +158,16 @@ def summarize(trace_dir, fetch_dir, write_dir):
         kib = sum(float(r["Counter_Value"]) for r in cal) / len(cal)
         scale[cname] = (CAL_BYTES / 1024.0) / kib
         for name, (pat, _) in KERNELS.items():
-            vals = [float(r["Counter_Value"]) for r in rows if pat in r["Kernel_Name"]]
+            vals = [float(r["Counter_Value"]) for r in rows if _matches(pat, r["Kernel_Name"])]
             per_kernel.setdefault(name, {})[cname] = sum(vals) / len(vals) if vals else None
-    n = ROWS * COLS
-    qb, nb = algorithmic_bytes(n)
-    alg = {"quantize_kbit_bf16_k4": qb, "dequantize_4bit_nested_bf16": nb}
+    alg = kernel_bytes(ROWS * COLS)
     out = {"calibration": {"copy_bytes": CAL_BYTES, "copies": CAL_COPIES,
                            "fetch_scale": round(scale["FETCH_SIZE"], 4),
                            "write_scale": round(scale["WRITE_SIZE"], 4)},
            "kernels": {}}
-    lines = ["# rocprofv3 summary: quantize + nested dequantize, 8192x8192 bf16, NF4, blocksize 64", "",
+    lines = ["# rocprofv3 summary: k-bit quantize / dequantize kernels, 8192x8192 bf16, NF4, blocksize 64", "",
+             "The bench step is quantize_kbit_bf16_k4 + dequantize_4bit_nested_bf16; the E4M4-scale pair and "
+             "the plain fp32-scale dequantize run on the same tensor as side measurements.", "",
              "Commands (R = repository root; the counter runs are separate passes):", "", "```"]
     lines += PROFILE_COMMANDS + ["```", "",
                                  f"Calibration: the last {CAL_COPIES} device copies of {CAL_BYTES >> 20} MiB each; "
@@ -153,8 +177,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
                                  "| algorithmic MB | traffic / algorithmic | GB/s (algorithmic) |",
                                  "|---|---|---|---|---|---|---|---|---|---|"]
     for name, (pat, srcs) in KERNELS.items():
-        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace if pat in r["Kernel_Name"]]
-        if not durs:
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+                if _matches(pat, r["Kernel_Name"])]
+        if not durs or per_kernel[name]["FETCH_SIZE"] is None or per_kernel[name]["WRITE_SIZE"] is None:
             continue
         avg = sum(durs) / len(durs) / 1e3
         f_kib = per_kernel[name]["FETCH_SIZE"]
@@ -172,7 +197,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    md = os.path.join(ROOT, "profiles", "quantize_nested_dequant_8192sq_bf16_b64.md")
+    md = os.path.join(ROOT, "profiles", "kbit_kernels_8192sq_bf16_nf4_b64.md")
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -302,6 +327,7 @@ def main(argv=None):
             "code": torch.from_numpy(code_np).to(dev),
             "absmax2": torch.from_numpy(a2_np).to(dev),
             "out": torch.empty(n, dtype=torch.bfloat16, device=dev),
+            "code8": torch.empty(nb, dtype=torch.uint8, device=dev),
         })
     torch.cuda.synchronize()
 
@@ -316,6 +342,15 @@ def main(argv=None):
     def nested_only(s):
         kb.dequantize_4bit_nested(s["packed"], cb, s["code"], qmap, s["absmax2"], offset, n,
                                   torch.bfloat16, BLOCK, out=s["out"])
+
+    def quant_e4m4(s):
+        kb.quantize_kbit(s["A"], cb, K, BLOCK, absmax=s["code8"], packed=s["packed"], absmax_format="e4m4")
+
+    def dequant_e4m4(s):
+        kb.dequantize_kbit(s["packed"], cb, s["code8"], K, n, torch.bfloat16, BLOCK, out=s["out"])
+
+    def dequant_plain(s):
+        kb.dequantize_kbit(s["packed"], cb, s["absmax"], K, n, torch.bfloat16, BLOCK, out=s["out"])
 
     for s_ in sets:                              # eager once per set: per-device setup happens here
         step(s_)
@@ -350,26 +385,37 @@ def main(argv=None):
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
 
-    # Per-kernel launch time: eager bursts of one kernel over all buffer
-    # sets, HIP events on the stream the kernels run on (torch's current
-    # stream, which the binding passes to every launch).
-    def burst(fn, reps, warm=3):
+    # Per-kernel launch time, from HIP events on the stream the kernels run
+    # on (torch's current stream, which the binding passes to every launch).
+    # Round robin over the kernels: each round launches every kernel once per
+    # buffer set, with an event before and after each kernel's launches, so
+    # that all of them are timed under the same clock and power state.
+    def round_robin(fns, reps, warm=3, bufs=None):
+        bufs = sets if bufs is None else bufs
         for _ in range(warm):
-            for s_ in sets:
-                fn(s_)
+            for fn in fns.values():
+                for s_ in bufs:
+                    fn(s_)
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        ev[0].record()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps * len(fns))]
         for r in range(reps):
-            for s_ in sets:
-                fn(s_)
-            ev[r + 1].record()
+            for j, fn in enumerate(fns.values()):
+                e = ev[r * len(fns) + j]
+                e[0].record()
+                for s_ in bufs:
+                    fn(s_)
+                e[1].record()
         torch.cuda.synchronize()
-        return [ev[r].elapsed_time(ev[r + 1]) / len(sets) for r in range(reps)]
+        return {name: [ev[r * len(fns) + j][0].elapsed_time(ev[r * len(fns) + j][1]) / len(bufs)
+                       for r in range(reps)] for j, name in enumerate(fns)}
 
-    reps = max(5, args.steps // args.sets)
-    tq = burst(quant_only, reps)
-    tn = burst(nested_only, reps)
+    reps = args.rr_reps or max(5, args.steps // args.sets)
+    # quant_e4m4 before dequant_e4m4 and quant_only before dequant_plain in
+    # every round: each dequantize reads scales written by its own quantize.
+    rr = round_robin({"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only,
+                      "quantize_kbit_e4m4_bf16_k4": quant_e4m4, "dequantize_kbit_e4m4_bf16_k4": dequant_e4m4,
+                      "dequantize_kbit_bf16_k4": dequant_plain}, reps)
+    tq, tn = rr["quantize_kbit_bf16_k4"], rr["dequantize_4bit_nested_bf16"]
     qbytes, nbytes = algorithmic_bytes(n)
     ms_step = wall * 1e3 / args.steps
     value = (qbytes + nbytes) / (ms_step * 1e-3) / 1e9
@@ -385,20 +431,30 @@ def main(argv=None):
 
     kq, kn = kstats(tq, qbytes), kstats(tn, nbytes)
 
+    # One-byte E4M4 scales on the same tensor, and the plain fp32-scale
+    # dequantize (distinct kernels, so they do not mix into the step's
+    # per-kernel profile), from the same round robin.
+    kbytes = kernel_bytes(n)
+    e4 = {k: kstats(rr[k], kbytes[k]) for k in ("quantize_kbit_e4m4_bf16_k4", "dequantize_kbit_e4m4_bf16_k4",
+                                                "dequantize_kbit_bf16_k4")}
+    e4["note"] = ("same 8192x8192 bf16 tensor and NF4 codebook; scales as one E4M4 byte per block "
+                  "(the last entry: fp32 scales, for comparison)")
+
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
     fp4 = warm = act = None
     if not args.headline_only:
+        pair = {"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only}
         cb_nf = cb
         cb = torch.from_numpy(kb.codebook_fp4()).to(dev)
-        fp4 = {"quantize_kbit_bf16_k4": kstats(burst(quant_only, reps), qbytes),
-               "dequantize_4bit_nested_bf16": kstats(burst(nested_only, reps), nbytes)}
+        r4 = round_robin(pair, reps)
+        fp4 = {"quantize_kbit_bf16_k4": kstats(r4["quantize_kbit_bf16_k4"], qbytes),
+               "dequantize_4bit_nested_bf16": kstats(r4["dequantize_4bit_nested_bf16"], nbytes)}
         cb = cb_nf
-        warm_sets, sets = sets, sets[:1]
-        warm = {"quantize_kbit_bf16_k4": kstats(burst(quant_only, reps), qbytes),
-                "dequantize_4bit_nested_bf16": kstats(burst(nested_only, reps), nbytes),
+        rw = round_robin(pair, reps, bufs=sets[:1])
+        warm = {"quantize_kbit_bf16_k4": kstats(rw["quantize_kbit_bf16_k4"], qbytes),
+                "dequantize_4bit_nested_bf16": kstats(rw["dequantize_4bit_nested_bf16"], nbytes),
                 "note": "same buffer set every launch (warm cache); not the headline number"}
-        sets = warm_sets
         if not args.no_act:
             act = bench_act(torch, kb, synth, dev, reps)
 
@@ -447,6 +503,7 @@ def main(argv=None):
                    "buffer_sets": args.sets, "step_bytes": qbytes + nbytes},
         "quantize": kq,
         "nested_dequantize": kn,
+        "e4m4_scales": e4,
         "fp4_codebook": fp4,
         "warm": warm,
         "act_fwht": act,

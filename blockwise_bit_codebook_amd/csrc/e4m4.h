@@ -24,20 +24,20 @@ namespace kbit {
 
 __device__ __forceinline__ uint32_t e4m4_encode(float a) {
     const uint32_t u = __float_as_uint(a);
-    const int ex = static_cast<int>((u >> 23) & 0xFFu);  // biased fp32 exponent
-    // normal E4M4 range: round the fraction to 4 bits, half to even
-    const uint32_t frac = u & 0x7FFFFFu;
-    uint32_t q = frac >> 19;
-    const uint32_t r = frac & 0x7FFFFu;
-    q += (r > 0x40000u || (r == 0x40000u && (q & 1u))) ? 1u : 0u;
-    q = min(q, 15u);
-    const uint32_t eb = static_cast<uint32_t>(min(ex - 127 + 11, 15));
-    const uint32_t normal = (eb << 4) | q;
-    // subnormal E4M4 range (a < 2^-10, including fp32 subnormals)
-    const uint32_t sub = static_cast<uint32_t>(__builtin_rintf(__builtin_amdgcn_fmed3f(a * 0x1p14f, 0.0f, 15.0f)));
-    uint32_t code = ex - 127 + 11 <= 0 ? sub : normal;
-    if (ex == 0xFF) code = 0xF0u;  // +inf (NaN is caught below)
-    return a > 0.0f ? code : 0u;
+    // normal E4M4 range [2^-10, +inf]: fp32 exponent field ex >= 117.  The
+    // 23 fraction bits are rounded to 4, half to even; fractions that would
+    // round up to 16 are first lowered to the largest one that rounds to 15,
+    // which is the clamp.  +inf has fraction 0 and lands on 0xF0.
+    const uint32_t ex = u >> 23;
+    const uint32_t f = min(u & 0x7FFFFFu, 0x7BFFFFu);
+    const uint32_t q = (f + 0x3FFFFu + ((f >> 19) & 1u)) >> 19;
+    const uint32_t normal = ((min(ex, 131u) - 116u) << 4) + q;
+    // subnormal E4M4 range [+0, 2^-10): a * 2^14 is exact and below 16, so
+    // adding 2^23 in one rounding (fma) leaves RNE(a * 2^14) in the low bits
+    const uint32_t sub = min(__float_as_uint(__builtin_fmaf(a, 0x1p14f, 0x1p23f)) & 0x1Fu, 15u);
+    // anything else (negative, NaN) encodes as 0
+    const uint32_t code = u <= 0x7F800000u ? normal : 0u;
+    return u < 0x3A800000u ? sub : code;
 }
 
 __device__ __forceinline__ float e4m4_decode(uint32_t code) {

@@ -233,10 +233,12 @@ __device__ __forceinline__ float block_max_abs(const float (&x)[8]) {
 // Block scale output: the fp32 absmax itself, or its E4M4 byte.
 struct F32Scale {
     using type = float;
+    static constexpr bool kEncoded = false;
     __device__ static float encode(float m) { return m; }
 };
 struct E4m4Scale {
     using type = uint8_t;
+    static constexpr bool kEncoded = true;
     __device__ static uint8_t encode(float m) { return static_cast<uint8_t>(e4m4_encode(m)); }
 };
 
@@ -308,16 +310,31 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
         // partial step, if any, goes last.
         constexpr int kLpb = (1 << LOG2B) / kElemsPerLane;  // lanes per block
         const int64_t nsteps = (n + kStep - 1) / kStep;
+        // Encoded scales of a full two-row step are encoded once for both
+        // rows: even lanes carry row 0's block max, odd lanes row 1's (each
+        // block spans at least 4 lanes), and every lane stores its byte.
+        constexpr bool kPairScales = ROWS == 2 && S::kEncoded;
         auto do_step = [&](int64_t i, const u32x4 (&r)[ROWS][kV], auto full_tag) {
             constexpr bool kFull = decltype(full_tag)::value;
+            float m_prev = 0.0f;
 #pragma unroll
             for (int u = 0; u < ROWS; ++u) {
                 const int64_t base = i * kStep + u * kWaveTile;
                 float x[8];
                 E::unpack(r[u], x);
                 const float m = block_max_abs<kLpb>(x);
-                typename S::type* am = absmax + (base >> LOG2B);  // wave-uniform
-                if (kFull || ((lane & (kLpb - 1)) == 0 && base + lane_e < n)) am[lane_e >> LOG2B] = S::encode(m);
+                if constexpr (kFull && kPairScales) {
+                    if (u == 0) {
+                        m_prev = m;
+                    } else {
+                        const int odd = lane & 1;
+                        typename S::type* am = absmax + ((i * kStep) >> LOG2B);  // wave-uniform
+                        am[odd * (kWaveTile >> LOG2B) + (lane_e >> LOG2B)] = S::encode(odd ? m : m_prev);
+                    }
+                } else {
+                    typename S::type* am = absmax + (base >> LOG2B);  // wave-uniform
+                    if (kFull || ((lane & (kLpb - 1)) == 0 && base + lane_e < n)) am[lane_e >> LOG2B] = S::encode(m);
+                }
                 encode_row<E, K, kFull>(fast, T, tab, lane_off, lane, x, m, base, n, packed);
             }
         };

@@ -106,6 +106,9 @@ def test_quantize_special_blocks():
     x[3, 5] = np.inf
     x[4, 7] = -np.inf
     x[6, 0] = np.nan
+    xb = x.view(np.uint32)
+    xb[7, 3] = 0x7F800001          # NaN payloads: signalling, and with the sign bit set
+    xb[5, 9] = 0xFFC00123
     check_quantize(x.ravel().copy(), "fp32", codebooks.nf(3), 3, B, "special blocks")
 
 

@@ -136,3 +136,20 @@ def test_kbit_e4m4_paths(K):
     idx = kbit.unpack(words, K, n)
     scale = e4m4.decode(code)[np.arange(n) // B].astype(np.float64)
     assert np.array_equal(out.astype(np.float64), (np.float32(cb)[idx] * scale).astype(np.float32))
+
+
+@pytest.mark.parametrize("K", [2, 3, 4, 5])
+def test_sqnr_loss_below_page_bound(K):
+    # the page reports under 0.4 dB SQNR loss from E4M4 scales at every K
+    # (blocksize 32, normal data)
+    n, B = 1 << 18, 32
+    x = synth.normal(n, seed=77, dtype="fp32")
+    cb = codebooks.nf(K)
+    idx, a = kbit.quantize(x, cb, B)
+    code = e4m4.encode(a)
+    y32 = kbit.dequantize(idx, a, cb, B, "fp32").astype(np.float64)
+    ye = e4m4.dequantize(idx, code, cb, B, "fp32").astype(np.float64)
+    xs = x.astype(np.float64)
+    sqnr = lambda y: 10 * np.log10(np.sum(xs ** 2) / np.sum((xs - y) ** 2))  # noqa: E731
+    loss = sqnr(y32) - sqnr(ye)
+    assert loss < 0.4, loss          # measured: -0.004, 0.02, 0.11, 0.36 dB for K = 2..5
