@@ -113,14 +113,18 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
         fast = fast && (c[i] == c[i - 1] || (m > -0.97f * kZRange && m < 0.97f * kZRange));
     }
     if (threadIdx.x == 0) T.fail = 0;
-    if (threadIdx.x < 16) {
-        const int i = threadIdx.x;
-        T.code[i] = c[i];
+    if (threadIdx.x < 16) T.code[threadIdx.x] = c[threadIdx.x];
+    // One wave per threshold (the search is wave-cooperative); a failed
+    // search leaves the sentinel, which fails the table below.
+    for (int i = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) + 1; i < 16; i += kActThreads / kWave) {
+        const float lo = cb[i - 1], hi = cb[i];  // wave-uniform
         uint64_t m = 0;
-        if (fast && i > 0 && c[i] != c[i - 1] && !threshold_mid(c[i - 1], c[i], m)) T.fail = 1;
-        T.mid[i] = m;
+        if (fast && lo != hi && !threshold_mid_wave(lo, hi, m)) m = kNoMid;
+        if (lane == 0) T.mid[i] = m;
     }
+    if (threadIdx.x == 0) T.mid[0] = 0;
     __syncthreads();
+    if (threadIdx.x < 16 && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
         if (!build_entry<16, false>(c, T.mid, threadIdx.x, kActSlope, kActBase, e)) T.fail = 1;

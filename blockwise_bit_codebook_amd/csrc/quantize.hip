@@ -277,14 +277,18 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     for (int i = 0; i < C; ++i) c[i] = cb[i];
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
-    if (threadIdx.x < C) {
-        T.code[threadIdx.x] = c[threadIdx.x];
-        const int i = threadIdx.x;
+    if (threadIdx.x < C) T.code[threadIdx.x] = c[threadIdx.x];
+    // One wave per threshold (the search is wave-cooperative); a failed
+    // search leaves the sentinel, which fails the table below.
+    for (int i = wave + 1; i < C; i += kWaves_) {
+        const float lo = cb[i - 1], hi = cb[i];  // wave-uniform
         uint64_t m = 0;
-        if (fast && i > 0 && c[i] != c[i - 1] && !threshold_mid(c[i - 1], c[i], m)) T.fail = 1;
-        T.mid[i] = m;
+        if (fast && lo != hi && !threshold_mid_wave(lo, hi, m)) m = kNoMid;
+        if (lane == 0) T.mid[i] = m;
     }
+    if (threadIdx.x == 0) T.mid[0] = 0;
     __syncthreads();
+    if (threadIdx.x < C && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
         if (!build_entry<C, K == 5>(c, T.mid, threadIdx.x, kSlope, kBase, e)) T.fail = 1;

@@ -27,6 +27,7 @@ namespace kbit {
 constexpr int kBuckets = 128;
 constexpr int kCopies = 16;
 constexpr float kDelta = 0x1p-18f;  // bucket window half-width in q
+constexpr uint64_t kNoMid = ~uint64_t(0);  // marks a failed search (never an M: bits 1:0 of M are 0)
 
 // Bucket rows, their master copy, and the per-threshold M (fp64 bits).
 template <int C>
@@ -53,21 +54,11 @@ __device__ __forceinline__ bool upper_wins(float xn, float lo, float hi) {
     return fabsf(xn - hi) < fabsf(xn - lo);
 }
 
-// fp64 bits of M for the threshold between codes lo < hi: RN(x/s) >= u
-// <=> x - M*s > 0 (s > 0).  The choice is monotone in x_n on [lo, hi], so u
-// is found by bisection over the fp32 values in between (at most 32 steps;
-// near a midpoint of 0 it can lie far from the midpoint, where the rounded
-// distances tie).  Returns false if the bracket is not as expected.
-__device__ inline bool threshold_mid(float lo, float hi, uint64_t& bits) {
-    uint32_t L = order_key(lo), R = order_key(hi);
-    if (upper_wins(lo, lo, hi) || !upper_wins(hi, lo, hi)) return false;
-    while (R - L > 1u) {
-        const uint32_t m = L + (R - L) / 2u;
-        if (upper_wins(from_key(m), lo, hi)) R = m;
-        else L = m;
-    }
-    const float u = from_key(R);
-    const double M = (static_cast<double>(u) + static_cast<double>(from_key(L))) * 0.5;  // exact
+// fp64 bits of M for the switching point u (the smallest fp32 value for
+// which the upper code wins) and its fp32 predecessor p: RN(x/s) >= u <=>
+// x - M*s > 0 (s > 0).
+__device__ inline uint64_t mid_bits(float u, float p) {
+    const double M = (static_cast<double>(u) + static_cast<double>(p)) * 0.5;  // exact
     // An exact tie x/s == M rounds to the even one of pred(u), u: to u means
     // "upper" at equality, so M moves down by 4 fp64 ulps; otherwise it moves
     // up (or stays).  Bits 1:0 stay free for the plane-4 flags of K = 5.
@@ -75,12 +66,43 @@ __device__ inline bool threshold_mid(float lo, float hi, uint64_t& bits) {
     uint64_t b = static_cast<uint64_t>(__double_as_longlong(M));
     if (M > 0.0) b = tie_up ? b - 4u : b;
     else b = tie_up ? b + 4u : b - 4u;
-    bits = b & ~static_cast<uint64_t>(3u);
+    return b & ~static_cast<uint64_t>(3u);
+}
+
+// M for the threshold between codes lo < hi, found by a whole wave.  The
+// choice is monotone in x_n on [lo, hi], so u is found by searching the
+// fp32 values in between in key order (near a midpoint of 0, u can lie far
+// from the midpoint, where the rounded distances tie).  Every round the 64
+// lanes test 64 evenly spaced keys of the bracket [L, R], and the bracket
+// shrinks to the two neighbouring tested keys where the choice changes:
+// 2^32 keys take about 6 rounds.  lo and hi must be the same in every lane
+// (the loop is wave-uniform); every lane gets the result.  Returns false if
+// the bracket is not as expected.
+__device__ inline bool threshold_mid_wave(float lo, float hi, uint64_t& bits) {
+    const uint32_t lane = __lane_id();
+    uint32_t L = order_key(lo), R = order_key(hi);
+    if (upper_wins(lo, lo, hi) || !upper_wins(hi, lo, hi)) return false;
+    while (R - L > 1u) {
+        const uint64_t w = R - L;
+        auto key = [&](uint32_t i) { return L + static_cast<uint32_t>((w * i) >> 6); };
+        // lane 0 tests L itself, known to choose the lower code
+        const bool up = lane != 0 && upper_wins(from_key(key(lane)), lo, hi);
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(up);
+        if (mask == 0) {
+            L = key(63);
+        } else {
+            const uint32_t j = static_cast<uint32_t>(__builtin_ctzll(mask));
+            const uint32_t kj = key(j), kp = key(j - 1);
+            R = kj;
+            L = kp;
+        }
+    }
+    bits = mid_bits(from_key(R), from_key(L));
     return true;
 }
 
 // Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
-// threshold whose window meets the bucket (mid[i] from threshold_mid), the
+// threshold whose window meets the bucket (mid[i] from threshold_mid_wave), the
 // plane bytes of the indices below and above it, and with PLANE4 their
 // plane-4 bits in bits 0 and 1 of M.  Returns false if two windows meet
 // the bucket.
