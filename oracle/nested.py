@@ -15,7 +15,9 @@ Encode is not on the pages (the configuration text says "per-block absmax
 minus its mean offset is 8-bit dynamic-map quantized in groups of 256").
 Reading used here:
 
-    offset    = fp32( correctly rounded float64 mean of the fp32 absmax )
+    offset    = RN32( (sum of a_b, exact) / nb ): the mean, rounded once to
+                fp32 (0 for nb = 0; NaN if any a_b is NaN or both infinities
+                occur; +-inf if one infinity occurs)
     r_b       = RN(a_b - offset)
     (code, absmax2) = blockwise quantize of r with block 256 and the dynamic
                       map as codebook (the same first-index nearest rule, the
@@ -24,18 +26,32 @@ Reading used here:
 Parity: dequantize is pinned in ``tests/test_oracle_nested.py`` (reduction to
 the plain path when offset = 0 and absmax2 = 1; an FMA canary whose fused
 result differs from the separately rounded one, checked with exact
-rationals).  Encode is deterministic by construction; parity unpinned beyond
-its round-trip error bound, because the GPU consumes the state as data.
+rationals).  Encode is pinned in the same file: the offset against exact
+rational means (including sums that fp32 or fp64 accumulation gets wrong),
+the rest against the definition written with exact rationals, and the
+round-trip error bound.
 """
-
-import math
 
 import numpy as np
 
 from . import kbit
-from .numerics import narrow
+from .numerics import exact_sum_f32, narrow, rn32_rational
 
 GROUP2 = 256
+
+
+def mean_offset(a):
+    """RN32 of the exact mean of fp32 values (see the reading above)."""
+    a = np.asarray(a, dtype=np.float32).ravel()
+    if a.size == 0:
+        return np.float32(0.0)
+    if np.isnan(a).any() or (np.isposinf(a).any() and np.isneginf(a).any()):
+        return np.float32(np.nan)
+    if np.isposinf(a).any():
+        return np.float32(np.inf)
+    if np.isneginf(a).any():
+        return np.float32(-np.inf)
+    return rn32_rational(exact_sum_f32(a), a.size << 149)
 
 
 def encode(absmax, qmap2):
@@ -44,8 +60,9 @@ def encode(absmax, qmap2):
     nb = a.size
     if nb == 0:
         return np.zeros(0, np.uint8), np.zeros(0, np.float32), np.float32(0.0)
-    offset = np.float32(math.fsum(a.astype(np.float64).tolist()) / nb)
-    r = (a - offset).astype(np.float32)
+    offset = mean_offset(a)
+    with np.errstate(invalid="ignore", over="ignore"):
+        r = (a - offset).astype(np.float32)
     code, absmax2 = kbit.quantize(r, qmap2, GROUP2)
     return code, absmax2, offset
 

@@ -67,3 +67,52 @@ def raw_bits(a):
     if a.dtype == np.float16:
         return a.view(np.uint16)
     return a
+
+
+def f32_exact_int(a):
+    """Finite fp32 values as exact integers times 2^-149: (sign, magnitude).
+
+    IEEE binary32: biased exponent e, fraction f; normal (e > 0) values are
+    (2^23 + f) * 2^(e - 150), subnormal (e = 0) values f * 2^-149."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).ravel()
+    e = ((bits >> 23) & 0xFF).astype(np.int64)
+    f = (bits & 0x7FFFFF).astype(np.int64)
+    m = np.where(e > 0, f | 0x800000, f)
+    shift = np.maximum(e, 1) - 1
+    neg = (bits >> 31).astype(bool)
+    return neg, m, shift
+
+
+def exact_sum_f32(a):
+    """Exact sum of finite fp32 values, as an integer X with sum = X * 2^-149."""
+    neg, m, shift = f32_exact_int(a)
+    total = 0
+    for s, mm, sh in zip(neg.tolist(), m.tolist(), shift.tolist()):
+        total += -(mm << sh) if s else (mm << sh)
+    return total
+
+
+def rn32_rational(num, den):
+    """num / den (integers, den > 0) rounded to binary32, to nearest, ties to
+    even, with gradual underflow; overflow gives +-inf."""
+    if num == 0:
+        return np.float32(0.0)
+    sign = -1 if num < 0 else 1
+    num = abs(num)
+    # e = floor(log2(num / den))
+    e = num.bit_length() - den.bit_length()
+    if (num << max(0, -e)) < (den << max(0, e)):
+        e -= 1
+    e = max(e, -126)                      # below the normal range: subnormal spacing 2^-149
+    # q = num / den / 2^(e - 23), rounded to an integer (24 significant bits)
+    sh = 23 - e
+    n2, d2 = (num << sh, den) if sh >= 0 else (num, den << -sh)
+    q, r = divmod(n2, d2)
+    if 2 * r > d2 or (2 * r == d2 and q & 1):
+        q += 1
+    if q == 1 << 24:                      # rounding carried into the next binade
+        q >>= 1
+        e += 1
+    if e > 127:
+        return np.float32(sign * np.inf)
+    return np.float32(sign * float(q) * 2.0 ** (e - 23))
