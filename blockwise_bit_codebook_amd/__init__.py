@@ -20,7 +20,7 @@ import numpy as np
 
 __all__ = [
     "KbitError", "lib", "codebook_nf", "codebook_fp4", "codebook_lloyd_max_normal",
-    "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested",
+    "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax",
     "quantize_act_fwht_k4_bf16", "n_words", "n_blocks",
 ]
 
@@ -169,6 +169,30 @@ def dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offs
     _check(name, fn(_ptr(packed), _ptr(codebook16), _ptr(absmax_code), _ptr(qmap2), _ptr(absmax2),
                     ct.c_float(float(offset)), _ptr(out), n, blocksize, _stream(packed.device)))
     return out
+
+
+def quantize_nested_absmax(absmax, qmap2, absmax_code=None, absmax2=None, offset=None, workspace=None):
+    """Nested state of fp32 per-block absmax -> (absmax_code u8, absmax2 fp32, offset fp32[1]).
+
+    offset stays on the device; the workspace is allocated here unless given."""
+    torch = _torch()
+    nb = absmax.numel()
+    dev = absmax.device
+    if absmax_code is None:
+        absmax_code = torch.empty(nb, dtype=torch.uint8, device=dev)
+    if absmax2 is None:
+        absmax2 = torch.empty(-(-nb // 256), dtype=torch.float32, device=dev)
+    if offset is None:
+        offset = torch.zeros(1, dtype=torch.float32, device=dev)
+    need = lib().kbit_nested_workspace_bytes(nb)
+    if need < 0:
+        raise KbitError("kbit_nested_workspace_bytes", -1, "nb out of range")
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    name = "quantize_nested_absmax"
+    _check(name, lib().quantize_nested_absmax(_ptr(absmax), nb, _ptr(qmap2), _ptr(absmax_code), _ptr(absmax2),
+                                              _ptr(offset), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return absmax_code, absmax2, offset
 
 
 def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=None):

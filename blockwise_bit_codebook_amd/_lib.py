@@ -29,6 +29,8 @@ def _signatures():
         ("kbit_codebook_lloyd_max_normal", [ct.c_int, _p]),
         ("kbit_dynamic_map8", [_p]),
         ("quantize_act_fwht_k4_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p]),
+        ("kbit_nested_workspace_bytes", [_i64]),
+        ("quantize_nested_absmax", [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]),
     ]
     for t in DTYPES:
         for k in KS:
@@ -52,7 +54,7 @@ def load(path=LIB_PATH):
     for name, args in SIGNATURES:
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ct.c_char_p if name == "kbit_strerror" else ct.c_int
+        fn.restype = {"kbit_strerror": ct.c_char_p, "kbit_nested_workspace_bytes": ct.c_int64}.get(name, ct.c_int)
     return lib
 
 

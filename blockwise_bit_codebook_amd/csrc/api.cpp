@@ -97,6 +97,8 @@ int do_nested(Dtype t, const uint32_t* packed, const float* codebook16, const ui
 
 }  // namespace
 
+constexpr int64_t kMaxNestedBlocks = int64_t(1) << 36;
+
 int device_cu_count() {
     const int v = current_device_cus();
     return v > 0 ? v : 1;
@@ -175,6 +177,26 @@ KBIT_DEFINE_ALL_K(bf16, uint16_t, Dtype::bf16)
 KBIT_DEFINE_NESTED(fp32, float, Dtype::fp32)
 KBIT_DEFINE_NESTED(fp16, uint16_t, Dtype::fp16)
 KBIT_DEFINE_NESTED(bf16, uint16_t, Dtype::bf16)
+
+int64_t kbit_nested_workspace_bytes(int64_t nb) {
+    if (nb < 0 || nb > kbit::kMaxNestedBlocks) return -1;
+    return nb == 0 ? 0 : kbit::nested_workspace_bytes(nb);
+}
+
+int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2, uint8_t* absmax_code,
+                           float* absmax2, float* offset, void* workspace, int64_t workspace_bytes,
+                           void* stream) {
+    if (nb < 0 || nb > kbit::kMaxNestedBlocks) return KBIT_EINVAL;
+    if (nb == 0) return KBIT_OK;
+    if (!absmax || !qmap2 || !absmax_code || !absmax2 || !offset || !workspace) return KBIT_EINVAL;
+    if (workspace_bytes < kbit::nested_workspace_bytes(nb)) return KBIT_EINVAL;
+    if (!kbit::aligned(absmax, 4) || !kbit::aligned(qmap2, 4) || !kbit::aligned(absmax2, 4) ||
+        !kbit::aligned(offset, 4) || !kbit::aligned(workspace, 8))
+        return KBIT_EALIGN;
+    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
+    return kbit::map_launch(
+        kbit::launch_nested_encode(absmax, nb, qmap2, absmax_code, absmax2, offset, workspace, stream));
+}
 
 int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const uint32_t* sign_bits,
                               const float* codebook16, float* row_norm, uint32_t* packed, void* stream) {

@@ -23,6 +23,12 @@ int launch_dequantize_nested(Dtype t, const uint32_t* packed, const float* codeb
                              const uint8_t* code, const float* qmap2, const float* absmax2,
                              float offset, void* out, int64_t n, int log2B, void* stream);
 
+// Workspace bytes the nested-state encoder needs for nb blocks.
+int64_t nested_workspace_bytes(int64_t nb);
+
+int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
+                         float* offset, void* workspace, void* stream);
+
 int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
 

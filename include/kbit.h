@@ -207,6 +207,35 @@ KBIT_DECLARE_NESTED(fp16, uint16_t)
 KBIT_DECLARE_NESTED(bf16, uint16_t)
 
 /* ------------------------------------------------------------------------
+ * Nested-state encoder: the input of dequantize_4bit_nested from the fp32
+ * per-block absmax.  [PR2051] Summary describes the state (8-bit codes per
+ * block over groups of 256, a group absmax and a mean offset) but not its
+ * encoder; this is the plain reading:
+ *   offset        = RN32( (exact sum of absmax) / nb )   (one rounding;
+ *                   NaN if any value is NaN or both infinities occur; an
+ *                   infinity if only that one occurs)
+ *   r_b           = RN(absmax[b] - offset)
+ *   absmax2[g]    = max |r_b| over blocks 256g .. min(256g+255, nb-1)
+ *                   (NaN propagates)
+ *   absmax_code[b]= smallest i minimising
+ *                   |RN( RN(r_b / max(absmax2[b/256], 1e-8f)) - qmap2[i] )|
+ * absmax      : device, nb float32 (any values; the output of quantize_kbit_*).
+ * qmap2       : device, 256 finite float32 (e.g. kbit_dynamic_map8; sorted
+ *               maps take a binary search, others the full scan).
+ * absmax_code : device, nb uint8 (output).
+ * absmax2     : device, ceil(nb/256) float32 (output).
+ * offset      : device, 1 float32 (output; not written when nb == 0).
+ * workspace   : device, >= kbit_nested_workspace_bytes(nb) bytes, 8-byte
+ *               aligned, owned by the caller; its contents are scratch (no
+ *               initialisation needed, overwritten by every call).
+ * nb <= 2^36.  Three kernels run in order on the stream.
+ * --------------------------------------------------------------------- */
+int64_t kbit_nested_workspace_bytes(int64_t nb);  /* -1 for nb outside [0, 2^36] */
+int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2,
+                           uint8_t* absmax_code, float* absmax2, float* offset,
+                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * W4A4-style activation assignment ([ORBIT] README W4A4 fast path and
  * CARD.md quantize_activations_packed_w4; exact Lloyd-Max centroids, packed
  * 4-bit output).  Per row r of X (rows x d, bf16, row-major):

@@ -26,7 +26,7 @@ def _lib():
 
 def _declared_functions():
     out = subprocess.run(["gcc", "-E", "-P", "-x", "c", HEADER], capture_output=True, text=True, check=True).stdout
-    names = re.findall(r"\b(?:int|const char\s*\*)\s+(\w+)\s*\(", out)
+    names = re.findall(r"\b(?:int|int64_t|const char\s*\*)\s+(\w+)\s*\(", out)
     return sorted(set(names))
 
 
@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 24 + 3 + 1, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 1, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -110,6 +110,20 @@ def test_validation_codes_before_any_device_access():
     assert de(_A16, _A16, _B1, _A4, 10, 64, None) == -3           # out misaligned
     assert de(_A16, _A16, None, _A16, 10, 64, None) == -1
     assert de(None, None, None, None, 0, 64, None) == 0
+    assert lib.kbit_nested_workspace_bytes(0) == 0
+    assert lib.kbit_nested_workspace_bytes(-1) == -1
+    assert lib.kbit_nested_workspace_bytes((1 << 36) + 1) == -1
+    wsb = lib.kbit_nested_workspace_bytes(1000)
+    assert wsb >= 8 * (2 * 256 + 1)
+    ne = lib.quantize_nested_absmax
+    _W8 = ct.c_void_p(0x40000)
+    assert ne(None, 0, None, None, None, None, None, 0, None) == 0                   # empty: no-op
+    assert ne(_A16, -1, _A16, _A16, _A16, _A16, _W8, wsb, None) == -1
+    assert ne(_A16, 1000, _A16, _A16, _A16, _A16, None, wsb, None) == -1          # no workspace
+    assert ne(_A16, 1000, _A16, _A16, _A16, _A16, _W8, wsb - 1, None) == -1       # workspace too small
+    assert ne(_A16, 1000, _A16, _A16, _A16, _A16, ct.c_void_p(0x40004), wsb, None) == -3
+    assert ne(_A16, 1000, _A16, None, _A16, _A16, _W8, wsb, None) == -1
+    assert ne(_A16, 1000, ct.c_void_p(0x20002), _A16, _A16, _A16, _W8, wsb, None) == -3
     act = lib.quantize_act_fwht_k4_bf16
     assert act(_A16, 4, 2048, _A16, _A16, _A16, _A16, None) == -1  # d must be 4096
     assert act(_A16, 0, 4096, None, None, None, None, None) == 0
