@@ -63,6 +63,9 @@ def kernel_bytes(n):
         "quantize_kbit_e4m4_bf16_k4": 2 * n + planes + nb + tables,
         "dequantize_kbit_e4m4_bf16_k4": planes + nb + 2 * n + tables,
         "dequantize_kbit_bf16_k4": planes + 4 * nb + 2 * n + tables,
+        # nested-state encoder: absmax read twice (the mean comes first),
+        # codes, group absmax, offset and the map
+        "quantize_nested_absmax": 8 * nb + nb + 4 * (-(-nb // GROUP2)) + 4 + 4 * 256,
     }
 
 
@@ -98,6 +101,8 @@ _Q_SRC = ["blockwise_bit_codebook_amd/csrc/quantize.hip", "blockwise_bit_codeboo
           "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/e4m4.h"]
 _D_SRC = ["blockwise_bit_codebook_amd/csrc/dequantize.hip", "blockwise_bit_codebook_amd/csrc/device.h",
           "blockwise_bit_codebook_amd/csrc/e4m4.h"]
+_E_SRC = ["blockwise_bit_codebook_amd/csrc/nested_encode.hip", "blockwise_bit_codebook_amd/csrc/exact_mean.h",
+          "blockwise_bit_codebook_amd/csrc/device.h"]
 KERNELS = {
     # name used in the JSON line: (substrings that all appear in the HIP kernel's demangled name,
     # sources that define it)
@@ -106,6 +111,10 @@ KERNELS = {
     "quantize_kbit_e4m4_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "E4m4Scale, 4,"), _Q_SRC),
     "dequantize_kbit_e4m4_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "E4m4Scale>"), _D_SRC),
     "dequantize_kbit_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "PlainScale>"), _D_SRC),
+    # the nested-state encoder's three launches
+    "nested_bins_kernel": (("::nested_bins_kernel",), _E_SRC),
+    "nested_offset_kernel": (("::nested_offset_kernel",), _E_SRC),
+    "nested_encode_kernel": (("::nested_encode_kernel",), _E_SRC),
 }
 
 
@@ -166,8 +175,10 @@ def summarize(trace_dir, fetch_dir, write_dir):
                            "write_scale": round(scale["WRITE_SIZE"], 4)},
            "kernels": {}}
     lines = ["# rocprofv3 summary: k-bit quantize / dequantize kernels, 8192x8192 bf16, NF4, blocksize 64", "",
-             "The bench step is quantize_kbit_bf16_k4 + dequantize_4bit_nested_bf16; the E4M4-scale pair and "
-             "the plain fp32-scale dequantize run on the same tensor as side measurements.", "",
+             "The bench step is quantize_kbit_bf16_k4 + dequantize_4bit_nested_bf16; the E4M4-scale pair, "
+             "the plain fp32-scale dequantize and the nested-state encoder (quantize_nested_absmax: "
+             "nested_bins/offset/encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements.",
+             "",
              "Commands (R = repository root; the counter runs are separate passes):", "", "```"]
     lines += PROFILE_COMMANDS + ["```", "",
                                  f"Calibration: the last {CAL_COPIES} device copies of {CAL_BYTES >> 20} MiB each; "
@@ -186,13 +197,15 @@ def summarize(trace_dir, fetch_dir, write_dir):
         w_kib = per_kernel[name]["WRITE_SIZE"]
         rd = f_kib * 1024 * scale["FETCH_SIZE"]
         wr = w_kib * 1024 * scale["WRITE_SIZE"]
+        ab = alg.get(name)
         out["kernels"][name] = {"avg_us": round(avg, 3), "dispatches": len(durs),
                                 "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
                                 "read_bytes": int(rd), "write_bytes": int(wr), "traffic": int(rd + wr),
-                                "algorithmic_bytes": alg[name], "source_sha256_16": source_digest(srcs)}
+                                "algorithmic_bytes": ab, "source_sha256_16": source_digest(srcs)}
+        ratio = f"{(rd + wr) / ab:.3f}" if ab else "—"
+        gbs = f"{ab / (avg * 1e-6) / 1e9:.0f}" if ab else "—"
         lines.append(f"| {name} | {len(durs)} | {avg:.2f} | {min(durs) / 1e3:.2f} | {max(durs) / 1e3:.2f} | "
-                     f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {alg[name] / 1e6:.1f} | {(rd + wr) / alg[name]:.3f} | "
-                     f"{alg[name] / (avg * 1e-6) / 1e9:.0f} |")
+                     f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {ab / 1e6 if ab else 0:.1f} | {ratio} | {gbs} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
@@ -328,6 +341,10 @@ def main(argv=None):
             "absmax2": torch.from_numpy(a2_np).to(dev),
             "out": torch.empty(n, dtype=torch.bfloat16, device=dev),
             "code8": torch.empty(nb, dtype=torch.uint8, device=dev),
+            "enc_code": torch.empty(nb, dtype=torch.uint8, device=dev),
+            "enc_a2": torch.empty(-(-nb // GROUP2), dtype=torch.float32, device=dev),
+            "enc_off": torch.zeros(1, dtype=torch.float32, device=dev),
+            "ws": torch.empty(kb.lib().kbit_nested_workspace_bytes(nb), dtype=torch.uint8, device=dev),
         })
     torch.cuda.synchronize()
 
@@ -351,6 +368,10 @@ def main(argv=None):
 
     def dequant_plain(s):
         kb.dequantize_kbit(s["packed"], cb, s["absmax"], K, n, torch.bfloat16, BLOCK, out=s["out"])
+
+    def encode_nested(s):
+        kb.quantize_nested_absmax(s["absmax"], qmap, absmax_code=s["enc_code"], absmax2=s["enc_a2"],
+                                  offset=s["enc_off"], workspace=s["ws"])
 
     for s_ in sets:                              # eager once per set: per-device setup happens here
         step(s_)
@@ -414,7 +435,7 @@ def main(argv=None):
     # every round: each dequantize reads scales written by its own quantize.
     rr = round_robin({"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only,
                       "quantize_kbit_e4m4_bf16_k4": quant_e4m4, "dequantize_kbit_e4m4_bf16_k4": dequant_e4m4,
-                      "dequantize_kbit_bf16_k4": dequant_plain}, reps)
+                      "dequantize_kbit_bf16_k4": dequant_plain, "quantize_nested_absmax": encode_nested}, reps)
     tq, tn = rr["quantize_kbit_bf16_k4"], rr["dequantize_4bit_nested_bf16"]
     qbytes, nbytes = algorithmic_bytes(n)
     ms_step = wall * 1e3 / args.steps
@@ -439,6 +460,9 @@ def main(argv=None):
                                                 "dequantize_kbit_bf16_k4")}
     e4["note"] = ("same 8192x8192 bf16 tensor and NF4 codebook; scales as one E4M4 byte per block "
                   "(the last entry: fp32 scales, for comparison)")
+    enc = kstats(rr["quantize_nested_absmax"], kbytes["quantize_nested_absmax"], elems=nb)
+    enc["note"] = ("nested-state encoder on the 1,048,576 fp32 block absmax of the same tensor: three launches "
+                   "(significand sums, exact mean, codes); elements_per_s counts blocks")
 
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
@@ -504,6 +528,7 @@ def main(argv=None):
         "quantize": kq,
         "nested_dequantize": kn,
         "e4m4_scales": e4,
+        "nested_state_encoder": enc,
         "fp4_codebook": fp4,
         "warm": warm,
         "act_fwht": act,

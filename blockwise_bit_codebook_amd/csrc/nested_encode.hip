@@ -14,10 +14,12 @@
 //
 // How: three launches on one stream.
 //   1. Each workgroup adds the integer significands of its values into
-//      per-wave LDS bins by (sign, exponent) with 64-bit LDS atomics, and
-//      writes its 512 bin sums and its NaN/infinity flags to the workspace.
-//   2. One workgroup adds the bins over workgroups, builds the exact sum as
-//      a 320-bit integer and rounds the mean once (exact_mean.h).
+//      per-wave LDS bins by (sign, exponent) with 64-bit LDS atomics, folds
+//      the bins into 32-bit-limb accumulators of the positive and negative
+//      sums (exact_mean.h), and writes them and its NaN/infinity flags to
+//      the workspace: 25 words per workgroup.
+//   2. One workgroup adds the records (32 threads per word), resolves the
+//      carries of the 320-bit sums and rounds the mean once.
 //   3. One wave per group: four blocks per lane, IEEE division, and the
 //      nearest code by binary search over the sorted map plus a walk to the
 //      lowest index with the same rounded distance (a full scan if the map
@@ -32,7 +34,9 @@ namespace {
 constexpr int kBinThreads = 256;
 constexpr int kBinWaves = kBinThreads / kWave;
 constexpr int kMaxBinGroups = 256;  // workgroups of launch 1 (the workspace holds one record each)
-constexpr int kRecordWords = 2 * 256 + 1;  // uint64: bins[sign][exponent], then the flags
+constexpr int kLimbWords = kWideLimbs + 2;
+constexpr int kRecordWords = 2 * kLimbWords + 1;  // uint64: limbs[sign][i], then the flags
+constexpr int kOffsetParts = 32;                  // threads per record word in launch 2
 constexpr int kGroup2 = 256;
 constexpr float kEps2 = 1e-8f;
 constexpr uint32_t kFlagNan = 1, kFlagPosInf = 2, kFlagNegInf = 4;
@@ -51,55 +55,67 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
     if (threadIdx.x == 0) flags = 0;
     __syncthreads();
     uint32_t my_flags = 0;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBinThreads + threadIdx.x; i < nb;
-         i += static_cast<int64_t>(gridDim.x) * kBinThreads) {
-        const uint32_t u = __float_as_uint(a[i]);
-        const uint32_t e = (u >> 23) & 0xFFu, f = u & 0x7FFFFFu, sg = u >> 31;
-        if (e == 0xFFu) {
-            my_flags |= f ? kFlagNan : (sg ? kFlagNegInf : kFlagPosInf);
-        } else if (e | f) {
-            atomicAdd(&bins[wave][sg][e], static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
+    // four independent loads in flight per thread
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBinThreads;
+    for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kBinThreads + threadIdx.x; i0 < nb; i0 += 4 * stride) {
+        uint32_t u[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) u[k] = i0 + k * stride < nb ? __float_as_uint(a[i0 + k * stride]) : 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t e = (u[k] >> 23) & 0xFFu, f = u[k] & 0x7FFFFFu, sg = u[k] >> 31;
+            if (e == 0xFFu) {
+                my_flags |= f ? kFlagNan : (sg ? kFlagNegInf : kFlagPosInf);
+            } else if (e | f) {
+                atomicAdd(&bins[wave][sg][e], static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
+            }
         }
     }
     if (my_flags) atomicOr(&flags, my_flags);
     __syncthreads();
-    uint64_t* rec = ws + static_cast<int64_t>(blockIdx.x) * kRecordWords;
+    // bins -> limb accumulators (each limb below 2^44 per workgroup)
+    __shared__ unsigned long long limbs[2][kLimbWords];
+    if (threadIdx.x < 2 * kLimbWords) (&limbs[0][0])[threadIdx.x] = 0;
+    __syncthreads();
     for (int i = threadIdx.x; i < 2 * 256; i += kBinThreads) {
-        uint64_t s = 0;
+        uint64_t sum = 0;
 #pragma unroll
-        for (int w = 0; w < kBinWaves; ++w) s += (&bins[w][0][0])[i];
-        rec[i] = s;
+        for (int w = 0; w < kBinWaves; ++w) sum += (&bins[w][0][0])[i];
+        const int sg = i >> 8, e = i & 255;
+        if (sum != 0) {
+            const WidePieces q = wide_pieces(sum, (e > 0 ? e : 1) - 1);
+            atomicAdd(&limbs[sg][q.w], static_cast<unsigned long long>(q.p0));
+            atomicAdd(&limbs[sg][q.w + 1], static_cast<unsigned long long>(q.p1));
+            atomicAdd(&limbs[sg][q.w + 2], static_cast<unsigned long long>(q.p2));
+        }
     }
-    if (threadIdx.x == 0) rec[2 * 256] = flags;
+    __syncthreads();
+    uint64_t* rec = ws + static_cast<int64_t>(blockIdx.x) * kRecordWords;
+    if (threadIdx.x < 2 * kLimbWords) rec[threadIdx.x] = (&limbs[0][0])[threadIdx.x];
+    if (threadIdx.x == 0) rec[2 * kLimbWords] = flags;
 }
 
-// One workgroup: thread t sums bin t (sign t / 256, exponent t % 256) over
-// the records, adds its three 32-bit-limb pieces into LDS accumulators, and
-// thread 0 rounds the mean from the limbs.
-__global__ __launch_bounds__(512) void nested_offset_kernel(const uint64_t* __restrict__ ws, int groups, int64_t nb,
-                                                            float* __restrict__ offset) {
-    __shared__ unsigned long long limbs[2][kWideLimbs + 2];
-    __shared__ uint32_t flags;
-    if (threadIdx.x < 2 * (kWideLimbs + 2)) (&limbs[0][0])[threadIdx.x] = 0;
-    if (threadIdx.x == 0) flags = 0;
+// One workgroup: word k of the records (a limb of one sign, or the flags)
+// is summed (ORed) over the records by kOffsetParts threads; thread 0 then
+// rounds the mean from the limbs.  Limb totals stay below 2^52.
+__global__ __launch_bounds__(kRecordWords * kOffsetParts) void nested_offset_kernel(
+    const uint64_t* __restrict__ ws, int groups, int64_t nb, float* __restrict__ offset) {
+    __shared__ unsigned long long total[kRecordWords];
+    if (threadIdx.x < kRecordWords) total[threadIdx.x] = 0;
     __syncthreads();
-    uint64_t s = 0;
-    uint32_t f = 0;
-    for (int g = 0; g < groups; ++g) {
-        const uint64_t* rec = ws + static_cast<int64_t>(g) * kRecordWords;
-        s += rec[threadIdx.x];
-        if (threadIdx.x == 0) f |= static_cast<uint32_t>(rec[2 * 256]);
+    const int k = threadIdx.x % kRecordWords, part = threadIdx.x / kRecordWords;
+    uint64_t acc = 0;
+    for (int g = part; g < groups; g += kOffsetParts) {
+        const uint64_t v = ws[static_cast<int64_t>(g) * kRecordWords + k];
+        acc = k == 2 * kLimbWords ? (acc | v) : acc + v;
     }
-    const int sg = threadIdx.x >> 8, e = threadIdx.x & 255;
-    if (s != 0 && e != 255) {
-        const WidePieces q = wide_pieces(s, (e > 0 ? e : 1) - 1);
-        atomicAdd(&limbs[sg][q.w], static_cast<unsigned long long>(q.p0));
-        atomicAdd(&limbs[sg][q.w + 1], static_cast<unsigned long long>(q.p1));
-        atomicAdd(&limbs[sg][q.w + 2], static_cast<unsigned long long>(q.p2));
+    if (acc != 0) {
+        if (k == 2 * kLimbWords) atomicOr(&total[k], static_cast<unsigned long long>(acc));
+        else atomicAdd(&total[k], static_cast<unsigned long long>(acc));
     }
-    if (threadIdx.x == 0) flags = f;
     __syncthreads();
     if (threadIdx.x == 0) {
+        const uint32_t flags = static_cast<uint32_t>(total[2 * kLimbWords]);
         uint32_t bits;
         if ((flags & kFlagNan) || ((flags & kFlagPosInf) && (flags & kFlagNegInf))) {
             bits = 0x7FC00000u;
@@ -108,11 +124,11 @@ __global__ __launch_bounds__(512) void nested_offset_kernel(const uint64_t* __re
         } else if (flags & kFlagNegInf) {
             bits = 0xFF800000u;
         } else {
-            uint64_t pos[kWideLimbs + 2], neg[kWideLimbs + 2];
+            uint64_t pos[kLimbWords], neg[kLimbWords];
 #pragma unroll
-            for (int i = 0; i < kWideLimbs + 2; ++i) {
-                pos[i] = limbs[0][i];
-                neg[i] = limbs[1][i];
+            for (int i = 0; i < kLimbWords; ++i) {
+                pos[i] = total[i];
+                neg[i] = total[kLimbWords + i];
             }
             bits = mean_from_limbs(pos, neg, static_cast<uint64_t>(nb));
         }
@@ -219,7 +235,8 @@ int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, ui
     const int groups = bin_groups(nb);
     uint64_t* ws = static_cast<uint64_t*>(workspace);
     hipLaunchKernelGGL(nested_bins_kernel, dim3(groups), dim3(kBinThreads), 0, st, absmax, nb, ws);
-    hipLaunchKernelGGL(nested_offset_kernel, dim3(1), dim3(512), 0, st, ws, groups, nb, offset);
+    hipLaunchKernelGGL(nested_offset_kernel, dim3(1), dim3(kRecordWords * kOffsetParts), 0, st, ws, groups, nb,
+                       offset);
     const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
     const int64_t grid = (ngroups + kEncWaves - 1) / kEncWaves;
     hipLaunchKernelGGL(nested_encode_kernel, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st, absmax, nb,
