@@ -21,9 +21,12 @@
 // contiguous halves, so every partial is the same tree node as in the
 // definition) and LDS across the 4 waves of the row.  The 12 butterfly
 // stages run in registers as three 16-point passes over the index bits
-// 0-3, 4-7 and 8-11: between passes the row goes through LDS (padded by 16
-// floats per 256 so that the strided reads are conflict-free) and each
-// thread picks up the 16 elements that differ in the next 4 bits.  Every
+// 0-3, 4-7 and 8-11: between passes the row goes through LDS and each
+// thread picks up the 16 elements that differ in the next 4 bits.  The LDS
+// layout of element 256a + 16b + c is 272a + 16b + (c ^ 4*((b >> 1) & 3)):
+// the 16 floats per 256 of padding keep the strided passes conflict-free,
+// and the swizzle of the four 16-byte chunks does the same for the
+// contiguous 16-byte-per-lane accesses.  Every
 // butterfly of a stage is independent and the stages keep their order, so
 // the result is the definition's.  The row then goes back to contiguous
 // order for the assignment, which uses the exact switching-point test of
@@ -51,7 +54,8 @@ constexpr float kActMinGap = 0x1p-12f;               // |z| <= 64: distances rou
 constexpr float kQMax = 0x1.fffffep+1f;              // largest float below 4
 constexpr int kBufFloats = kD + (kD / 256) * 16;     // padded row buffer
 
-__device__ __forceinline__ int pad(int e) { return e + ((e >> 8) << 4); }
+// LDS position of element 256a + 16b + c of the row.
+__device__ __forceinline__ int swz(int a, int b, int c) { return 272 * a + 16 * b + (c ^ (((b >> 1) & 3) << 2)); }
 
 using ActTables = ThresholdTables<16>;
 
@@ -100,6 +104,22 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     const int lane = __lane_id();
     const int wave = t / kWave;
 
+    // The raw 32 bytes of the thread's share of a row (zeros past the last
+    // row).  The first row's loads go out before the table build, and each
+    // iteration loads the next row before it works on the current one.
+    const int64_t row_step = static_cast<int64_t>(gridDim.x) * kSlots;
+    auto load_raw = [&](int64_t row, uint4& a, uint4& b) {
+        a = make_uint4(0, 0, 0, 0);
+        b = make_uint4(0, 0, 0, 0);
+        if (row < rows) {
+            const uint16_t* xr = X + row * kD + t * kPer;
+            a = *reinterpret_cast<const uint4*>(xr);
+            b = *reinterpret_cast<const uint4*>(xr + 8);
+        }
+    };
+    uint4 cur_a, cur_b;
+    load_raw(static_cast<int64_t>(blockIdx.x) * kSlots + slot, cur_a, cur_b);
+
     // ---- table build (once per workgroup) ---------------------------------
     float c[16];
 #pragma unroll
@@ -114,13 +134,19 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     }
     if (threadIdx.x == 0) T.fail = 0;
     if (threadIdx.x < 16) T.code[threadIdx.x] = c[threadIdx.x];
-    // One wave per threshold (the search is wave-cooperative); a failed
-    // search leaves the sentinel, which fails the table below.
-    for (int i = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave) + 1; i < 16; i += kActThreads / kWave) {
-        const float lo = cb[i - 1], hi = cb[i];  // wave-uniform
-        uint64_t m = 0;
-        if (fast && lo != hi && !threshold_mid_wave(lo, hi, m)) m = kNoMid;
-        if (lane == 0) T.mid[i] = m;
+    // One half-wave per threshold, all searched at once; a failed search
+    // leaves the sentinel, which fails the table below.
+    {
+        constexpr int kGroups = 2 * kActThreads / kWave;
+        const int gid = 2 * static_cast<int>(threadIdx.x / kWave) + (lane >> 5);
+        for (int i0 = 1; i0 < 16; i0 += kGroups) {  // uniform trip count
+            const int i = i0 + gid;
+            const bool real = i < 16;
+            const float lo = real ? cb[i - 1] : 0.0f, hi = real ? cb[i] : 0.0f;
+            uint64_t m = 0;
+            const bool ok = threshold_mid_group<32>(lo, hi, m);  // every lane calls it
+            if (real && (lane & 31) == 0) T.mid[i] = (fast && lo != hi) ? (ok ? m : kNoMid) : 0u;
+        }
     }
     if (threadIdx.x == 0) T.mid[0] = 0;
     __syncthreads();
@@ -147,6 +173,9 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     for (int i = 0; i < kPer / 2; ++i)
         flip[i] = (((signs >> (2 * i)) & 1u) << 15) | (((signs >> (2 * i + 1)) & 1u) << 31);
     const int hi4 = t >> 4, lo4 = t & 15;
+    // contiguous access of elements 16t .. 16t+15 (a = hi4, b = lo4): chunk k
+    // of the thread's 16 sits at float offset 4*(k ^ s) of its segment
+    const int seg = 272 * hi4 + 16 * lo4, sw = (lo4 >> 1) & 3;
 
     // Every thread runs the same number of iterations (barriers inside);
     // a slot past the last row computes on zeros and stores nothing.
@@ -158,12 +187,8 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
         float* ws = wave_sum[slot];
         float v[kPer];
         {
-            uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-            if (valid) {
-                const uint16_t* xr = X + row * kD + t * kPer;
-                a = *reinterpret_cast<const uint4*>(xr);
-                b = *reinterpret_cast<const uint4*>(xr + 8);
-            }
+            const uint4 a = cur_a, b = cur_b;
+            load_raw(row + row_step, cur_a, cur_b);
             const uint32_t w[8] = {a.x ^ flip[0], a.y ^ flip[1], a.z ^ flip[2], a.w ^ flip[3],
                                    b.x ^ flip[4], b.y ^ flip[5], b.z ^ flip[6], b.w ^ flip[7]};
 #pragma unroll
@@ -191,38 +216,35 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
         }
         // --- pass 1 (bits 0-3), to LDS -----------------------------------------
         fwht16(v);
-        {
-            float4* p = reinterpret_cast<float4*>(rb + pad(t * kPer));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-        }
+        for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<float4*>(rb + seg + 4 * (k ^ sw)) = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2],
+                                                                              v[4 * k + 3]);
         __syncthreads();
         const float norm = sqrtf((ws[0] + ws[1]) + (ws[2] + ws[3]));
         // --- pass 2 (bits 4-7): elements hi4*256 + i*16 + lo4 ---------------
         {
-            const int b0 = pad(hi4 * 256 + lo4);
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) v[i] = rb[b0 + i * 16];
+            for (int i = 0; i < kPer; ++i) v[i] = rb[swz(hi4, i, lo4)];
             fwht16(v);
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) rb[b0 + i * 16] = v[i];
+            for (int i = 0; i < kPer; ++i) rb[swz(hi4, i, lo4)] = v[i];
         }
         __syncthreads();
         // --- pass 3 (bits 8-11): elements i*256 + t --------------------------
         {
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) v[i] = rb[i * 272 + t];
+            for (int i = 0; i < kPer; ++i) v[i] = rb[swz(i, hi4, lo4)];
             fwht16(v);
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) rb[i * 272 + t] = v[i];
+            for (int i = 0; i < kPer; ++i) rb[swz(i, hi4, lo4)] = v[i];
         }
         __syncthreads();
         // --- back to contiguous order: elements 16t .. 16t+15 ---------------
         {
-            const float4* p = reinterpret_cast<const float4*>(rb + pad(t * kPer));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float4 f = p[k];
+                const float4 f = *reinterpret_cast<const float4*>(rb + seg + 4 * (k ^ sw));
                 v[4 * k] = f.x;
                 v[4 * k + 1] = f.y;
                 v[4 * k + 2] = f.z;

@@ -69,40 +69,81 @@ __device__ inline uint64_t mid_bits(float u, float p) {
     return b & ~static_cast<uint64_t>(3u);
 }
 
-// M for the threshold between codes lo < hi, found by a whole wave.  The
-// choice is monotone in x_n on [lo, hi], so u is found by searching the
-// fp32 values in between in key order (near a midpoint of 0, u can lie far
-// from the midpoint, where the rounded distances tie).  Every round the 64
-// lanes test 64 evenly spaced keys of the bracket [L, R], and the bracket
-// shrinks to the two neighbouring tested keys where the choice changes:
-// 2^32 keys take about 6 rounds.  lo and hi must be the same in every lane
-// (the loop is wave-uniform); every lane gets the result.  Returns false if
-// the bracket is not as expected.
-__device__ inline bool threshold_mid_wave(float lo, float hi, uint64_t& bits) {
+// M for the threshold between codes lo < hi, found by a group of G lanes
+// (G = 32 or 64; lane group lane / G searches its own lo, hi).  The choice
+// is monotone in x_n on [lo, hi], so u is found by searching the fp32
+// values in between in key order (near a midpoint of 0, u can lie far from
+// the midpoint, where the rounded distances tie).  The first round tests
+// the G keys centred on the fp32 midpoint, where u almost always lies;
+// then every round the lanes test G evenly spaced keys of the bracket
+// [L, R], which shrinks to the two neighbouring tested keys where the
+// choice changes (2^32 keys take at most 7 rounds of 32).  The loop runs
+// until every group of the wave is done, so all lanes of the wave must
+// call it; each lane gets its group's result.  Returns false if the bracket
+// is not as expected.
+template <int G>
+__device__ inline bool threshold_mid_group(float lo, float hi, uint64_t& bits) {
+    static_assert(G == 32 || G == 64, "lane groups of 32 or 64");
     const uint32_t lane = __lane_id();
+    const uint32_t i = lane % G;
+    const uint32_t gshift = G == 64 ? 0u : (lane / G) * 32u;  // the group's bits in a ballot
+    auto group_bits = [&](uint64_t m) -> uint64_t {
+        return G == 64 ? m : ((m >> gshift) & 0xFFFFFFFFull);
+    };
     uint32_t L = order_key(lo), R = order_key(hi);
-    if (upper_wins(lo, lo, hi) || !upper_wins(hi, lo, hi)) return false;
-    while (R - L > 1u) {
+    const bool ok = !upper_wins(lo, lo, hi) && upper_wins(hi, lo, hi);
+    if (!ok) L = R - 1;  // nothing to search; reported below
+    // round 0: keys mid - G/2 + 1 .. mid + G/2 inside (L, R)
+    {
+        const uint32_t mk = order_key((lo + hi) * 0.5f);
+        const uint32_t k = mk + i - (G / 2 - 1);
+        const bool inside = k > L && k < R;
+        const bool up = inside && upper_wins(from_key(k), lo, hi);
+        const uint64_t upm = group_bits(__builtin_amdgcn_ballot_w64(up));
+        const uint64_t inm = group_bits(__builtin_amdgcn_ballot_w64(inside));
+        // the tested keys are consecutive: the first "up" key and the key
+        // below it bracket u if that key is also inside (or is L)
+        if (R - L > 1u && inm != 0) {
+            const uint32_t first_in = mk - (G / 2 - 1) + static_cast<uint32_t>(__builtin_ctzll(inm));
+            const uint32_t last_in = mk - (G / 2 - 1) + static_cast<uint32_t>(63 - __builtin_clzll(inm));
+            if (upm != 0) {
+                const uint32_t kj = mk - (G / 2 - 1) + static_cast<uint32_t>(__builtin_ctzll(upm));
+                R = kj;
+                if (kj > first_in) L = kj - 1;
+                else L = L;  // u may still lie below the window: keep L
+            } else {
+                L = last_in;
+            }
+        }
+    }
+    while (__builtin_amdgcn_ballot_w64(R - L > 1u) != 0) {
         const uint64_t w = R - L;
-        auto key = [&](uint32_t i) { return L + static_cast<uint32_t>((w * i) >> 6); };
-        // lane 0 tests L itself, known to choose the lower code
-        const bool up = lane != 0 && upper_wins(from_key(key(lane)), lo, hi);
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(up);
-        if (mask == 0) {
-            L = key(63);
-        } else {
-            const uint32_t j = static_cast<uint32_t>(__builtin_ctzll(mask));
-            const uint32_t kj = key(j), kp = key(j - 1);
-            R = kj;
-            L = kp;
+        auto key = [&](uint32_t j) { return L + static_cast<uint32_t>((w * j) / G); };
+        // i = 0 tests L itself, known to choose the lower code
+        const bool up = w > 1 && i != 0 && upper_wins(from_key(key(i)), lo, hi);
+        const uint64_t mask = group_bits(__builtin_amdgcn_ballot_w64(up));
+        if (w > 1) {
+            if (mask == 0) {
+                L = key(G - 1);
+            } else {
+                const uint32_t j = static_cast<uint32_t>(__builtin_ctzll(mask));
+                const uint32_t kj = key(j), kp = key(j - 1);
+                R = kj;
+                L = kp;
+            }
         }
     }
     bits = mid_bits(from_key(R), from_key(L));
-    return true;
+    return ok;
+}
+
+// The same with the whole wave on one threshold.
+__device__ inline bool threshold_mid_wave(float lo, float hi, uint64_t& bits) {
+    return threshold_mid_group<64>(lo, hi, bits);
 }
 
 // Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
-// threshold whose window meets the bucket (mid[i] from threshold_mid_wave), the
+// threshold whose window meets the bucket (mid[i] from threshold_mid_group), the
 // plane bytes of the indices below and above it, and with PLANE4 their
 // plane-4 bits in bits 0 and 1 of M.  Returns false if two windows meet
 // the bucket.
