@@ -20,7 +20,7 @@ import numpy as np
 
 __all__ = [
     "KbitError", "lib", "codebook_nf", "codebook_fp4", "codebook_lloyd_max_normal",
-    "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax",
+    "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax", "linear_4bit",
     "quantize_act_fwht_k4_bf16", "n_words", "n_blocks",
 ]
 
@@ -193,6 +193,30 @@ def quantize_nested_absmax(absmax, qmap2, absmax_code=None, absmax2=None, offset
     _check(name, lib().quantize_nested_absmax(_ptr(absmax), nb, _ptr(qmap2), _ptr(absmax_code), _ptr(absmax2),
                                               _ptr(offset), _ptr(workspace), workspace.numel(), _stream(dev)))
     return absmax_code, absmax2, offset
+
+
+def linear_4bit(X, packed, codebook16, N, blocksize, absmax=None, absmax_code=None, qmap2=None, absmax2=None,
+                offset=None, out=None):
+    """out[M, N] = X[M, K] @ W[N, K]^T with W decoded from its 4-bit planes inside
+    the kernel (bf16 in and out).  Scales: fp32 ``absmax``, or the nested state
+    (``absmax_code``, ``qmap2``, ``absmax2``, ``offset``)."""
+    torch = _torch()
+    if X.dtype != torch.bfloat16 or X.dim() != 2:
+        raise TypeError("X must be a 2-D bfloat16 tensor")
+    M, K = X.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    if absmax_code is not None:
+        name = "linear_4bit_nested_bf16"
+        status = lib().linear_4bit_nested_bf16(_ptr(X), M, K, _ptr(packed), _ptr(codebook16), _ptr(absmax_code),
+                                               _ptr(qmap2), _ptr(absmax2), ct.c_float(float(offset)), N,
+                                               blocksize, _ptr(out), _stream(X.device))
+    else:
+        name = "linear_kbit_bf16_k4"
+        status = lib().linear_kbit_bf16_k4(_ptr(X), M, K, _ptr(packed), _ptr(codebook16), _ptr(absmax), N,
+                                           blocksize, _ptr(out), _stream(X.device))
+    _check(name, status)
+    return out
 
 
 def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=None):

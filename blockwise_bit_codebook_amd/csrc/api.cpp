@@ -95,6 +95,20 @@ int do_nested(Dtype t, const uint32_t* packed, const float* codebook16, const ui
         launch_dequantize_nested(t, packed, codebook16, code, qmap2, absmax2, offset, out, n, l2b, stream));
 }
 
+// Shared checks of the linear entry points (K % 32 == 0; packed 16-byte
+// aligned, since each lane reads one group's four plane words at once).
+int check_linear(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed, const float* codebook16,
+                 int32_t N, int32_t blocksize, const uint16_t* out, int& l2b) {
+    l2b = log2_block(blocksize);
+    if (l2b < 0) return KBIT_EBLOCK;
+    if (M < 0 || K <= 0 || N <= 0 || (K % 32) != 0) return KBIT_EINVAL;
+    if (static_cast<int64_t>(N) * K > kMaxElems || M > kMaxElems / K || M > kMaxElems / N) return KBIT_EINVAL;
+    if (M == 0) return KBIT_OK;
+    if (!X || !packed || !codebook16 || !out) return KBIT_EINVAL;
+    if (!aligned(X, 16) || !aligned(packed, 16) || !aligned(codebook16, 4) || !aligned(out, 2)) return KBIT_EALIGN;
+    return 1;  // proceed (the caller checks its scale arguments, then the device)
+}
+
 }  // namespace
 
 constexpr int64_t kMaxNestedBlocks = int64_t(1) << 36;
@@ -196,6 +210,31 @@ int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2, 
     if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
     return kbit::map_launch(
         kbit::launch_nested_encode(absmax, nb, qmap2, absmax_code, absmax2, offset, workspace, stream));
+}
+
+int linear_kbit_bf16_k4(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed, const float* codebook16,
+                        const float* absmax, int32_t N, int32_t blocksize, uint16_t* out, void* stream) {
+    int l2b = 0;
+    const int c = kbit::check_linear(X, M, K, packed, codebook16, N, blocksize, out, l2b);
+    if (c != 1) return c;
+    if (!absmax) return KBIT_EINVAL;
+    if (!kbit::aligned(absmax, 4)) return KBIT_EALIGN;
+    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
+    return kbit::map_launch(kbit::launch_linear4_plain(X, M, K, packed, codebook16, absmax, N, l2b, out, stream));
+}
+
+int linear_4bit_nested_bf16(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed,
+                            const float* codebook16, const uint8_t* absmax_code, const float* qmap2,
+                            const float* absmax2, float offset, int32_t N, int32_t blocksize, uint16_t* out,
+                            void* stream) {
+    int l2b = 0;
+    const int c = kbit::check_linear(X, M, K, packed, codebook16, N, blocksize, out, l2b);
+    if (c != 1) return c;
+    if (!absmax_code || !qmap2 || !absmax2) return KBIT_EINVAL;
+    if (!kbit::aligned(qmap2, 4) || !kbit::aligned(absmax2, 4)) return KBIT_EALIGN;
+    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
+    return kbit::map_launch(kbit::launch_linear4_nested(X, M, K, packed, codebook16, absmax_code, qmap2, absmax2,
+                                                        offset, N, l2b, out, stream));
 }
 
 int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const uint32_t* sign_bits,

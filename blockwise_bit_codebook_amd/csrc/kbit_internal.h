@@ -29,6 +29,13 @@ int64_t nested_workspace_bytes(int64_t nb);
 int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
                          float* offset, void* workspace, void* stream);
 
+int launch_linear4_plain(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* codebook16,
+                         const float* absmax, int N, int log2B, uint16_t* out, void* stream);
+
+int launch_linear4_nested(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* codebook16,
+                          const uint8_t* code, const float* qmap2, const float* absmax2, float offset, int N,
+                          int log2B, uint16_t* out, void* stream);
+
 int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
 

@@ -1,0 +1,164 @@
+// Linear layer over 4-bit blockwise-quantized weights for gfx950, with the
+// weight decode fused into the matrix product: the "dequantize-plus-linear"
+// consumer of [PR2051] Summary (and the performance controls with M = 1, 8,
+// 32 rows, N = 4096 or 11008, K = 4096), without materialising the weights.
+//
+// What is computed (W stored as the K = 4 bit planes of the row-major
+// [N, K] weight, blocks of B along the flattened index):
+//   W[n][k]   = RN_bf16( RN(codebook16[idx(n, k)] * s_b) ),  b = (nK + k) / B
+//               with s_b = absmax[b] (plain) or the nested scale
+//               RN( RN(qmap2[code_b] * absmax2[b / 256]) + offset )
+//               -- exactly the bf16 output of dequantize_kbit_bf16_k4 /
+//               dequantize_4bit_nested_bf16 on the same state;
+//   out[m][n] = RN_bf16( sum over k of X[m][k] * W[n][k] ),
+//               products exact, sums in fp32 (matrix-core order).
+//
+// How: one workgroup per 16 output channels, 8 waves splitting K.  Per step
+// of 32 k a wave decodes its 16 x 32 weight slice straight into the B
+// operand of v_mfma_f32_16x16x32_bf16 (lane l: 8 consecutive k of channel
+// n0 + l % 16, which are one byte of each of the group's 4 plane words), and
+// runs one MFMA per 16 rows of X with that operand (up to 4 row tiles per
+// pass).  The 8 partial tiles are added in LDS in wave order, so the
+// result does not depend on scheduling.  The kernel is bound by reading the
+// packed weights when M is small.
+#include "device.h"
+#include "kbit_internal.h"
+#include "launch.h"
+
+namespace kbit {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLinWaves = 8;                   // K split inside a workgroup
+constexpr int kLinThreads = kLinWaves * kWave;
+constexpr int kTileN = 16;                     // output channels per workgroup
+constexpr int kMaxMt = 4;                      // 16-row tiles of X per pass
+
+struct LinPlain {
+    const float* absmax;
+    __device__ float scale(int64_t b, const float*) const { return absmax[b]; }
+};
+
+struct LinNested {
+    const uint8_t* code;
+    const float* absmax2;
+    float offset;
+    __device__ float scale(int64_t b, const float* qmap_lds) const {
+#pragma clang fp contract(off)
+        const float prod = qmap_lds[code[b]] * absmax2[b >> 8];
+        return prod + offset;
+    }
+};
+
+template <class Scale>
+__global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __restrict__ X, int64_t M, int K,
+                                                              const uint32_t* __restrict__ packed,
+                                                              const float* __restrict__ cb, Scale sc,
+                                                              const float* __restrict__ qmap2, int N, int log2B,
+                                                              uint16_t* __restrict__ out) {
+    __shared__ float2 pair_lds[256];
+    __shared__ float qmap_lds[256];
+    __shared__ float red[kLinWaves][kMaxMt][16][17];
+    {
+        const int t = threadIdx.x;
+        if (t < 256) {
+            pair_lds[t] = make_float2(cb[t & 15], cb[t >> 4]);
+            qmap_lds[t] = qmap2 ? qmap2[t] : 0.0f;
+        }
+    }
+    __syncthreads();
+
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nn = lane & 15, q = lane >> 4;
+    const int n0 = blockIdx.x * kTileN;
+    const int n = n0 + nn;
+    const bool n_ok = n < N;
+    const int T = K / kGroup;  // 32-wide k steps
+    const int s_begin = wave * T / kLinWaves, s_end = (wave + 1) * T / kLinWaves;
+
+    for (int64_t m0 = 0; m0 < M; m0 += 16 * kMaxMt) {
+        f32x4 acc[kMaxMt];
+#pragma unroll
+        for (int mt = 0; mt < kMaxMt; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int s = s_begin; s < s_end; ++s) {
+            const int k0 = s * kGroup;
+            // B operand: w[n][k0 + 8q + i], i = 0..7
+            u32x4 wd = u32x4{0u, 0u, 0u, 0u};
+            float scale = 0.0f;
+            if (n_ok) {
+                wd = load16<false>(packed + (static_cast<int64_t>(n) * T + s) * 4);
+                scale = sc.scale((static_cast<int64_t>(n) * K + k0) >> log2B, qmap_lds);
+            }
+            // byte q of each plane word -> plane bytes of the lane's 8 elements
+            const uint32_t sh = 8u * static_cast<uint32_t>(q);
+            const uint32_t p = ((wd[0] >> sh) & 0xFFu) | (((wd[1] >> sh) & 0xFFu) << 8) |
+                               (((wd[2] >> sh) & 0xFFu) << 16) | (((wd[3] >> sh) & 0xFFu) << 24);
+            const uint32_t nib = planes_to_nibbles(p);
+            u32x4 wv;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float2 c2 = pair_lds[(nib >> (8 * t)) & 0xFFu];
+                wv[t] = pack_bf16x2(c2.x * scale, c2.y * scale);
+            }
+            const bf16x8 bw = __builtin_bit_cast(bf16x8, wv);
+#pragma unroll
+            for (int mt = 0; mt < kMaxMt; ++mt) {
+                const int64_t row = m0 + mt * 16 + nn;
+                if (m0 + mt * 16 < M) {  // wave-uniform
+                    u32x4 xa = u32x4{0u, 0u, 0u, 0u};
+                    if (row < M) xa = load16<false>(X + row * K + k0 + 8 * q);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa), bw, acc[mt],
+                                                                      0, 0, 0);
+                }
+            }
+        }
+        // lane l holds D[4q + i][nn] of each row tile
+#pragma unroll
+        for (int mt = 0; mt < kMaxMt; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][mt][4 * q + i][nn] = acc[mt][i];
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < kMaxMt * 16 * 16; idx += kLinThreads) {
+            const int mt = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
+            const int64_t m = m0 + mt * 16 + r;
+            const int nc = n0 + c;
+            if (m < M && nc < N) {
+                float sum = red[0][mt][r][c];
+#pragma unroll
+                for (int w = 1; w < kLinWaves; ++w) sum += red[w][mt][r][c];
+                float hi = 0.0f;
+                fence_f32(sum, hi);
+                out[m * N + nc] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sum));
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <class Scale>
+int launch_linear4(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* cb, Scale sc,
+                   const float* qmap2, int N, int log2B, uint16_t* out, void* stream) {
+    const int grid = (N + kTileN - 1) / kTileN;
+    hipLaunchKernelGGL(linear4_kernel<Scale>, dim3(static_cast<unsigned>(grid)), dim3(kLinThreads), 0,
+                       static_cast<hipStream_t>(stream), X, M, K, packed, cb, sc, qmap2, N, log2B, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_linear4_plain(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* codebook16,
+                         const float* absmax, int N, int log2B, uint16_t* out, void* stream) {
+    return launch_linear4(X, M, K, packed, codebook16, LinPlain{absmax}, nullptr, N, log2B, out, stream);
+}
+
+int launch_linear4_nested(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* codebook16,
+                          const uint8_t* code, const float* qmap2, const float* absmax2, float offset, int N,
+                          int log2B, uint16_t* out, void* stream) {
+    return launch_linear4(X, M, K, packed, codebook16, LinNested{code, absmax2, offset}, qmap2, N, log2B, out,
+                          stream);
+}
+
+}  // namespace kbit

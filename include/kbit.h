@@ -207,6 +207,33 @@ KBIT_DECLARE_NESTED(fp16, uint16_t)
 KBIT_DECLARE_NESTED(bf16, uint16_t)
 
 /* ------------------------------------------------------------------------
+ * Linear layer over 4-bit quantized weights, decode fused into the product
+ * ([PR2051] Summary: the dequantize-plus-linear consumer; its controls use
+ * M = 1, 8, 32 rows, N = 4096 or 11008, K = 4096).  W is the row-major
+ * [N, K] weight stored as quantize_kbit_*_k4 stores it (K = 4 bit planes of
+ * the flattened W, blocks of `blocksize` along the flattened index):
+ *   W[n][k]   = exactly the bf16 output of dequantize_kbit_bf16_k4 (plain
+ *               fp32 absmax) or dequantize_4bit_nested_bf16 (nested state)
+ *               on the same state, element n*K + k;
+ *   out[m][n] = RN_bf16( sum over k of X[m][k] * W[n][k] ): exact products,
+ *               fp32 sums in an unspecified order, so the result is within
+ *               (K + 8) * 2^-24 * sum |X[m][k] * W[n][k]| of the exact sum
+ *               before the final rounding.
+ * X      : device, M x K bf16 (row-major, 16-byte aligned).
+ * packed : device, N*K/32*4 uint32 (16-byte aligned).
+ * out    : device, M x N bf16 (row-major, output).
+ * K must be a positive multiple of 32, N positive; M == 0 is a no-op.  The
+ * kernel is tuned for small M (it re-reads the weights every 64 rows of X).
+ * --------------------------------------------------------------------- */
+int linear_kbit_bf16_k4(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed,
+                        const float* codebook16, const float* absmax, int32_t N, int32_t blocksize,
+                        uint16_t* out, void* stream);
+int linear_4bit_nested_bf16(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed,
+                            const float* codebook16, const uint8_t* absmax_code, const float* qmap2,
+                            const float* absmax2, float offset, int32_t N, int32_t blocksize,
+                            uint16_t* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Nested-state encoder: the input of dequantize_4bit_nested from the fp32
  * per-block absmax.  [PR2051] Summary describes the state (8-bit codes per
  * block over groups of 256, a group absmax and a mean offset) but not its

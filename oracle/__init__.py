@@ -35,4 +35,4 @@ import numpy as _np
 # Flush-to-zero on the host would silently change subnormal results.
 assert _np.float32(1e-45) > 0, "host FPU flushes subnormals; oracle invalid"
 
-from . import numerics, codebooks, kbit, nested, act, e4m4  # noqa: E402,F401
+from . import numerics, codebooks, kbit, nested, act, e4m4, linear  # noqa: E402,F401

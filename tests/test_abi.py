@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 1, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 2 + 1, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -124,6 +124,16 @@ def test_validation_codes_before_any_device_access():
     assert ne(_A16, 1000, _A16, _A16, _A16, _A16, ct.c_void_p(0x40004), wsb, None) == -3
     assert ne(_A16, 1000, _A16, None, _A16, _A16, _W8, wsb, None) == -1
     assert ne(_A16, 1000, ct.c_void_p(0x20002), _A16, _A16, _A16, _W8, wsb, None) == -3
+    li = lib.linear_kbit_bf16_k4
+    assert li(_A16, 4, 48, _A16, _A16, _A16, 64, 64, _A16, None) == -1            # K not a multiple of 32
+    assert li(_A16, 4, 64, _A16, _A16, _A16, 0, 64, _A16, None) == -1             # N = 0
+    assert li(_A16, 4, 64, _A16, _A16, _A16, 64, 96, _A16, None) == -2            # blocksize
+    assert li(None, 0, 64, None, None, None, 64, 64, None, None) == 0              # M = 0: no-op
+    assert li(_A16, 4, 64, _A4, _A16, _A16, 64, 64, _A16, None) == -3             # packed not 16-byte aligned
+    assert li(_A16, 4, 64, _A16, _A16, None, 64, 64, _A16, None) == -1            # no absmax
+    ln = lib.linear_4bit_nested_bf16
+    assert ln(_A16, 4, 64, _A16, _A16, None, _A16, _A16, ct.c_float(0), 64, 64, _A16, None) == -1
+    assert ln(_A4, 4, 64, _A16, _A16, _A16, _A16, _A16, ct.c_float(0), 64, 64, _A16, None) == -3
     act = lib.quantize_act_fwht_k4_bf16
     assert act(_A16, 4, 2048, _A16, _A16, _A16, _A16, None) == -1  # d must be 4096
     assert act(_A16, 0, 4096, None, None, None, None, None) == 0

@@ -1,0 +1,61 @@
+"""Pins for the linear-layer reference."""
+
+from fractions import Fraction
+
+import numpy as np
+
+from oracle import codebooks, kbit, linear, numerics
+from blockwise_bit_codebook_amd import synth
+from tests import exact
+
+
+def test_reference_equals_exact_rational_sums():
+    rng = np.random.default_rng(4)
+    M, N, K = 3, 5, 96
+    xb = numerics.to_bf16_bits(rng.normal(0, 1, (M, K)).astype(np.float32))
+    wb = numerics.to_bf16_bits(rng.normal(0, 0.05, (N, K)).astype(np.float32))
+    ref, absum = linear.reference(xb, wb)
+    xf = numerics.widen(xb, "bf16")
+    wf = numerics.widen(wb, "bf16")
+    for m in range(M):
+        for n in range(N):
+            s = sum(exact.frac(xf[m, k]) * exact.frac(wf[n, k]) for k in range(K))
+            a = sum(abs(exact.frac(xf[m, k]) * exact.frac(wf[n, k])) for k in range(K))
+            assert abs(Fraction(ref[m, n]) - s) <= K * Fraction(2) ** -53 * a
+            assert Fraction(absum[m, n]) == a or abs(Fraction(absum[m, n]) - a) <= K * Fraction(2) ** -53 * a
+
+
+def test_bound_holds_for_worst_order_fp32_sums():
+    # sequential fp32 sums in ascending and descending magnitude order and a
+    # split into 8 partial sums all stay inside the bound
+    rng = np.random.default_rng(6)
+    K = 4096
+    p = (rng.normal(0, 1, K) * np.exp2(rng.integers(-20, 20, K))).astype(np.float32)
+    exact_sum = sum(exact.frac(v) for v in p)
+    bound = linear.tolerance(float(np.sum(np.abs(p.astype(np.float64)))), K)
+    for order in (np.argsort(np.abs(p)), np.argsort(-np.abs(p)), np.arange(K)):
+        s = np.float32(0)
+        for v in p[order]:
+            s = np.float32(s + v)
+        assert abs(float(Fraction(float(s)) - exact_sum)) <= bound
+    parts = [np.float32(0)] * 8
+    for i, v in enumerate(p):
+        parts[i * 8 // K] = np.float32(parts[i * 8 // K] + v)
+    s = parts[0]
+    for v in parts[1:]:
+        s = np.float32(s + v)
+    assert abs(float(Fraction(float(s)) - exact_sum)) <= bound
+
+
+def test_weights_are_the_dequantized_state():
+    N, K, B = 8, 128, 64
+    w = synth.weight(N, K, "fp32", seed=2)
+    cb = codebooks.nf(4)
+    words, absmax = kbit.quantize_packed(w, cb, 4, B)
+    wb = linear.weights_bf16(words, cb, N, K, B, absmax=absmax)
+    idx = kbit.unpack(words, 4, N * K)
+    # element (n, k) is block (nK + k) // B of the flattened tensor
+    for n, k in ((0, 0), (3, 65), (7, 127)):
+        e = n * K + k
+        v = np.float32(cb[idx[e]] * absmax[e // B])
+        assert wb[n, k] == numerics.to_bf16_bits(np.float32([v]))[0]
