@@ -340,6 +340,79 @@ def bench_act(torch, kb, synth, dev, reps, sets=12):
             "rows_per_s": round(ACT_ROWS / (avg * 1e-3), 1)}
 
 
+# The page's dequantize-plus-linear controls (M, N, K) and their candidate
+# medians on the page's GPU (context only, another machine).
+LINEAR_SHAPES = [(1, 4096, 4096, 26.735), (8, 4096, 4096, 24.748), (32, 4096, 4096, 24.752),
+                 (32, 11008, 4096, 61.726)]
+
+
+def linear_bytes(M, N, K):
+    """Minimum bytes of one fused linear call with a nested state (B = 64):
+    packed weights, codes, group absmax, map and codebook, X and out."""
+    nb = N * K // BLOCK
+    return N * K // 2 + nb + 4 * (-(-nb // GROUP2)) + 4 * 256 + 64 + 2 * M * K + 2 * M * N
+
+
+def bench_linear(torch, kb, synth, dev, reps=20):
+    """Fused 4-bit linear (nested state) at the page's shapes.  Each timed
+    call uses a different weight set (rotated through > 400 MB, beyond the
+    last-level cache); the launches are captured in a HIP graph so that
+    Python's launch cost is not timed.  The warm figure reuses one set."""
+    cb = torch.from_numpy(kb.codebook_nf(K)).to(dev)
+    q = torch.from_numpy(kb.dynamic_map8()).to(dev)
+    res = []
+    for M, N, Kd, page_us in LINEAR_SHAPES:
+        nb = N * Kd // BLOCK
+        nbytes = linear_bytes(M, N, Kd)
+        sets = int(min(64, max(2, -(-(400 << 20) // nbytes))))
+        g = torch.Generator(device="cpu").manual_seed(M * 131 + N)
+        w0 = torch.randint(-2 ** 31, 2 ** 31 - 1, (N * Kd // 8,), dtype=torch.int32, generator=g).to(dev)
+        code_np, a2_np, off = synth.nested_state_synthetic(nb, seed=M + 5)
+        code0 = torch.from_numpy(code_np).to(dev)
+        a20 = torch.from_numpy(a2_np).to(dev)
+        X = torch.from_numpy(synth.normal(M * Kd, seed=M, dtype="bf16").view(np.int16)).to(dev).view(
+            torch.bfloat16).reshape(M, Kd)
+        bufs = [(w0 if i == 0 else w0.clone(), code0 if i == 0 else code0.clone(), a20 if i == 0 else a20.clone(),
+                 torch.empty((M, N), dtype=torch.bfloat16, device=dev)) for i in range(sets)]
+        torch.cuda.synchronize()
+
+        def call(b):
+            kb.linear_4bit(X, b[0], cb, N, BLOCK, absmax_code=b[1], qmap2=q, absmax2=b[2], offset=off, out=b[3])
+
+        for b in bufs:
+            call(b)
+        torch.cuda.synchronize()
+
+        def timed(items):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                for b in items:
+                    call(b)
+            gr.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / (reps * len(items))
+
+        us = timed(bufs)
+        warm = timed([bufs[0]] * sets)
+        res.append({"M": M, "N": N, "K": Kd, "avg_us": round(us, 3), "warm_avg_us": round(warm, 3),
+                    "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "TFLOP/s": round(2.0 * M * N * Kd / (us * 1e-6) / 1e12, 3),
+                    "weight_sets": sets, "page_candidate_us": page_us})
+        del bufs
+        torch.cuda.empty_cache()
+    return {"workload": "linear_4bit_nested_bf16: bf16 X [M, K] x NF4 weights [N, K] with a nested state, B=64, "
+                        "graph-replayed launches over rotated weight sets",
+            "shapes": res,
+            "note": "page_candidate_us: the page's fused dequantize + linear medians on its own GPU, context only"}
+
+
 def main(argv=None):
     args = parse(argv)
     if args.summarize:
@@ -506,7 +579,7 @@ def main(argv=None):
 
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
-    fp4 = warm = act = None
+    fp4 = warm = act = lin = None
     if not args.headline_only:
         pair = {"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only}
         cb_nf = cb
@@ -521,6 +594,7 @@ def main(argv=None):
                 "note": "same buffer set every launch (warm cache); not the headline number"}
         if not args.no_act:
             act = bench_act(torch, kb, synth, dev, reps)
+        lin = bench_linear(torch, kb, synth, dev)
 
     dom_name, dom = ("quantize_kbit_bf16_k4", kq) if kq["avg_us"] >= kn["avg_us"] else \
         ("dequantize_4bit_nested_bf16", kn)
@@ -571,6 +645,7 @@ def main(argv=None):
         "fp4_codebook": fp4,
         "warm": warm,
         "act_fwht": act,
+        "linear_4bit": lin,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -13,12 +13,13 @@
 //   out[m][n] = RN_bf16( sum over k of X[m][k] * W[n][k] ),
 //               products exact, sums in fp32 (matrix-core order).
 //
-// How: one workgroup per 16 output channels, 8 waves splitting K.  Per step
-// of 32 k a wave decodes its 16 x 32 weight slice straight into the B
+// How: one workgroup per 16 output channels, 16 waves splitting K.  Per
+// step of 32 k a wave decodes its 16 x 32 weight slice straight into the B
 // operand of v_mfma_f32_16x16x32_bf16 (lane l: 8 consecutive k of channel
 // n0 + l % 16, which are one byte of each of the group's 4 plane words), and
-// runs one MFMA per 16 rows of X with that operand (up to 4 row tiles per
-// pass).  The 8 partial tiles are added in LDS in wave order, so the
+// runs one MFMA per 16 rows of X with that operand (1, 2 or 4 row tiles per
+// pass, from M).  The loads of four steps are issued together, and the
+// next four steps' loads go out before the current ones are decoded.  The 16 partial tiles are added in LDS in wave order, so the
 // result does not depend on scheduling.  The kernel is bound by reading the
 // packed weights when M is small.
 #include "device.h"
@@ -31,44 +32,63 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kLinWaves = 8;                   // K split inside a workgroup
+constexpr int kLinWaves = 16;                  // K split inside a workgroup
 constexpr int kLinThreads = kLinWaves * kWave;
 constexpr int kTileN = 16;                     // output channels per workgroup
-constexpr int kMaxMt = 4;                      // 16-row tiles of X per pass
 
+// Block scales in two steps so that their loads can be issued ahead:
+// load() fetches what block b's scale is built from, finish() builds it.
 struct LinPlain {
     const float* absmax;
-    __device__ float scale(int64_t b, const float*) const { return absmax[b]; }
+    struct Raw {
+        float a;
+    };
+    __device__ Raw load(int64_t b) const { return Raw{absmax[b]}; }
+    __device__ float finish(const Raw& r, const float*) const { return r.a; }
 };
 
 struct LinNested {
     const uint8_t* code;
     const float* absmax2;
     float offset;
-    __device__ float scale(int64_t b, const float* qmap_lds) const {
+    struct Raw {
+        uint32_t code;
+        float a2;
+    };
+    __device__ Raw load(int64_t b) const { return Raw{code[b], absmax2[b >> 8]}; }
+    __device__ float finish(const Raw& r, const float* qmap_lds) const {
 #pragma clang fp contract(off)
-        const float prod = qmap_lds[code[b]] * absmax2[b >> 8];
+        const float prod = qmap_lds[r.code] * r.a2;
         return prod + offset;
     }
 };
 
-template <class Scale>
+// The loads of one chunk of kU = 4 consecutive k steps: the 4 plane words of
+// each step's group, the raw scale of step s + q of channel nn (lane (nn,
+// q); the lanes take each step's scale from there), and, for a single row
+// tile, the step's 8 values of X.
+constexpr int kU = 4;
+template <class Scale, bool XAHEAD>
+struct Chunk {
+    u32x4 wd[kU];
+    typename Scale::Raw raw;
+    u32x4 xa[XAHEAD ? kU : 1];
+};
+
+// MT: 16-row tiles of X per pass.  Chunks are double-buffered: the next
+// chunk's loads are issued before the current one is decoded, and the
+// first chunk's before the prologue's barrier.
+template <class Scale, int MT>
 __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __restrict__ X, int64_t M, int K,
                                                               const uint32_t* __restrict__ packed,
                                                               const float* __restrict__ cb, Scale sc,
                                                               const float* __restrict__ qmap2, int N, int log2B,
                                                               uint16_t* __restrict__ out) {
+    constexpr bool kXAhead = MT == 1;
+    using C = Chunk<Scale, kXAhead>;
     __shared__ float2 pair_lds[256];
     __shared__ float qmap_lds[256];
-    __shared__ float red[kLinWaves][kMaxMt][16][17];
-    {
-        const int t = threadIdx.x;
-        if (t < 256) {
-            pair_lds[t] = make_float2(cb[t & 15], cb[t >> 4]);
-            qmap_lds[t] = qmap2 ? qmap2[t] : 0.0f;
-        }
-    }
-    __syncthreads();
+    __shared__ float red[kLinWaves][MT][16][17];
 
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -78,50 +98,90 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
     const bool n_ok = n < N;
     const int T = K / kGroup;  // 32-wide k steps
     const int s_begin = wave * T / kLinWaves, s_end = (wave + 1) * T / kLinWaves;
+    const uint32_t sh = 8u * static_cast<uint32_t>(q);
 
-    for (int64_t m0 = 0; m0 < M; m0 += 16 * kMaxMt) {
-        f32x4 acc[kMaxMt];
+    auto load_chunk = [&](int s, int64_t m0, C& c) {
+        c.raw = typename Scale::Raw{};
+        if (n_ok && s + q < s_end) c.raw = sc.load((static_cast<int64_t>(n) * K + (s + q) * kGroup) >> log2B);
 #pragma unroll
-        for (int mt = 0; mt < kMaxMt; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int s = s_begin; s < s_end; ++s) {
-            const int k0 = s * kGroup;
-            // B operand: w[n][k0 + 8q + i], i = 0..7
-            u32x4 wd = u32x4{0u, 0u, 0u, 0u};
-            float scale = 0.0f;
-            if (n_ok) {
-                wd = load16<false>(packed + (static_cast<int64_t>(n) * T + s) * 4);
-                scale = sc.scale((static_cast<int64_t>(n) * K + k0) >> log2B, qmap_lds);
+        for (int u = 0; u < kU; ++u) {
+            const int step = s + u;
+            const bool live = step < s_end;  // wave-uniform
+            c.wd[u] = u32x4{0u, 0u, 0u, 0u};
+            if (live && n_ok) c.wd[u] = load16<false>(packed + (static_cast<int64_t>(n) * T + step) * 4);
+            if constexpr (kXAhead) {
+                const int64_t row = m0 + nn;
+                c.xa[u] = u32x4{0u, 0u, 0u, 0u};
+                if (live && row < M) c.xa[u] = load16<false>(X + row * K + step * kGroup + 8 * q);
             }
-            // byte q of each plane word -> plane bytes of the lane's 8 elements
-            const uint32_t sh = 8u * static_cast<uint32_t>(q);
-            const uint32_t p = ((wd[0] >> sh) & 0xFFu) | (((wd[1] >> sh) & 0xFFu) << 8) |
-                               (((wd[2] >> sh) & 0xFFu) << 16) | (((wd[3] >> sh) & 0xFFu) << 24);
-            const uint32_t nib = planes_to_nibbles(p);
-            u32x4 wv;
+        }
+    };
+
+    C ca, cb2;
+    if (s_begin < s_end) load_chunk(s_begin, 0, ca);
+    {
+        const int t = threadIdx.x;
+        if (t < 256) {
+            pair_lds[t] = make_float2(cb[t & 15], cb[t >> 4]);
+            qmap_lds[t] = qmap2 ? qmap2[t] : 0.0f;
+        }
+    }
+    __syncthreads();
+
+    for (int64_t m0 = 0; m0 < M; m0 += 16 * MT) {
+        f32x4 acc[MT];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float2 c2 = pair_lds[(nib >> (8 * t)) & 0xFFu];
-                wv[t] = pack_bf16x2(c2.x * scale, c2.y * scale);
-            }
-            const bf16x8 bw = __builtin_bit_cast(bf16x8, wv);
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (m0 > 0 && s_begin < s_end) load_chunk(s_begin, m0, ca);
+
+        auto compute = [&](int s, const C& c) {
+            const float my_scale = n_ok ? sc.finish(c.raw, qmap_lds) : 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < kMaxMt; ++mt) {
-                const int64_t row = m0 + mt * 16 + nn;
-                if (m0 + mt * 16 < M) {  // wave-uniform
-                    u32x4 xa = u32x4{0u, 0u, 0u, 0u};
-                    if (row < M) xa = load16<false>(X + row * K + k0 + 8 * q);
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa), bw, acc[mt],
-                                                                      0, 0, 0);
+            for (int u = 0; u < kU; ++u) {
+                if (s + u >= s_end) break;  // wave-uniform
+                // byte q of each plane word -> plane bytes of the lane's 8 k
+                const uint32_t p = ((c.wd[u][0] >> sh) & 0xFFu) | (((c.wd[u][1] >> sh) & 0xFFu) << 8) |
+                                   (((c.wd[u][2] >> sh) & 0xFFu) << 16) | (((c.wd[u][3] >> sh) & 0xFFu) << 24);
+                const uint32_t nib = planes_to_nibbles(p);
+                const float scale = __shfl(my_scale, u * 16 + nn);
+                u32x4 wv;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float2 c2 = pair_lds[(nib >> (8 * t)) & 0xFFu];
+                    wv[t] = pack_bf16x2(c2.x * scale, c2.y * scale);
+                }
+                const bf16x8 bw = __builtin_bit_cast(bf16x8, wv);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    if (m0 + mt * 16 < M) {  // wave-uniform
+                        u32x4 x;
+                        if constexpr (kXAhead) {
+                            x = c.xa[u];
+                        } else {
+                            const int64_t row = m0 + mt * 16 + nn;
+                            x = u32x4{0u, 0u, 0u, 0u};
+                            if (row < M) x = load16<false>(X + row * K + (s + u) * kGroup + 8 * q);
+                        }
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), bw, acc[mt],
+                                                                          0, 0, 0);
+                    }
                 }
             }
+        };
+        for (int s = s_begin; s < s_end; s += 2 * kU) {
+            if (s + kU < s_end) load_chunk(s + kU, m0, cb2);
+            compute(s, ca);
+            if (s + kU >= s_end) break;
+            if (s + 2 * kU < s_end) load_chunk(s + 2 * kU, m0, ca);
+            compute(s + kU, cb2);
         }
         // lane l holds D[4q + i][nn] of each row tile
 #pragma unroll
-        for (int mt = 0; mt < kMaxMt; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) red[wave][mt][4 * q + i][nn] = acc[mt][i];
         __syncthreads();
-        for (int idx = threadIdx.x; idx < kMaxMt * 16 * 16; idx += kLinThreads) {
+        for (int idx = threadIdx.x; idx < MT * 16 * 16; idx += kLinThreads) {
             const int mt = idx >> 8, r = (idx >> 4) & 15, c = idx & 15;
             const int64_t m = m0 + mt * 16 + r;
             const int nc = n0 + c;
@@ -138,13 +198,23 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
     }
 }
 
+template <class Scale, int MT>
+int launch_mt(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* cb, Scale sc,
+              const float* qmap2, int N, int log2B, uint16_t* out, void* stream) {
+    const int grid = (N + kTileN - 1) / kTileN;
+    hipLaunchKernelGGL((linear4_kernel<Scale, MT>), dim3(static_cast<unsigned>(grid)), dim3(kLinThreads), 0,
+                       static_cast<hipStream_t>(stream), X, M, K, packed, cb, sc, qmap2, N, log2B, out);
+    return static_cast<int>(hipGetLastError());
+}
+
+// Row tiles per pass from M: fewer tiles keep registers (and LDS) low for
+// the small-M case the kernel is meant for.
 template <class Scale>
 int launch_linear4(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* cb, Scale sc,
                    const float* qmap2, int N, int log2B, uint16_t* out, void* stream) {
-    const int grid = (N + kTileN - 1) / kTileN;
-    hipLaunchKernelGGL(linear4_kernel<Scale>, dim3(static_cast<unsigned>(grid)), dim3(kLinThreads), 0,
-                       static_cast<hipStream_t>(stream), X, M, K, packed, cb, sc, qmap2, N, log2B, out);
-    return static_cast<int>(hipGetLastError());
+    if (M <= 16) return launch_mt<Scale, 1>(X, M, K, packed, cb, sc, qmap2, N, log2B, out, stream);
+    if (M <= 32) return launch_mt<Scale, 2>(X, M, K, packed, cb, sc, qmap2, N, log2B, out, stream);
+    return launch_mt<Scale, 4>(X, M, K, packed, cb, sc, qmap2, N, log2B, out, stream);
 }
 
 }  // namespace

@@ -217,7 +217,7 @@ KBIT_DECLARE_NESTED(bf16, uint16_t)
  *               on the same state, element n*K + k;
  *   out[m][n] = RN_bf16( sum over k of X[m][k] * W[n][k] ): exact products,
  *               fp32 sums in an unspecified order, so the result is within
- *               (K + 8) * 2^-24 * sum |X[m][k] * W[n][k]| of the exact sum
+ *               (K + 16) * 2^-24 * sum |X[m][k] * W[n][k]| of the exact sum
  *               before the final rounding.
  * X      : device, M x K bf16 (row-major, 16-byte aligned).
  * packed : device, N*K/32*4 uint32 (16-byte aligned).

@@ -12,8 +12,8 @@ order):
   computed in float64 (each bf16 x bf16 product is exact there; the float64
   sum of K terms differs from the exact sum by at most K * 2^-53 * sum|p|);
 * a kernel that adds in fp32 in any order is within
-  (K + 8) * 2^-24 * sum_k |X[m][k] * W[n][k]| of the exact sum (K - 1
-  additions along k plus the 8-way split added at the end), and rounding
+  (K + 16) * 2^-24 * sum_k |X[m][k] * W[n][k]| of the exact sum (K - 1
+  additions along k plus the 16-way split added at the end), and rounding
   that to bf16 adds at most 2^-8 of the value.
 
 Parity: pinned in ``tests/test_oracle_linear.py`` (reference against exact
@@ -44,6 +44,6 @@ def reference(x_bits, w_bits):
 
 
 def tolerance(abs_sum, K):
-    """Largest distance of an fp32 sum (any order, K terms plus an 8-way
+    """Largest distance of an fp32 sum (any order, K terms plus a 16-way
     split) from the exact sum, before the output rounding."""
-    return (K + 8) * 2.0 ** -24 * abs_sum
+    return (K + 16) * 2.0 ** -24 * abs_sum

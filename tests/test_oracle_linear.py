@@ -27,7 +27,7 @@ def test_reference_equals_exact_rational_sums():
 
 def test_bound_holds_for_worst_order_fp32_sums():
     # sequential fp32 sums in ascending and descending magnitude order and a
-    # split into 8 partial sums all stay inside the bound
+    # split into 16 partial sums all stay inside the bound
     rng = np.random.default_rng(6)
     K = 4096
     p = (rng.normal(0, 1, K) * np.exp2(rng.integers(-20, 20, K))).astype(np.float32)
@@ -38,9 +38,9 @@ def test_bound_holds_for_worst_order_fp32_sums():
         for v in p[order]:
             s = np.float32(s + v)
         assert abs(float(Fraction(float(s)) - exact_sum)) <= bound
-    parts = [np.float32(0)] * 8
+    parts = [np.float32(0)] * 16
     for i, v in enumerate(p):
-        parts[i * 8 // K] = np.float32(parts[i * 8 // K] + v)
+        parts[i * 16 // K] = np.float32(parts[i * 16 // K] + v)
     s = parts[0]
     for v in parts[1:]:
         s = np.float32(s + v)
