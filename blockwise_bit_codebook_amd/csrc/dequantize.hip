@@ -17,9 +17,10 @@
 // How: a lane owns 8 consecutive elements of one 32-element group.  Lane l
 // of each quad loads plane word l of its group (K = 4: one coalesced dword
 // per lane), a byte transpose inside the quad gives every lane the K plane
-// bytes of its own 8 elements, and four index-bit swaps turn those into
-// eight 4-bit indices.  Pairs of indices address a 256-entry table of code
-// pairs in LDS (one 8-byte read per two outputs).  Each lane multiplies by
+// bytes of its own 8 elements, and two index-bit swaps turn those into four
+// bytes, each holding the plane bits of two neighbouring elements.  Such a
+// byte addresses a 256-entry table of code pairs in LDS (one 8-byte read per
+// two outputs).  Each lane multiplies by
 // its block scale, narrows with the packed RNE converts and writes 16 bytes
 // (bf16/fp16) or 32 bytes (fp32).  K = 5 adds a fifth plane byte and looks
 // codes up one by one.
@@ -103,17 +104,18 @@ __device__ __forceinline__ void decode_tile(const TileIn<K, Scale>& in, const Sc
                                             int64_t tile, int64_t n, int lane) {
     const int64_t e0 = tile * kWaveTile + static_cast<int64_t>(lane) * kElemsPerLane;
     const uint32_t p = quad_transpose_bytes(in.w, lane);
-    const uint32_t nib = planes_to_nibbles(p);
     const float s = scale.finish(in.sc);
     float v[kElemsPerLane];
     if constexpr (K <= 4) {
+        const uint32_t pr = planes_to_pairs(p);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float2 c2 = pair_lds[(nib >> (8 * t)) & 0xFFu];
+            const float2 c2 = pair_lds[(pr >> (8 * t)) & 0xFFu];
             v[2 * t] = c2.x * s;
             v[2 * t + 1] = c2.y * s;
         }
     } else {
+        const uint32_t nib = planes_to_nibbles(p);
         const uint32_t p4 = (dpp_u32<kDppQuadBcast0>(in.w4) >> (8 * (lane & 3))) & 0xFFu;
 #pragma unroll
         for (int t = 0; t < kElemsPerLane; ++t) {
@@ -175,9 +177,8 @@ __device__ __forceinline__ void stage_codebook(const float* __restrict__ cb, flo
     const int tid = threadIdx.x;
     if (tid < C) cb_lds[tid] = cb[tid];
     if constexpr (K <= 4) {
-        // pair index = i0 | i1 << 4 with 4-bit fields; fields >= 2^K never occur
-        const int i0 = tid & 15, i1 = tid >> 4;
-        pair_lds[tid] = make_float2(cb[i0 & (C - 1)], cb[i1 & (C - 1)]);
+        // a pair byte (planes_to_pairs); indices >= 2^K never occur
+        pair_lds[tid] = make_float2(cb[pair_index(tid, 0) & (C - 1)], cb[pair_index(tid, 1) & (C - 1)]);
     }
 }
 

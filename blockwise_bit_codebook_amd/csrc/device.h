@@ -93,6 +93,24 @@ __device__ __forceinline__ uint32_t planes_to_nibbles(uint32_t p) {
     return p;
 }
 
+// Plane bytes -> pair bytes: input byte j bit s (plane j of element s)
+// becomes bit 8*(s/2) + 2*j + (s%2), i.e. byte t holds the four plane bits
+// of elements 2t and 2t+1 interleaved (the index bits (j1 j0 s2 s1 s0) go
+// to (s2 s1 j1 j0 s0): the first two swaps of planes_to_nibbles).  A table
+// of code pairs indexed by such a byte replaces the last two swaps.
+__device__ __forceinline__ uint32_t planes_to_pairs(uint32_t p) {
+    p = delta_swap(p, 0x0000F0F0u, 12);
+    p = delta_swap(p, 0x00CC00CCu, 6);
+    return p;
+}
+
+// The 4-bit index held in the even (s0 = 0) or odd (s0 = 1) bits of a pair
+// byte.
+__host__ __device__ __forceinline__ int pair_index(int b, int s0) {
+    b >>= s0;
+    return (b & 1) | ((b >> 1) & 2) | ((b >> 2) & 4) | ((b >> 3) & 8);
+}
+
 // ---------------------------------------------------------------------------
 // Element types.  Each trait loads the 8 consecutive elements of one lane
 // (16 bytes for 16-bit types, 32 bytes for fp32) widened exactly to float,

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
     {
         const int t = threadIdx.x;
         if (t < 256) {
-            pair_lds[t] = make_float2(cb[t & 15], cb[t >> 4]);
+            pair_lds[t] = make_float2(cb[pair_index(t, 0)], cb[pair_index(t, 1)]);
             qmap_lds[t] = qmap2 ? qmap2[t] : 0.0f;
         }
     }
@@ -142,12 +142,12 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
                 // byte q of each plane word -> plane bytes of the lane's 8 k
                 const uint32_t p = ((c.wd[u][0] >> sh) & 0xFFu) | (((c.wd[u][1] >> sh) & 0xFFu) << 8) |
                                    (((c.wd[u][2] >> sh) & 0xFFu) << 16) | (((c.wd[u][3] >> sh) & 0xFFu) << 24);
-                const uint32_t nib = planes_to_nibbles(p);
+                const uint32_t pr = planes_to_pairs(p);
                 const float scale = __shfl(my_scale, u * 16 + nn);
                 u32x4 wv;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const float2 c2 = pair_lds[(nib >> (8 * t)) & 0xFFu];
+                    const float2 c2 = pair_lds[(pr >> (8 * t)) & 0xFFu];
                     wv[t] = pack_bf16x2(c2.x * scale, c2.y * scale);
                 }
                 const bf16x8 bw = __builtin_bit_cast(bf16x8, wv);
