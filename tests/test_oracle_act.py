@@ -89,3 +89,153 @@ def test_assign_exact_rule_against_exact_scalar_search():
         for j in range(d):
             zn = exact.f32(exact.frac(u[r, j]) / exact.frac(den))
             assert idx[r, j] == exact.nearest_first(zn, cb)
+
+
+# ---- block Hadamard (h = largest power of two dividing d) and permutation ----
+
+def test_hadamard_block_audit_examples():
+    # methodology audit: the rule gives h = 256 for d = 3840 and d = 8960;
+    # CARD.md: d = 12288 is a blocked case with h = 4096
+    assert act.hadamard_block(3840) == 256
+    assert act.hadamard_block(8960) == 256
+    assert act.hadamard_block(12288) == 4096
+    assert act.hadamard_block(4096) == 4096
+    assert act.hadamard_block(96) == 32
+    with pytest.raises(ValueError):
+        act.hadamard_block(0)
+
+
+@pytest.mark.parametrize("d", [96, 768, 1536])
+def test_block_fwht_matches_dense_block_diagonal(d):
+    from scipy.linalg import block_diag
+    h = act.hadamard_block(d)
+    rng = np.random.default_rng(d)
+    u = rng.standard_normal((3, d)).astype(np.float32)
+    got = act.fwht_rows(u, h).astype(np.float64)
+    H = block_diag(*([hadamard(h).astype(np.float64)] * (d // h)))
+    want = u.astype(np.float64) @ H.T
+    scale = np.sqrt(h) * np.max(np.abs(u))
+    assert np.max(np.abs(got - want)) <= 1e-5 * scale
+
+
+def test_block_fwht_large_blocks_per_block_product():
+    d, h = 12288, 4096
+    u = np.random.default_rng(5).standard_normal((2, d)).astype(np.float32)
+    got = act.fwht_rows(u, h).astype(np.float64).reshape(2, 3, h)
+    want = u.astype(np.float64).reshape(2, 3, h) @ hadamard(h).T.astype(np.float64)
+    assert np.max(np.abs(got - want)) <= 1e-5 * np.sqrt(h) * np.max(np.abs(u))
+
+
+def test_block_fwht_keeps_blocks_apart():
+    # energy moves only inside a block: a unit vector in block 1 transforms
+    # to +-1 entries over block 1 and zeros elsewhere
+    d, h = 768, 256
+    u = np.zeros((1, d), np.float32)
+    u[0, h + 7] = 1.0
+    got = act.fwht_rows(u, h)[0]
+    assert np.all(got[:h] == 0) and np.all(got[2 * h:] == 0)
+    assert np.all(np.abs(got[h:2 * h]) == 1.0)
+    # per-block involution and Parseval
+    v = np.random.default_rng(6).standard_normal((2, d)).astype(np.float32)
+    hv = act.fwht_rows(v, h)
+    assert np.allclose(act.fwht_rows(hv, h), h * v, rtol=1e-5, atol=1e-3)
+    e1 = np.sum(hv.astype(np.float64).reshape(2, 3, h) ** 2, axis=2)
+    e0 = h * np.sum(v.astype(np.float64).reshape(2, 3, h) ** 2, axis=2)
+    assert np.allclose(e1, e0, rtol=1e-5)
+
+
+def test_token_sum_blocks_against_fsum():
+    x, _ = synth.activations_bf16(tokens=4, d=3840, seed=8)
+    q = numerics.widen(x, "bf16").reshape(4, 3840)
+    q = (q * q).astype(np.float32)
+    got = act.token_sum_rows(q, 256)
+    for r in range(4):
+        want = math.fsum(q[r].astype(np.float64).tolist())
+        assert abs(float(got[r]) - want) <= 1e-6 * want
+
+
+def test_token_sum_blocks_left_to_right():
+    # block sums 2^24, 1, 1: (2^24 + 1) + 1 loses both ones to ties-to-even;
+    # adding from the right (or over a tree of blocks) would keep them
+    h = 32
+    q = np.zeros((1, 3 * h), np.float32)
+    q[0, 0] = 2.0 ** 24
+    q[0, h] = 1.0
+    q[0, 2 * h] = 1.0
+    assert float(act.token_sum_rows(q, h)[0]) == 2.0 ** 24
+    q2 = np.zeros((1, 3 * h), np.float32)
+    q2[0, 0], q2[0, h], q2[0, 2 * h] = 1.0, 1.0, 2.0 ** 24
+    assert float(act.token_sum_rows(q2, h)[0]) == 2.0 ** 24 + 2.0
+    # one block: the plain tree
+    q3 = np.random.default_rng(1).random((3, 64)).astype(np.float32)
+    assert np.array_equal(act.token_sum_rows(q3, 64), act.tree_sum_rows(q3))
+
+
+def _check_brute_force(x, signs, cb, perm):
+    rows, d = x.shape
+    h = act.hadamard_block(d)
+    words, norms = act.assign(x, signs, cb, perm=perm)
+    xf = numerics.widen(x, "bf16").reshape(rows, d).astype(np.float64)
+    flip = act.sign_mask_to_bool(signs, d)
+    from scipy.linalg import block_diag
+    H = block_diag(*([hadamard(h).astype(np.float64)] * (d // h)))
+    idx = kbit.unpack(words, 4, rows * d).reshape(rows, d)
+    p = np.arange(d) if perm is None else np.asarray(perm)
+    checked = 0
+    for r in range(rows):
+        want_norm = math.sqrt(float(np.sum(xf[r] ** 2)))
+        assert abs(float(norms[r]) - want_norm) <= 1e-6 * max(want_norm, 1e-30)
+        u = H @ np.where(flip, -xf[r, p], xf[r, p])
+        den = max(float(norms[r]), float(np.float32(1e-10)))
+        for j in range(d):
+            dist = np.abs(u[j] / den - cb.astype(np.float64))
+            order = np.argsort(dist)
+            if dist[order[1]] - dist[order[0]] > 1e-4:
+                assert idx[r, j] == order[0]
+                checked += 1
+    assert checked > 0.9 * rows * d
+
+
+def test_assign_blocked_brute_force():
+    x, signs = synth.activations_bf16(tokens=3, d=96, seed=12)
+    cb = (codebooks.lloyd_max_normal(16) * np.float32(np.sqrt(1.0 / 3.0))).astype(np.float32)
+    _check_brute_force(x, signs, cb, None)
+
+
+def test_assign_permuted_brute_force():
+    x, signs = synth.activations_bf16(tokens=3, d=96, seed=13)
+    perm = np.random.default_rng(13).permutation(96)
+    cb = (codebooks.lloyd_max_normal(16) * np.float32(np.sqrt(1.0 / 3.0))).astype(np.float32)
+    _check_brute_force(x, signs, cb, perm)
+    # the norm is the token's: a permutation does not change it, and the
+    # identity permutation changes nothing
+    w0, n0 = act.assign(x, signs, cb)
+    w1, n1 = act.assign(x, signs, cb, perm=perm)
+    assert np.array_equal(n0, n1)
+    w2, n2 = act.assign(x, signs, cb, perm=np.arange(96))
+    assert np.array_equal(w0, w2) and np.array_equal(n0, n2)
+
+
+def test_assign_blocked_exact_rule_against_exact_scalar_search():
+    rows, d = 2, 96
+    x, signs = synth.activations_bf16(tokens=rows, d=d, seed=14)
+    perm = np.random.default_rng(14).permutation(d)
+    cb = codebooks.lloyd_max_normal(16)
+    words, norms = act.assign(x, signs, cb, perm=perm)
+    xf = numerics.widen(x, "bf16").reshape(rows, d)[:, perm]
+    u = act.fwht_rows(np.where(act.sign_mask_to_bool(signs, d)[None, :], -xf, xf), 32)
+    idx = kbit.unpack(words, 4, rows * d).reshape(rows, d)
+    for r in range(rows):
+        den = max(float(norms[r]), float(np.float32(1e-10)))
+        for j in range(d):
+            zn = exact.f32(exact.frac(u[r, j]) / exact.frac(den))
+            assert idx[r, j] == exact.nearest_first(zn, cb)
+
+
+def test_assign_rejects_bad_inputs():
+    x, signs = synth.activations_bf16(tokens=1, d=64, seed=1)
+    cb = codebooks.lloyd_max_normal(16)
+    with pytest.raises(ValueError):
+        act.assign(x[:, :48], signs, cb)
+    with pytest.raises(ValueError):
+        act.assign(x, signs, cb, perm=np.zeros(64, np.int64))
