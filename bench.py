@@ -300,20 +300,26 @@ def act_bytes(rows=ACT_ROWS, d=ACT_D):
     return 2 * n + d // 8 + 64 + (n // 32) * 4 * 4 + 4 * rows
 
 
-def bench_act(torch, kb, synth, dev, reps, sets=12):
-    """Timing of the W4A4 activation assignment on 4096 x 4096 bf16
-    (rows N(0,1) x 10^U(-1,1), shared sign mask, Lloyd-Max-16)."""
-    x, signs = synth.activations_bf16(ACT_ROWS, ACT_D)
-    cbl = torch.from_numpy(kb.codebook_lloyd_max_normal(16)).to(dev)
+def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, sets=12):
+    """Timing of the W4A4 activation assignment on rows x d bf16 (rows
+    N(0,1) x 10^U(-1,1), shared sign mask, Lloyd-Max-16 scaled by sqrt(h/d)
+    for d/h Hadamard blocks; with ``perm`` a random column permutation)."""
+    x, signs = synth.activations_bf16(rows, d)
+    h = d & -d
+    cb = (kb.codebook_lloyd_max_normal(16) * np.float32(np.sqrt(h / d))).astype(np.float32)
+    cbl = torch.from_numpy(cb).to(dev)
     sg = torch.from_numpy(signs.view(np.int32)).to(dev)
+    pm = None
+    if perm:
+        pm = torch.from_numpy(np.random.default_rng(d).permutation(d).astype(np.int32)).to(dev)
     x0 = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
     bufs = [(x0 if i == 0 else x0.clone(),
-             torch.empty(ACT_ROWS, dtype=torch.float32, device=dev),
-             torch.empty(kb.n_words(ACT_ROWS * ACT_D, 4), dtype=torch.int32, device=dev)) for i in range(sets)]
+             torch.empty(rows, dtype=torch.float32, device=dev),
+             torch.empty(kb.n_words(rows * d, 4), dtype=torch.int32, device=dev)) for i in range(sets)]
     torch.cuda.synchronize()
 
     def run(b):
-        kb.quantize_act_fwht_k4_bf16(b[0], sg, cbl, row_norm=b[1], packed=b[2])
+        kb.quantize_act_fwht_k4_bf16(b[0], sg, cbl, row_norm=b[1], packed=b[2], perm=pm)
 
     for _ in range(3):
         for b in bufs:
@@ -328,16 +334,23 @@ def bench_act(torch, kb, synth, dev, reps, sets=12):
     torch.cuda.synchronize()
     ts = np.array([ev[r].elapsed_time(ev[r + 1]) / sets for r in range(reps)])
     avg = float(ts.mean())
-    nbytes = act_bytes()
-    flops = ACT_FLOPS_PER_ELEM * ACT_ROWS * ACT_D
+    nbytes = act_bytes(rows, d) + (4 * d if perm else 0)
+    flops = ACT_FLOPS_PER_ELEM * rows * d
     gbps = nbytes / (avg * 1e-3) / 1e9
     tflops = flops / (avg * 1e-3) / 1e12
-    return {"workload": "4096 x 4096 bf16 activations, Lloyd-Max-16, K=4 planes, 12 rotated buffer sets",
+    return {"workload": f"{rows} x {d} bf16 activations, Hadamard blocks of {h}"
+                        f"{', column permutation' if perm else ''}, Lloyd-Max-16, K=4 planes, "
+                        f"{sets} rotated buffer sets",
             "avg_us": round(avg * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
             "bytes": nbytes, "GB/s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
             "algorithmic_flops": flops, "TFLOP/s": round(tflops, 3),
             "frac_of_fp32_valu_peak": round(tflops / VALU_FP32_PEAK_TFLOPS, 4),
-            "rows_per_s": round(ACT_ROWS / (avg * 1e-3), 1)}
+            "rows_per_s": round(rows / (avg * 1e-3), 1)}
+
+
+# Block-Hadamard activation cases: (rows, d, permutation).
+ACT_BLOCK_CASES = [(4096, 3840, False), (4096, 3840, True), (4096, 12288, False), (4096, 12288, True),
+                   (4096, 4096, True)]
 
 
 # The page's dequantize-plus-linear controls (M, N, K) and their candidate
@@ -579,7 +592,7 @@ def main(argv=None):
 
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
-    fp4 = warm = act = lin = None
+    fp4 = warm = act = act_block = lin = None
     if not args.headline_only:
         pair = {"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only}
         cb_nf = cb
@@ -594,6 +607,8 @@ def main(argv=None):
                 "note": "same buffer set every launch (warm cache); not the headline number"}
         if not args.no_act:
             act = bench_act(torch, kb, synth, dev, reps)
+            act_block = [bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp)
+                         for r, dd, pp in ACT_BLOCK_CASES]
         lin = bench_linear(torch, kb, synth, dev)
 
     dom_name, dom = ("quantize_kbit_bf16_k4", kq) if kq["avg_us"] >= kn["avg_us"] else \
@@ -645,6 +660,7 @@ def main(argv=None):
         "fp4_codebook": fp4,
         "warm": warm,
         "act_fwht": act,
+        "act_block_hadamard": act_block,
         "linear_4bit": lin,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": roofline,

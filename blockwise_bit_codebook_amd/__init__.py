@@ -21,7 +21,7 @@ import numpy as np
 __all__ = [
     "KbitError", "lib", "codebook_nf", "codebook_fp4", "codebook_lloyd_max_normal",
     "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax", "linear_4bit",
-    "quantize_act_fwht_k4_bf16", "n_words", "n_blocks",
+    "quantize_act_fwht_k4_bf16", "quantize_act_rpbh_k4_bf16", "n_words", "n_blocks",
 ]
 
 _TORCH_NAME = {"fp32": "float32", "fp16": "float16", "bf16": "bfloat16"}
@@ -219,8 +219,10 @@ def linear_4bit(X, packed, codebook16, N, blocksize, absmax=None, absmax_code=No
     return out
 
 
-def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=None):
-    """Token norm + sign flip + FWHT + Lloyd-Max assignment of bf16 [rows, 4096]."""
+def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=None, perm=None):
+    """Token norm + sign flip + block FWHT (h = largest power of two dividing
+    d) + Lloyd-Max assignment of bf16 [rows, d]; with ``perm`` (int32 [d])
+    the columns are permuted first (quantize_act_rpbh_k4_bf16)."""
     torch = _torch()
     if X.dtype != torch.bfloat16 or X.dim() != 2:
         raise TypeError("X must be a 2-D bfloat16 tensor")
@@ -229,10 +231,23 @@ def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=No
         row_norm = torch.empty(rows, dtype=torch.float32, device=X.device)
     if packed is None:
         packed = torch.empty(n_words(rows * d, 4), dtype=torch.int32, device=X.device)
-    name = "quantize_act_fwht_k4_bf16"
-    _check(name, lib().quantize_act_fwht_k4_bf16(_ptr(X), rows, d, _ptr(sign_bits), _ptr(codebook16),
-                                                  _ptr(row_norm), _ptr(packed), _stream(X.device)))
+    if perm is None:
+        name = "quantize_act_fwht_k4_bf16"
+        status = lib().quantize_act_fwht_k4_bf16(_ptr(X), rows, d, _ptr(sign_bits), _ptr(codebook16),
+                                                  _ptr(row_norm), _ptr(packed), _stream(X.device))
+    else:
+        if perm.dtype != torch.int32 or perm.numel() != d:
+            raise TypeError("perm must be an int32 tensor of d entries")
+        name = "quantize_act_rpbh_k4_bf16"
+        status = lib().quantize_act_rpbh_k4_bf16(_ptr(X), rows, d, _ptr(perm), _ptr(sign_bits), _ptr(codebook16),
+                                                  _ptr(row_norm), _ptr(packed), _stream(X.device))
+    _check(name, status)
     return packed, row_norm
+
+
+def quantize_act_rpbh_k4_bf16(X, perm, sign_bits, codebook16, row_norm=None, packed=None):
+    """Column permutation, then quantize_act_fwht_k4_bf16's path."""
+    return quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=row_norm, packed=packed, perm=perm)
 
 
 def _make_named(fn_name, generic, **fixed):

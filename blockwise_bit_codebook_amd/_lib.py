@@ -29,6 +29,7 @@ def _signatures():
         ("kbit_codebook_lloyd_max_normal", [ct.c_int, _p]),
         ("kbit_dynamic_map8", [_p]),
         ("quantize_act_fwht_k4_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p]),
+        ("quantize_act_rpbh_k4_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p, _p]),
         ("kbit_nested_workspace_bytes", [_i64]),
         ("linear_kbit_bf16_k4", [_p, _i64, _i32, _p, _p, _p, _i32, _i32, _p, _p]),
         ("linear_4bit_nested_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p, _f32, _i32, _i32, _p, _p]),

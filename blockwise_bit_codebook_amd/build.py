@@ -26,7 +26,8 @@ LIB = os.path.join(PKG, "libkbit.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["quantize.hip", "dequantize.hip", "nested_encode.hip", "linear.hip", "act_fwht.hip"]
+HIP_SOURCES = ["quantize.hip", "dequantize.hip", "nested_encode.hip", "linear.hip", "act_fwht.hip",
+               "act_block.hip"]
 CXX_SOURCES = ["api.cpp", "codebook.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC]

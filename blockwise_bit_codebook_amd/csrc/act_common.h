@@ -1,0 +1,180 @@
+// Pieces shared by the activation-assignment kernels: the threshold tables
+// for the 16 Lloyd-Max centroids, the row-buffer layout in LDS, the 16-point
+// butterfly pass, the per-element assignment and the bit-plane packing.
+//
+// Assignment ([ORBIT] methodology audit: divide by max(norm, 1e-10) when
+// choosing indices): z = RN(u / max(norm, 1e-10f)), idx = first-index
+// argmin |RN(z - c_i)|, decided with the exact switching-point test of
+// threshold.h (q clamped into [2, 4)).  |z| <= sqrt(h) <= 128 for Hadamard
+// blocks of h <= 16384 (|u| <= sqrt(h) * norm), so the distances round at
+// <= 2^-17, far below the smallest centroid gap the fast path accepts.
+// Rows whose norm is not finite, and codebooks that do not qualify, take
+// the exact path (IEEE division and the full scan).
+#pragma once
+
+#include "device.h"
+#include "threshold.h"
+
+namespace kbit {
+namespace act {
+
+constexpr float kActEps = 1e-10f;
+constexpr float kZRange = 4.0f;               // thresholds must lie inside (-4, 4)
+constexpr float kActSlope = 0.99f / kZRange;  // q = kActBase + kActSlope * z
+constexpr float kActBase = 3.0f + 0x1p-10f;
+constexpr float kActMinGap = 0x1p-12f;
+constexpr float kQMax = 0x1.fffffep+1f;       // largest float below 4
+
+using ActTables = ThresholdTables<16>;
+
+// LDS position of element 256a + 16b + c of a row: 16 floats of padding per
+// 256 keep the strided passes conflict-free, and the swizzle of the four
+// 16-byte chunks of each 16 does the same for 16-byte-per-lane accesses.
+__device__ __forceinline__ int swz(int a, int b, int c) { return 272 * a + 16 * b + (c ^ (((b >> 1) & 3) << 2)); }
+__device__ __forceinline__ int swz_i(int i) { return swz(i >> 8, (i >> 4) & 15, i & 15); }
+
+// Stages s = 1, 2, ..., N/2 of the butterfly over the first N entries of v
+// (every output rounded to fp32; the stages keep their order).
+template <int N>
+__device__ __forceinline__ void fwht_pts(float (&v)[16]) {
+#pragma unroll
+    for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            if ((j & h) == 0) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t nearest16_lds(const float* c, float z) {
+    uint32_t best = 0;
+    float bd = fabsf(z - c[0]);
+#pragma unroll 1
+    for (int i = 1; i < 16; ++i) {
+        const float d = fabsf(z - c[i]);
+        if (d < bd) {
+            bd = d;
+            best = i;
+        }
+    }
+    return best;
+}
+
+// Builds T for the codebook cb.  Every thread of the workgroup calls it
+// (nthreads = blockDim.x, a multiple of 64 and at least 128); it holds
+// barriers.  Returns whether the fast path applies.
+__device__ inline bool build_act_tables(ActTables& T, const float* __restrict__ cb, int nthreads) {
+    const int lane = __lane_id();
+    float c[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = cb[i];
+    bool fast = true;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) fast = fast && (c[i] == c[i - 1] || c[i] - c[i - 1] >= kActMinGap);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        const float m = (c[i - 1] + c[i]) * 0.5f;
+        fast = fast && (c[i] == c[i - 1] || (m > -0.97f * kZRange && m < 0.97f * kZRange));
+    }
+    if (threadIdx.x == 0) T.fail = 0;
+    if (threadIdx.x < 16) T.code[threadIdx.x] = c[threadIdx.x];
+    // One half-wave per threshold, all searched at once; a failed search
+    // leaves the sentinel, which fails the table below.
+    {
+        const int groups = 2 * nthreads / kWave;
+        const int gid = 2 * static_cast<int>(threadIdx.x / kWave) + (lane >> 5);
+        for (int i0 = 1; i0 < 16; i0 += groups) {  // uniform trip count
+            const int i = i0 + gid;
+            const bool real = i < 16;
+            const float lo = real ? cb[i - 1] : 0.0f, hi = real ? cb[i] : 0.0f;
+            uint64_t m = 0;
+            const bool ok = threshold_mid_group<32>(lo, hi, m);  // every lane calls it
+            if (real && (lane & 31) == 0) T.mid[i] = (fast && lo != hi) ? (ok ? m : kNoMid) : 0u;
+        }
+    }
+    if (threadIdx.x == 0) T.mid[0] = 0;
+    __syncthreads();
+    if (threadIdx.x < 16 && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
+    if (fast && threadIdx.x < kBuckets) {
+        u32x4 e;
+        if (!build_entry<16, false>(c, T.mid, threadIdx.x, kActSlope, kActBase, e)) T.fail = 1;
+        T.master[threadIdx.x] = e;
+    }
+    __syncthreads();
+    fast = fast && (T.fail == 0);
+    if (fast) {
+        for (int i = threadIdx.x; i < kBuckets * kCopies; i += nthreads) T.row[i] = T.master[i / kCopies];
+    }
+    __syncthreads();
+    return fast;
+}
+
+// Indices of the 16 transformed values v of a row with norm `norm`, as two
+// plane accumulators: bit k of byte j of acc[h] is plane j of element
+// 8h + k.  Every lane of the wave must work on the same row (the finite-norm
+// test is a wave vote).
+__device__ __forceinline__ void assign16(const float (&v)[16], float norm, bool fast, const ActTables& T,
+                                         uint32_t (&acc)[2]) {
+    const uint32_t lane_off = static_cast<uint32_t>(__lane_id() & (kCopies - 1)) * 16u;
+    const char* tab = reinterpret_cast<const char*>(T.row);
+    // max(norm, eps) with a NaN norm kept NaN (fmaxf would drop it)
+    const float den = norm < kActEps ? kActEps : norm;
+    acc[0] = 0u;
+    acc[1] = 0u;
+    if (fast && __builtin_amdgcn_ballot_w64(!(norm < __builtin_inff())) == 0) {
+        const float r = __builtin_amdgcn_rcpf(den) * kActSlope;
+        const double d64 = static_cast<double>(den);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int k = 7; k >= 0; --k) {
+                const float z = v[8 * h + k];
+                const float q = __builtin_amdgcn_fmed3f(__builtin_fmaf(z, r, kActBase), 2.0f, kQMax);
+                const Decision d = decide(z, q, d64, tab, lane_off);
+                acc[h] = (acc[h] << 1) | (d.up ? d.e[3] : d.e[2]);
+            }
+        }
+    } else {
+        // one element per iteration (rare path): rotate a copy so that the
+        // element in use is always y[0]
+        float y[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) y[i] = v[i];
+#pragma unroll 1
+        for (int k = 0; k < 16; ++k) {
+            acc[k >> 3] |= spread4(nearest16_lds(T.code, y[0] / den)) << (k & 7);
+#pragma unroll
+            for (int i = 0; i < 15; ++i) y[i] = y[i + 1];
+        }
+    }
+}
+
+// The 4 plane words of a group of 32 elements from the two lanes 2g (first
+// 16) and 2g + 1 (last 16); `odd` is the lane's parity.  Both lanes of the
+// pair must be active.  The lane gets words 2*odd and 2*odd + 1.
+__device__ __forceinline__ uint2 pack_pair(const uint32_t (&acc)[2], bool odd) {
+    // per lane: plane j's 16 bits = [acc0 byte j, acc1 byte j]
+    const uint32_t h01 = __builtin_amdgcn_perm(acc[1], acc[0], 0x05010400u);
+    const uint32_t h23 = __builtin_amdgcn_perm(acc[1], acc[0], 0x07030602u);
+    const uint32_t mine = odd ? h23 : h01;
+    const uint32_t recv = dpp_u32<kDppXor1>(odd ? h01 : h23);
+    const uint32_t lo = odd ? recv : mine, hi = odd ? mine : recv;  // even lane's half first
+    return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05040100u), __builtin_amdgcn_perm(hi, lo, 0x07060302u));
+}
+
+// Sum of the lanes' values over each aligned group of 16 lanes, as a tree
+// of contiguous halves (pairs, then quads, eights, sixteens).
+__device__ __forceinline__ float sum16_tree(float S) {
+    S = S + dpp_f32<kDppXor1>(S);
+    S = S + dpp_f32<kDppXor2>(S);
+    S = S + dpp_f32<kDppHalfMirror>(S);
+    S = S + dpp_f32<kDppMirror>(S);
+    return S;
+}
+
+}  // namespace act
+}  // namespace kbit

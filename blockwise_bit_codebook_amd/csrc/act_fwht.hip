@@ -34,59 +34,21 @@
 // |u| <= sqrt(4096)*norm): one LDS entry read and one fp64 fma per element.
 // Rows whose norm is not finite, and codebooks that do not qualify, take
 // the exact path (IEEE division and the full scan).
+#include "act_common.h"
 #include "device.h"
 #include "kbit_internal.h"
 #include "launch.h"
-#include "threshold.h"
 
 namespace kbit {
 namespace {
+
+using namespace act;
 
 constexpr int kD = 4096;
 constexpr int kRowThreads = 256;
 constexpr int kPer = kD / kRowThreads;  // 16 elements per thread
 constexpr int kSlotsDefault = 2;        // rows in flight per workgroup
-constexpr float kActEps = 1e-10f;
-constexpr float kZRange = 4.0f;                      // thresholds must lie inside (-4, 4)
-constexpr float kActSlope = 0.99f / kZRange;         // q = kActBase + kActSlope * z
-constexpr float kActBase = 3.0f + 0x1p-10f;
-constexpr float kActMinGap = 0x1p-12f;               // |z| <= 64: distances round at <= 2^-17
-constexpr float kQMax = 0x1.fffffep+1f;              // largest float below 4
 constexpr int kBufFloats = kD + (kD / 256) * 16;     // padded row buffer
-
-// LDS position of element 256a + 16b + c of the row.
-__device__ __forceinline__ int swz(int a, int b, int c) { return 272 * a + 16 * b + (c ^ (((b >> 1) & 3) << 2)); }
-
-using ActTables = ThresholdTables<16>;
-
-// In-register 16-point butterfly passes: stages h = 1, 2, 4, 8 of v's index.
-__device__ __forceinline__ void fwht16(float (&v)[kPer]) {
-#pragma unroll
-    for (int h = 1; h < kPer; h <<= 1) {
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            if ((j & h) == 0) {
-                const float a = v[j], b = v[j + h];
-                v[j] = a + b;
-                v[j + h] = a - b;
-            }
-        }
-    }
-}
-
-__device__ __forceinline__ uint32_t nearest16_lds(const float* c, float z) {
-    uint32_t best = 0;
-    float bd = fabsf(z - c[0]);
-#pragma unroll 1
-    for (int i = 1; i < 16; ++i) {
-        const float d = fabsf(z - c[i]);
-        if (d < bd) {
-            bd = d;
-            best = i;
-        }
-    }
-    return best;
-}
 
 template <int kSlots>
 __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const uint16_t* __restrict__ X, int64_t rows,
@@ -121,50 +83,8 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     load_raw(static_cast<int64_t>(blockIdx.x) * kSlots + slot, cur_a, cur_b);
 
     // ---- table build (once per workgroup) ---------------------------------
-    float c[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = cb[i];
-    bool fast = true;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) fast = fast && (c[i] == c[i - 1] || c[i] - c[i - 1] >= kActMinGap);
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-        const float m = (c[i - 1] + c[i]) * 0.5f;
-        fast = fast && (c[i] == c[i - 1] || (m > -0.97f * kZRange && m < 0.97f * kZRange));
-    }
-    if (threadIdx.x == 0) T.fail = 0;
-    if (threadIdx.x < 16) T.code[threadIdx.x] = c[threadIdx.x];
-    // One half-wave per threshold, all searched at once; a failed search
-    // leaves the sentinel, which fails the table below.
-    {
-        constexpr int kGroups = 2 * kActThreads / kWave;
-        const int gid = 2 * static_cast<int>(threadIdx.x / kWave) + (lane >> 5);
-        for (int i0 = 1; i0 < 16; i0 += kGroups) {  // uniform trip count
-            const int i = i0 + gid;
-            const bool real = i < 16;
-            const float lo = real ? cb[i - 1] : 0.0f, hi = real ? cb[i] : 0.0f;
-            uint64_t m = 0;
-            const bool ok = threshold_mid_group<32>(lo, hi, m);  // every lane calls it
-            if (real && (lane & 31) == 0) T.mid[i] = (fast && lo != hi) ? (ok ? m : kNoMid) : 0u;
-        }
-    }
-    if (threadIdx.x == 0) T.mid[0] = 0;
-    __syncthreads();
-    if (threadIdx.x < 16 && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
-    if (fast && threadIdx.x < kBuckets) {
-        u32x4 e;
-        if (!build_entry<16, false>(c, T.mid, threadIdx.x, kActSlope, kActBase, e)) T.fail = 1;
-        T.master[threadIdx.x] = e;
-    }
-    __syncthreads();
-    fast = fast && (T.fail == 0);
-    if (fast) {
-        for (int i = threadIdx.x; i < kBuckets * kCopies; i += kActThreads) T.row[i] = T.master[i / kCopies];
-    }
-    __syncthreads();
+    const bool fast = build_act_tables(T, cb, kActThreads);
 
-    const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
-    const char* tab = reinterpret_cast<const char*>(T.row);
     // Sign flips as XOR masks on the raw bf16 words: element 2i is the low
     // half of word i (sign bit 15), element 2i+1 the high half (bit 31).
     const uint32_t signs = (sign_bits[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
@@ -205,17 +125,13 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
             for (int wd = kPer; wd > 1; wd >>= 1)
 #pragma unroll
                 for (int i = 0; i < wd / 2; ++i) q[i] = q[2 * i] + q[2 * i + 1];
-            float S = q[0];
-            S = S + dpp_f32<kDppXor1>(S);
-            S = S + dpp_f32<kDppXor2>(S);
-            S = S + dpp_f32<kDppHalfMirror>(S);
-            S = S + dpp_f32<kDppMirror>(S);
+            float S = sum16_tree(q[0]);
             S = S + shfl_xor_f32(S, 16);
             S = S + shfl_xor_f32(S, 32);
             if (lane == 0) ws[wave] = S;
         }
         // --- pass 1 (bits 0-3), to LDS -----------------------------------------
-        fwht16(v);
+        fwht_pts<16>(v);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             *reinterpret_cast<float4*>(rb + seg + 4 * (k ^ sw)) = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2],
@@ -226,7 +142,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
         {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) v[i] = rb[swz(hi4, i, lo4)];
-            fwht16(v);
+            fwht_pts<16>(v);
 #pragma unroll
             for (int i = 0; i < kPer; ++i) rb[swz(hi4, i, lo4)] = v[i];
         }
@@ -235,7 +151,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
         {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) v[i] = rb[swz(i, hi4, lo4)];
-            fwht16(v);
+            fwht_pts<16>(v);
 #pragma unroll
             for (int i = 0; i < kPer; ++i) rb[swz(i, hi4, lo4)] = v[i];
         }
@@ -251,46 +167,12 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
                 v[4 * k + 3] = f.w;
             }
         }
-        // --- assignment: two 8-element plane accumulators -------------------
-        const float den = fmaxf(norm, kActEps);
-        uint32_t acc[2] = {0u, 0u};
-        if (fast && __builtin_amdgcn_ballot_w64(!(norm < __builtin_inff())) == 0) {
-            const float r = __builtin_amdgcn_rcpf(den) * kActSlope;
-            const double d64 = static_cast<double>(den);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int k = 7; k >= 0; --k) {
-                    const float z = v[8 * h + k];
-                    const float q = __builtin_amdgcn_fmed3f(__builtin_fmaf(z, r, kActBase), 2.0f, kQMax);
-                    const Decision d = decide(z, q, d64, tab, lane_off);
-                    acc[h] = (acc[h] << 1) | (d.up ? d.e[3] : d.e[2]);
-                }
-            }
-        } else {
-            // one element per iteration (rare path): rotate a copy so that
-            // the element in use is always y[0]
-            float y[kPer];
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) y[i] = v[i];
-#pragma unroll 1
-            for (int k = 0; k < kPer; ++k) {
-                acc[k >> 3] |= spread4(nearest16_lds(T.code, y[0] / den)) << (k & 7);
-#pragma unroll
-                for (int i = 0; i < kPer - 1; ++i) y[i] = y[i + 1];
-            }
-        }
-        // --- pack: lanes 2g, 2g+1 hold the 32 elements of group g ------------
+        // --- assignment and packing: lanes 2g, 2g+1 hold the 32 elements of
+        // group g -------------------------------------------------------------
+        uint32_t acc[2];
+        assign16(v, norm, fast, T, acc);
         {
-            // per lane: plane j's 16 bits = [acc0 byte j, acc1 byte j]
-            const uint32_t h01 = __builtin_amdgcn_perm(acc[1], acc[0], 0x05010400u);
-            const uint32_t h23 = __builtin_amdgcn_perm(acc[1], acc[0], 0x07030602u);
-            const bool odd = (t & 1) != 0;
-            const uint32_t mine = odd ? h23 : h01;
-            const uint32_t recv = dpp_u32<kDppXor1>(odd ? h01 : h23);
-            const uint32_t lo = odd ? recv : mine, hi = odd ? mine : recv;  // even lane's half first
-            const uint2 words = make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05040100u),
-                                           __builtin_amdgcn_perm(hi, lo, 0x07060302u));
+            const uint2 words = pack_pair(acc, (t & 1) != 0);
             if (valid) {
                 uint32_t* dst = packed + row * (kD / kGroup) * 4 + (t >> 1) * 4 + (t & 1) * 2;
                 dst[0] = words.x;

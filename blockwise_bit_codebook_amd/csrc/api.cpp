@@ -109,6 +109,20 @@ int check_linear(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed
     return 1;  // proceed (the caller checks its scale arguments, then the device)
 }
 
+
+// Shared argument checks of the activation entry points: 1 = go on.
+int check_act(const uint16_t* X, int64_t rows, int32_t d, const uint32_t* sign_bits, const int32_t* perm,
+              const float* codebook16, const float* row_norm, const uint32_t* packed) {
+    if (!act_block_supported(d)) return KBIT_EINVAL;
+    if (rows < 0 || rows > kMaxElems / d) return KBIT_EINVAL;
+    if (rows == 0) return KBIT_OK;
+    if (!X || !sign_bits || !codebook16 || !row_norm || !packed) return KBIT_EINVAL;
+    if (!aligned(X, 16) || !aligned(sign_bits, 4) || !aligned(codebook16, 4) || !aligned(row_norm, 4) ||
+        !aligned(packed, 4) || !aligned(perm, 16))
+        return KBIT_EALIGN;
+    if (current_device_cus() <= 0) return KBIT_EDEVICE;
+    return 1;
+}
 }  // namespace
 
 constexpr int64_t kMaxNestedBlocks = int64_t(1) << 36;
@@ -137,7 +151,7 @@ const char* kbit_strerror(int status) {
     }
 }
 
-int kbit_abi_version(void) { return 2; }
+int kbit_abi_version(void) { return 3; }
 
 #define KBIT_DEFINE_QUANTIZE(TNAME, CTYPE, DT, K)                                                   \
     int quantize_kbit_##TNAME##_k##K(const float* codebook, const CTYPE* A, float* absmax,          \
@@ -239,15 +253,22 @@ int linear_4bit_nested_bf16(const uint16_t* X, int64_t M, int32_t K, const uint3
 
 int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const uint32_t* sign_bits,
                               const float* codebook16, float* row_norm, uint32_t* packed, void* stream) {
-    if (d != 4096) return KBIT_EINVAL;
-    if (rows < 0 || rows > (kbit::kMaxElems >> 12)) return KBIT_EINVAL;
-    if (rows == 0) return KBIT_OK;
-    if (!X || !sign_bits || !codebook16 || !row_norm || !packed) return KBIT_EINVAL;
-    if (!kbit::aligned(X, 16) || !kbit::aligned(sign_bits, 4) || !kbit::aligned(codebook16, 4) ||
-        !kbit::aligned(row_norm, 4) || !kbit::aligned(packed, 4))
-        return KBIT_EALIGN;
-    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
-    return kbit::map_launch(kbit::launch_act_fwht(X, rows, d, sign_bits, codebook16, row_norm, packed, stream));
+    const int c = kbit::check_act(X, rows, d, sign_bits, nullptr, codebook16, row_norm, packed);
+    if (c != 1) return c;
+    if (d == 4096)
+        return kbit::map_launch(kbit::launch_act_fwht(X, rows, d, sign_bits, codebook16, row_norm, packed, stream));
+    return kbit::map_launch(
+        kbit::launch_act_block(X, rows, d, sign_bits, nullptr, codebook16, row_norm, packed, stream));
+}
+
+int quantize_act_rpbh_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const int32_t* perm,
+                              const uint32_t* sign_bits, const float* codebook16, float* row_norm,
+                              uint32_t* packed, void* stream) {
+    if (!perm && rows > 0) return KBIT_EINVAL;
+    const int c = kbit::check_act(X, rows, d, sign_bits, perm, codebook16, row_norm, packed);
+    if (c != 1) return c;
+    return kbit::map_launch(
+        kbit::launch_act_block(X, rows, d, sign_bits, perm, codebook16, row_norm, packed, stream));
 }
 
 }  // extern "C"

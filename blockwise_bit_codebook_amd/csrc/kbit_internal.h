@@ -38,6 +38,10 @@ int launch_linear4_nested(const uint16_t* X, int64_t M, int K, const uint32_t* p
 
 int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
+// Any d with act_block_supported(d); perm may be null (identity).
+bool act_block_supported(int d);
+int launch_act_block(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits, const int32_t* perm,
+                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
 
 // Number of workgroups that fill the current device for a kernel whose
 // per-CU residency is `blocks_per_cu`.  Returns 0 if no device is usable.

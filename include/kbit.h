@@ -265,27 +265,49 @@ int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2,
 /* ------------------------------------------------------------------------
  * W4A4-style activation assignment ([ORBIT] README W4A4 fast path and
  * CARD.md quantize_activations_packed_w4; exact Lloyd-Max centroids, packed
- * 4-bit output).  Per row r of X (rows x d, bf16, row-major):
- *   norm_r = RN(sqrt(S)), S = sum of x_i^2 over a perfect binary tree of
- *            contiguous halves, each addition rounded to fp32;
+ * 4-bit output; methodology audit: block Hadamard of size h = the largest
+ * power of two dividing d, e.g. h = 256 for d = 3840).  Per row r of X
+ * (rows x d, bf16, row-major), with the row split into d/h blocks of h
+ * contiguous columns:
+ *   norm_r = RN(sqrt(S)); S = sum of x_i^2, inside each block over a
+ *            perfect binary tree of contiguous halves, then the block sums
+ *            added left to right, every addition rounded to fp32;
  *   u      = x with its sign flipped where bit (i % 32) of sign_bits[i / 32]
  *            is 1 (one mask shared by all rows);
- *   u      = unnormalised Walsh-Hadamard transform of length d, natural
- *            order, stages h = 1, 2, ..., d/2 in that order, every
- *            butterfly (u_j + u_{j+h}, u_j - u_{j+h}) rounded to fp32;
- *   z      = RN(u / max(norm_r, 1e-10f));
+ *   u      = unnormalised Walsh-Hadamard transform of every block, natural
+ *            order, stages s = 1, 2, ..., h/2 in that order, every
+ *            butterfly (u_j + u_{j+s}, u_j - u_{j+s}) rounded to fp32;
+ *   z      = RN(u / max(norm_r, 1e-10f)) (a NaN norm stays NaN in the
+ *            max, so every z of that row is NaN and its indices are 0);
  *   index  = smallest i minimising |RN(z - codebook16[i])|.
- * X          : device, rows*d uint16 (bf16 bits).
+ * For d = h (e.g. 4096) this is one transform of the whole row.  The
+ * codebook is the caller's: with d/h blocks the entries of z have about
+ * h/d times the variance they have for d = h.
+ * X          : device, rows*d uint16 (bf16 bits), 16-byte aligned.
  * sign_bits  : device, d/32 uint32.
  * codebook16 : device, 16 float32 (e.g. kbit_codebook_lloyd_max_normal(16)).
  * row_norm   : device, rows float32 (output, unclamped norm).
  * packed     : device, rows*d/32*4 uint32 (output; K = 4 bit planes of the
  *              flattened index array, row after row).
- * d must be 4096 (KBIT_EINVAL otherwise); rows >= 0.
+ * d must be a multiple of 256 with 256 <= d <= 16384 (KBIT_EINVAL
+ * otherwise); rows >= 0.
  * --------------------------------------------------------------------- */
 int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d,
                               const uint32_t* sign_bits, const float* codebook16,
                               float* row_norm, uint32_t* packed, void* stream);
+
+/* The same with the column permutation of RPBH in front of the sign flip:
+ * u_i = x_{perm[i]}, then the sign flip of column i and the block
+ * transform; the norm is the token's (of x in its own order).  The pages
+ * do not say how the permutation is drawn, so it is an input.
+ * perm : device, d int32, 16-byte aligned, a permutation of 0..d-1
+ *        (required; KBIT_EINVAL if null and rows > 0).  Entries outside
+ *        [0, d) are not detected: they read column d - 1 (never outside
+ *        the row). */
+int quantize_act_rpbh_k4_bf16(const uint16_t* X, int64_t rows, int32_t d,
+                              const int32_t* perm, const uint32_t* sign_bits,
+                              const float* codebook16, float* row_norm,
+                              uint32_t* packed, void* stream);
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,8 @@ two dividing d; the row is d/h blocks of h contiguous columns):
      with j & s == 0 becomes (RN(u_j + u_{j+s}), RN(u_j - u_{j+s}));
      pairs never leave a block because s < h and blocks start at multiples
      of h;
-  6. z = RN(u / max(norm, 1e-10f));
+  6. z = RN(u / max(norm, 1e-10f)), the max keeping a NaN norm NaN (as
+     numpy's and torch's maximum do), so every z of such a row is NaN;
   7. idx = first-index argmin of |RN(z - c_i)| over the 16 centroids;
   8. pack idx along the flattened rows with the K = 4 bit-plane layout.
 Returns (packed words, norms).

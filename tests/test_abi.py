@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 2 + 1, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 2 + 2, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -75,7 +75,7 @@ def test_generator_argument_errors():
     assert lib.kbit_codebook_lloyd_max_normal(3, p) == -1
     assert lib.kbit_codebook_fp4(None) == -1
     assert lib.kbit_strerror(-2).decode().startswith("blocksize")
-    assert lib.kbit_abi_version() == 2
+    assert lib.kbit_abi_version() == 3
 
 
 # fake, never dereferenced device addresses
@@ -135,6 +135,14 @@ def test_validation_codes_before_any_device_access():
     assert ln(_A16, 4, 64, _A16, _A16, None, _A16, _A16, ct.c_float(0), 64, 64, _A16, None) == -1
     assert ln(_A4, 4, 64, _A16, _A16, _A16, _A16, _A16, ct.c_float(0), 64, 64, _A16, None) == -3
     act = lib.quantize_act_fwht_k4_bf16
-    assert act(_A16, 4, 2048, _A16, _A16, _A16, _A16, None) == -1  # d must be 4096
+    assert act(_A16, 4, 2000, _A16, _A16, _A16, _A16, None) == -1  # d not a multiple of 256
+    assert act(_A16, 4, 128, _A16, _A16, _A16, _A16, None) == -1   # d below 256
+    assert act(_A16, 4, 16640, _A16, _A16, _A16, _A16, None) == -1  # d above 16384
+    assert act(_A16, 1 << 40, 4096, _A16, _A16, _A16, _A16, None) == -1  # rows * d too large
     assert act(_A16, 0, 4096, None, None, None, None, None) == 0
     assert act(_A4, 4, 4096, _A16, _A16, _A16, _A16, None) == -3
+    rp = lib.quantize_act_rpbh_k4_bf16
+    assert rp(_A16, 4, 3840, None, _A16, _A16, _A16, _A16, None) == -1   # no permutation
+    assert rp(_A16, 4, 3900, _A16, _A16, _A16, _A16, _A16, None) == -1   # d
+    assert rp(_A16, 4, 3840, _A4, _A16, _A16, _A16, _A16, None) == -3    # perm not 16-byte aligned
+    assert rp(None, 0, 3840, None, None, None, None, None, None) == 0     # rows = 0: no-op
