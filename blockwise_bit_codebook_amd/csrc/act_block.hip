@@ -18,9 +18,11 @@
 //   z     = RN(u / max(norm, 1e-10f)); idx = first-index argmin |RN(z - c_i)|;
 //   packed: 4 bit-plane words per 32 elements along the row.
 //
-// How: 256 threads per row, one to four rows per workgroup (as many as
-// fit in LDS next to the shared threshold tables).  The row is d/16 units
-// of 16 contiguous elements; thread t takes units t, t + 256, ...  Loads
+// How: one to four rows per workgroup (as many as fit in LDS next to the
+// shared threshold tables), with 1024, 512 or 256 threads per row so that
+// the workgroup has 768 or 1024 threads.  The row is d/16 units of 16
+// contiguous elements; thread t of a row takes units t, t + T, ... (T
+// threads per row).  Loads
 // are 32 bytes per unit.  The squares of a unit are summed as a tree in
 // registers, the 16 units of each 256-chunk by DPP (tree of contiguous
 // halves), the chunks of a block by lane shuffles in wave 0 (again pairing
@@ -58,10 +60,10 @@ __host__ __device__ constexpr int row_buffer_floats(int d) { return (d / 256) * 
 // 2^P elements base + (m << LO), m < 2^P, with base's bits [LO, LO + P)
 // zero; unit u has base = (u mod 2^LO) + (u >> LO) * 2^(LO + P).
 template <int LO, int P>
-__device__ __forceinline__ void lds_pass(float* rb, int t, int d) {
+__device__ __forceinline__ void lds_pass(float* rb, int t, int rt, int d) {
     constexpr int kN = 1 << P;
     const int units = d >> P;
-    for (int u = t; u < units; u += kRowThreads) {
+    for (int u = t; u < units; u += rt) {
         const int base = (u & ((1 << LO) - 1)) | ((u >> LO) << (LO + P));
         float v[16];
 #pragma unroll
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
                                                                 const int32_t* __restrict__ perm,
                                                                 const float* __restrict__ cb,
                                                                 float* __restrict__ row_norm,
-                                                                uint32_t* __restrict__ packed) {
+                                                                uint32_t* __restrict__ packed, int slots) {
     constexpr int kH = 1 << L;
     constexpr int kChunksPerBlock = kH / 256;
     static_assert(L >= 8 && L <= 14, "Hadamard blocks of 256 .. 16384");
@@ -133,9 +135,9 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
     __shared__ float row_nrm[kMaxSlots];
 
     const int nthreads = static_cast<int>(blockDim.x);
-    const int slots = nthreads / kRowThreads;
-    const int slot = threadIdx.x / kRowThreads;
-    const int t = threadIdx.x % kRowThreads;
+    const int rt = nthreads / slots;  // threads per row, a multiple of 256
+    const int slot = threadIdx.x / rt;
+    const int t = threadIdx.x % rt;
     const int lane = __lane_id();
     const int units = d >> 4;
     const int chunks = d >> 8;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
     uint16_t* raw = reinterpret_cast<uint16_t*>(slot_lds + row_buffer_floats(d) * 4);  // permutation only
     float* cs = chunk_sum[slot];
 
-    const bool fast = build_act_tables(T, cb, nthreads);
+    const ActPlan plan = build_act_tables(T, cb, nthreads);
 
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * slots; base < rows;
          base += static_cast<int64_t>(gridDim.x) * slots) {
@@ -166,9 +168,9 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
             };
             uint4 na, nb;
             load_unit_raw(t, na, nb);
-            for (int u = t; u < units; u += kRowThreads) {
+            for (int u = t; u < units; u += rt) {
                 const uint4 a = na, b = nb;
-                load_unit_raw(u + kRowThreads, na, nb);
+                load_unit_raw(u + rt, na, nb);
                 const uint32_t signs = kPerm ? 0u : (sign_bits[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
                 float v[16];
                 widen_unit(a, b, signs, v);
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
         }
         if constexpr (kPerm) {
             // u_i = x_{perm[i]} gathered from the raw row, sign flip, bits 0-3
-            for (int u = t; u < units; u += kRowThreads) {
+            for (int u = t; u < units; u += rt) {
                 const uint32_t signs = (sign_bits[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
                 const int4* pp = reinterpret_cast<const int4*>(perm + 16 * u);
                 float v[16];
@@ -226,23 +228,23 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
             __syncthreads();
         }
         // ---- bits 4-7, 8..min(L,12)-1, 12..L-1 through LDS -------------------
-        lds_pass<4, 4>(rb, t, d);
+        lds_pass<4, 4>(rb, t, rt, d);
         __syncthreads();
         if constexpr (L > 8) {
-            lds_pass<8, (L - 8 < 4 ? L - 8 : 4)>(rb, t, d);
+            lds_pass<8, (L - 8 < 4 ? L - 8 : 4)>(rb, t, rt, d);
             __syncthreads();
         }
         if constexpr (L > 12) {
-            lds_pass<12, L - 12>(rb, t, d);
+            lds_pass<12, L - 12>(rb, t, rt, d);
             __syncthreads();
         }
         // ---- assignment and packing: lanes 2g, 2g+1 hold group g's 32 -------
         const float norm = row_nrm[slot];
-        for (int u = t; u < units; u += kRowThreads) {  // lanes t, t ^ 1 agree (units is even)
+        for (int u = t; u < units; u += rt) {  // lanes t, t ^ 1 agree (units is even)
             float v[16];
             load_unit(rb, u, v);
             uint32_t acc[2];
-            assign16(v, norm, fast, T, acc);
+            assign16(v, norm, plan, T, acc);
             const uint2 words = pack_pair(acc, (u & 1) != 0);
             if (valid) {
                 uint32_t* dst = packed + row * (d / kGroup) * 4 + (u >> 1) * 4 + (u & 1) * 2;
@@ -272,7 +274,9 @@ int launch_block_t(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_
     int slots = (kLdsBudget - kStaticLds - 1024) / row_bytes;
     if (slots > kMaxSlots) slots = kMaxSlots;
     if (slots < 1) slots = 1;
-    const int threads = slots * kRowThreads;
+    // up to 1024 threads: 256 per row, or all of them on one or two rows
+    const int rt = slots == 1 ? 1024 : slots == 2 ? 512 : kRowThreads;
+    const int threads = slots * rt;
     const size_t dyn = static_cast<size_t>(slots) * row_bytes;
     // workgroups per CU, by d / 256 (same answer for every caller)
     static int per_cu_cache[kMaxChunks + 1] = {};
@@ -287,7 +291,7 @@ int launch_block_t(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(threads), dyn, static_cast<hipStream_t>(stream),
-                       X, rows, d, sign_bits, perm, cb, row_norm, packed);
+                       X, rows, d, sign_bits, perm, cb, row_norm, packed, slots);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -5,7 +5,12 @@
 // Assignment ([ORBIT] methodology audit: divide by max(norm, 1e-10) when
 // choosing indices): z = RN(u / max(norm, 1e-10f)), idx = first-index
 // argmin |RN(z - c_i)|, decided with the exact switching-point test of
-// threshold.h (q clamped into [2, 4)).  |z| <= sqrt(h) <= 128 for Hadamard
+// threshold.h (q = base + slope * z clamped into [2, 4)).  The slope is
+// 0.99 / R for the smallest power of two R with every threshold inside
+// 0.97 * (-R, R), so that the 128 buckets of q spread over the codebook's
+// own range: the codebooks for rows of many Hadamard blocks are narrow
+// (entries of z have about h/d of the variance of a one-block row).
+// |z| <= sqrt(h) <= 128 for Hadamard
 // blocks of h <= 16384 (|u| <= sqrt(h) * norm), so the distances round at
 // <= 2^-17, far below the smallest centroid gap the fast path accepts.
 // Rows whose norm is not finite, and codebooks that do not qualify, take
@@ -19,9 +24,7 @@ namespace kbit {
 namespace act {
 
 constexpr float kActEps = 1e-10f;
-constexpr float kZRange = 4.0f;               // thresholds must lie inside (-4, 4)
-constexpr float kActSlope = 0.99f / kZRange;  // q = kActBase + kActSlope * z
-constexpr float kActBase = 3.0f + 0x1p-10f;
+constexpr float kActBase = 3.0f + 0x1p-10f;   // q = kActBase + slope * z
 constexpr float kActMinGap = 0x1p-12f;
 constexpr float kQMax = 0x1.fffffep+1f;       // largest float below 4
 
@@ -64,10 +67,16 @@ __device__ __forceinline__ uint32_t nearest16_lds(const float* c, float z) {
     return best;
 }
 
+// Whether the fast path applies, and its slope.
+struct ActPlan {
+    bool fast;
+    float slope;
+};
+
 // Builds T for the codebook cb.  Every thread of the workgroup calls it
 // (nthreads = blockDim.x, a multiple of 64 and at least 128); it holds
-// barriers.  Returns whether the fast path applies.
-__device__ inline bool build_act_tables(ActTables& T, const float* __restrict__ cb, int nthreads) {
+// barriers.
+__device__ inline ActPlan build_act_tables(ActTables& T, const float* __restrict__ cb, int nthreads) {
     const int lane = __lane_id();
     float c[16];
 #pragma unroll
@@ -75,10 +84,21 @@ __device__ inline bool build_act_tables(ActTables& T, const float* __restrict__ 
     bool fast = true;
 #pragma unroll
     for (int i = 1; i < 16; ++i) fast = fast && (c[i] == c[i - 1] || c[i] - c[i - 1] >= kActMinGap);
+    // range R: a power of two (2^-20 .. 2^20) above the largest |threshold|
+    float mmax = 0.0f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        if (c[i] != c[i - 1]) mmax = fmaxf(mmax, fabsf((c[i - 1] + c[i]) * 0.5f));
+    }
+    int ex = 0;
+    (void)frexpf(mmax / 0.97f, &ex);
+    ex = min(max(ex, -20), 20);
+    const float zr = ldexpf(1.0f, ex);
+    const float slope = 0.99f / zr;
 #pragma unroll
     for (int i = 1; i < 16; ++i) {
         const float m = (c[i - 1] + c[i]) * 0.5f;
-        fast = fast && (c[i] == c[i - 1] || (m > -0.97f * kZRange && m < 0.97f * kZRange));
+        fast = fast && (c[i] == c[i - 1] || (m > -0.97f * zr && m < 0.97f * zr));
     }
     if (threadIdx.x == 0) T.fail = 0;
     if (threadIdx.x < 16) T.code[threadIdx.x] = c[threadIdx.x];
@@ -101,7 +121,7 @@ __device__ inline bool build_act_tables(ActTables& T, const float* __restrict__ 
     if (threadIdx.x < 16 && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
-        if (!build_entry<16, false>(c, T.mid, threadIdx.x, kActSlope, kActBase, e)) T.fail = 1;
+        if (!build_entry<16, false>(c, T.mid, threadIdx.x, slope, kActBase, e)) T.fail = 1;
         T.master[threadIdx.x] = e;
     }
     __syncthreads();
@@ -110,23 +130,23 @@ __device__ inline bool build_act_tables(ActTables& T, const float* __restrict__ 
         for (int i = threadIdx.x; i < kBuckets * kCopies; i += nthreads) T.row[i] = T.master[i / kCopies];
     }
     __syncthreads();
-    return fast;
+    return ActPlan{fast, slope};
 }
 
 // Indices of the 16 transformed values v of a row with norm `norm`, as two
 // plane accumulators: bit k of byte j of acc[h] is plane j of element
 // 8h + k.  Every lane of the wave must work on the same row (the finite-norm
 // test is a wave vote).
-__device__ __forceinline__ void assign16(const float (&v)[16], float norm, bool fast, const ActTables& T,
-                                         uint32_t (&acc)[2]) {
+__device__ __forceinline__ void assign16(const float (&v)[16], float norm, const ActPlan& plan,
+                                         const ActTables& T, uint32_t (&acc)[2]) {
     const uint32_t lane_off = static_cast<uint32_t>(__lane_id() & (kCopies - 1)) * 16u;
     const char* tab = reinterpret_cast<const char*>(T.row);
     // max(norm, eps) with a NaN norm kept NaN (fmaxf would drop it)
     const float den = norm < kActEps ? kActEps : norm;
     acc[0] = 0u;
     acc[1] = 0u;
-    if (fast && __builtin_amdgcn_ballot_w64(!(norm < __builtin_inff())) == 0) {
-        const float r = __builtin_amdgcn_rcpf(den) * kActSlope;
+    if (plan.fast && __builtin_amdgcn_ballot_w64(!(norm < __builtin_inff())) == 0) {
+        const float r = __builtin_amdgcn_rcpf(den) * plan.slope;
         const double d64 = static_cast<double>(den);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {

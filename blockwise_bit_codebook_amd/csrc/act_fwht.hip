@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     load_raw(static_cast<int64_t>(blockIdx.x) * kSlots + slot, cur_a, cur_b);
 
     // ---- table build (once per workgroup) ---------------------------------
-    const bool fast = build_act_tables(T, cb, kActThreads);
+    const ActPlan plan = build_act_tables(T, cb, kActThreads);
 
     // Sign flips as XOR masks on the raw bf16 words: element 2i is the low
     // half of word i (sign bit 15), element 2i+1 the high half (bit 31).
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
         // --- assignment and packing: lanes 2g, 2g+1 hold the 32 elements of
         // group g -------------------------------------------------------------
         uint32_t acc[2];
-        assign16(v, norm, fast, T, acc);
+        assign16(v, norm, plan, T, acc);
         {
             const uint2 words = pack_pair(acc, (t & 1) != 0);
             if (valid) {

@@ -134,3 +134,13 @@ def test_block_workloads_full(d, rows):
     # per-token log-uniform scale in [0.1, 10], as the d = 4096 workload
     x, s = synth.activations_bf16(tokens=rows, d=d, seed=d + 3)
     check_act(x, s, scaled_lloyd_max(d), "block workload")
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -12, 2.0 ** -5, 0.3, 3.0, 40.0])
+def test_codebook_ranges(scale):
+    # the bucket range follows the codebook's thresholds; narrow and wide
+    # codebooks take the same exact decisions
+    cb = (codebooks.lloyd_max_normal(16) * np.float32(scale)).astype(np.float32)
+    for d in (4096, 8960):
+        x, s = synth.activations_bf16(tokens=9, d=d, seed=int(d * scale) + 5)
+        check_act(x, s, cb, f"codebook x {scale}")
