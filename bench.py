@@ -90,6 +90,12 @@ def parse(argv=None):
                     help="per-dispatch HBM bytes measured with rocprofv3 counters, if present")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: summarise rocprofv3 output of the profile commands into profiles/")
+    ap.add_argument("--side-only", action="store_true",
+                    help="run only the activation-path and fused-linear cases the side profile covers "
+                         "(eager launches; prints their timings, not the bench line)")
+    ap.add_argument("--side-reps", type=int, default=20, help="rounds per case with --side-only")
+    ap.add_argument("--summarize-side", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarise rocprofv3 output of the side profile commands into profiles/")
     return ap.parse_args(argv)
 
 
@@ -152,13 +158,21 @@ def _csv_rows(d, suffix):
         return list(csv.DictReader(f))
 
 
-def summarize(trace_dir, fetch_dir, write_dir):
+def _summarize_into(table, trace_dir, fetch_dir, write_dir, header, commands, md_name):
     """Per-kernel average duration (kernel trace) and HBM bytes per dispatch
     (FETCH_SIZE / WRITE_SIZE in KiB, each scaled by what the same counter
-    reads for the calibration copies of known size)."""
+    reads for the calibration copies of known size).  table: name ->
+    (substrings of the demangled kernel name, grid size in threads or None,
+    sources, algorithmic bytes per launch).  The entries are merged into
+    profiles/traffic.json and written as a table to profiles/<md_name>."""
     trace = _csv_rows(trace_dir, "kernel_trace.csv")
     counters = {c: _csv_rows(d, "counter_collection.csv") for c, d in (("FETCH_SIZE", fetch_dir),
                                                                         ("WRITE_SIZE", write_dir))}
+
+    def hit(entry, name, grid):
+        pat, g = entry[0], entry[1]
+        return _matches(pat, name) and (g is None or int(grid) == g)
+
     scale = {}
     per_kernel = {}
     for cname, rows in counters.items():
@@ -167,30 +181,31 @@ def summarize(trace_dir, fetch_dir, write_dir):
         cal = cal[-CAL_COPIES:]
         kib = sum(float(r["Counter_Value"]) for r in cal) / len(cal)
         scale[cname] = (CAL_BYTES / 1024.0) / kib
-        for name, (pat, _) in KERNELS.items():
-            vals = [float(r["Counter_Value"]) for r in rows if _matches(pat, r["Kernel_Name"])]
+        for name, entry in table.items():
+            vals = [float(r["Counter_Value"]) for r in rows if hit(entry, r["Kernel_Name"], r["Grid_Size"])]
             per_kernel.setdefault(name, {})[cname] = sum(vals) / len(vals) if vals else None
-    alg = kernel_bytes(ROWS * COLS)
-    out = {"calibration": {"copy_bytes": CAL_BYTES, "copies": CAL_COPIES,
-                           "fetch_scale": round(scale["FETCH_SIZE"], 4),
-                           "write_scale": round(scale["WRITE_SIZE"], 4)},
-           "kernels": {}}
-    lines = ["# rocprofv3 summary: k-bit quantize / dequantize kernels, 8192x8192 bf16, NF4, blocksize 64", "",
-             "The bench step is quantize_kbit_bf16_k4 + dequantize_4bit_nested_bf16; the E4M4-scale pair, "
-             "the plain fp32-scale dequantize and the nested-state encoder (quantize_nested_absmax: "
-             "nested_bins/offset/encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements.",
-             "",
-             "Commands (R = repository root; the counter runs are separate passes):", "", "```"]
-    lines += PROFILE_COMMANDS + ["```", "",
-                                 f"Calibration: the last {CAL_COPIES} device copies of {CAL_BYTES >> 20} MiB each; "
-                                 f"FETCH_SIZE x {scale['FETCH_SIZE']:.3f}, WRITE_SIZE x {scale['WRITE_SIZE']:.3f} "
-                                 "give bytes.", "",
-                                 "| kernel | dispatches | avg us | min us | max us | HBM read MB | HBM write MB "
-                                 "| algorithmic MB | traffic / algorithmic | GB/s (algorithmic) |",
-                                 "|---|---|---|---|---|---|---|---|---|---|"]
-    for name, (pat, srcs) in KERNELS.items():
+    tj = os.path.join(ROOT, "profiles", "traffic.json")
+    out = {"calibration": {}, "kernels": {}}
+    if os.path.exists(tj):
+        with open(tj) as f:
+            out = json.load(f)
+    cal = {"copy_bytes": CAL_BYTES, "copies": CAL_COPIES, "fetch_scale": round(scale["FETCH_SIZE"], 4),
+           "write_scale": round(scale["WRITE_SIZE"], 4)}
+    if "copy_bytes" in out.get("calibration", {}):  # older single-profile layout
+        out["calibration"] = {}
+    out.setdefault("calibration", {})[md_name] = cal
+    lines = header + ["", "Commands (R = repository root; the counter runs are separate passes):", "", "```"]
+    lines += commands + ["```", "",
+                         f"Calibration: the last {CAL_COPIES} device copies of {CAL_BYTES >> 20} MiB each; "
+                         f"FETCH_SIZE x {scale['FETCH_SIZE']:.3f}, WRITE_SIZE x {scale['WRITE_SIZE']:.3f} "
+                         "give bytes.", "",
+                         "| kernel | dispatches | avg us | min us | max us | HBM read MB | HBM write MB "
+                         "| algorithmic MB | traffic / algorithmic | GB/s (algorithmic) |",
+                         "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, entry in table.items():
+        srcs, ab = entry[2], entry[3]
         durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-                if _matches(pat, r["Kernel_Name"])]
+                if hit(entry, r["Kernel_Name"], r["Grid_Size_X"])]
         if not durs or per_kernel[name]["FETCH_SIZE"] is None or per_kernel[name]["WRITE_SIZE"] is None:
             continue
         avg = sum(durs) / len(durs) / 1e3
@@ -198,24 +213,45 @@ def summarize(trace_dir, fetch_dir, write_dir):
         w_kib = per_kernel[name]["WRITE_SIZE"]
         rd = f_kib * 1024 * scale["FETCH_SIZE"]
         wr = w_kib * 1024 * scale["WRITE_SIZE"]
-        ab = alg.get(name)
         out["kernels"][name] = {"avg_us": round(avg, 3), "dispatches": len(durs),
                                 "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
                                 "read_bytes": int(rd), "write_bytes": int(wr), "traffic": int(rd + wr),
-                                "algorithmic_bytes": ab, "source_sha256_16": source_digest(srcs)}
+                                "algorithmic_bytes": ab, "source_sha256_16": source_digest(srcs),
+                                "profile": md_name}
         ratio = f"{(rd + wr) / ab:.3f}" if ab else "—"
         gbs = f"{ab / (avg * 1e-6) / 1e9:.0f}" if ab else "—"
         lines.append(f"| {name} | {len(durs)} | {avg:.2f} | {min(durs) / 1e3:.2f} | {max(durs) / 1e3:.2f} | "
                      f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {ab / 1e6 if ab else 0:.1f} | {ratio} | {gbs} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    with open(tj, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    md = os.path.join(ROOT, "profiles", "kbit_kernels_8192sq_bf16_nf4_b64.md")
-    with open(md, "w") as f:
+    with open(os.path.join(ROOT, "profiles", md_name), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
     return 0
+
+
+def summarize(trace_dir, fetch_dir, write_dir):
+    alg = kernel_bytes(ROWS * COLS)
+    table = {name: (pat, None, srcs, alg.get(name)) for name, (pat, srcs) in KERNELS.items()}
+    header = ["# rocprofv3 summary: k-bit quantize / dequantize kernels, 8192x8192 bf16, NF4, blocksize 64", "",
+              "The bench step is quantize_kbit_bf16_k4 + dequantize_4bit_nested_bf16; the E4M4-scale pair, "
+              "the plain fp32-scale dequantize and the nested-state encoder (quantize_nested_absmax: "
+              "nested_bins/offset/encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements."]
+    return _summarize_into(table, trace_dir, fetch_dir, write_dir, header, PROFILE_COMMANDS,
+                           "kbit_kernels_8192sq_bf16_nf4_b64.md")
+
+
+def summarize_side(trace_dir, fetch_dir, write_dir):
+    header = ["# rocprofv3 summary: activation-path and fused-linear kernels, bf16", "",
+              "Activation assignment (quantize_act_fwht_k4_bf16 / quantize_act_rpbh_k4_bf16) on 4096 rows of "
+              "d = 4096 (dedicated kernel), d = 3840 (Hadamard blocks of 256) and d = 12288 (blocks of 4096), "
+              "with and without a column permutation; fused 4-bit linear (linear_4bit_nested_bf16, NF4 weights "
+              "[N, 4096] with a nested state, B = 64) at M x N = 8 x 4096, 32 x 4096 and 32 x 11008.  Eager "
+              "launches over rotated buffer sets (12 for the activations; > 400 MB of weights for the linear)."]
+    return _summarize_into(side_kernels(), trace_dir, fetch_dir, write_dir, header, SIDE_PROFILE_COMMANDS,
+                           "act_linear_kernels_bf16.md")
 
 
 _CPU_X = None          # the bf16 weight, shared with forked workers
@@ -359,6 +395,47 @@ LINEAR_SHAPES = [(1, 4096, 4096, 26.735), (8, 4096, 4096, 24.748), (32, 4096, 40
                  (32, 11008, 4096, 61.726)]
 
 
+# The side profile: one case per (kernel, grid) so that the trace can tell
+# them apart.  (rows, d, permutation) and (M, N, K).
+SIDE_ACT_CASES = [(4096, 4096, False), (4096, 3840, False), (4096, 3840, True), (4096, 12288, False),
+                  (4096, 12288, True)]
+SIDE_LINEAR_SHAPES = [(8, 4096, 4096), (32, 4096, 4096), (32, 11008, 4096)]
+_A_SRC = ["blockwise_bit_codebook_amd/csrc/act_fwht.hip", "blockwise_bit_codebook_amd/csrc/act_common.h",
+          "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/device.h"]
+_AB_SRC = ["blockwise_bit_codebook_amd/csrc/act_block.hip", "blockwise_bit_codebook_amd/csrc/act_common.h",
+           "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/device.h"]
+_L_SRC = ["blockwise_bit_codebook_amd/csrc/linear.hip", "blockwise_bit_codebook_amd/csrc/device.h"]
+SIDE_PROFILE_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/side_trace -o trace -- "
+    "python3 $R/bench.py --side-only --side-reps 20 --copy-calibration",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/side_fetch -o fetch -- "
+    "python3 $R/bench.py --side-only --side-reps 1 --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/side_write -o write -- "
+    "python3 $R/bench.py --side-only --side-reps 1 --copy-calibration",
+    "cd $R && python3 bench.py --summarize-side gpurun_out/side_trace gpurun_out/side_fetch gpurun_out/side_write",
+]
+
+
+def side_kernels():
+    """name -> (name substrings, grid size in threads or None, sources, algorithmic bytes per launch)."""
+    t = {}
+    for rows, d, perm in SIDE_ACT_CASES:
+        h = d & -d
+        if d == 4096 and not perm:
+            t[f"act_fwht {rows}x{d}"] = (("::act_fwht_kernel<2>",), None, _A_SRC, act_bytes(rows, d))
+        else:
+            L = h.bit_length() - 1
+            name = f"act_block {rows}x{d} h={h}" + (" perm" if perm else "")
+            t[name] = ((f"::act_block_kernel<{L}, {'true' if perm else 'false'}>",), None, _AB_SRC,
+                       act_bytes(rows, d) + (4 * d if perm else 0))
+    for M, N, Kd in SIDE_LINEAR_SHAPES:
+        mt = 1 if M <= 16 else 2 if M <= 32 else 4
+        t[f"linear_4bit_nested {M}x{N}x{Kd}"] = (("::linear4_kernel<", f"LinNested, {mt}>"), (N // 16) * 1024,
+                                                 _L_SRC, linear_bytes(M, N, Kd))
+    return t
+
+
 def linear_bytes(M, N, K):
     """Minimum bytes of one fused linear call with a nested state (B = 64):
     packed weights, codes, group absmax, map and codebook, X and out."""
@@ -366,7 +443,7 @@ def linear_bytes(M, N, K):
     return N * K // 2 + nb + 4 * (-(-nb // GROUP2)) + 4 * 256 + 64 + 2 * M * K + 2 * M * N
 
 
-def bench_linear(torch, kb, synth, dev, reps=20):
+def bench_linear(torch, kb, synth, dev, reps=20, shapes=None, eager=False):
     """Fused 4-bit linear (nested state) at the page's shapes.  Each timed
     call uses a different weight set (rotated through > 400 MB, beyond the
     last-level cache); the launches are captured in a HIP graph so that
@@ -374,7 +451,7 @@ def bench_linear(torch, kb, synth, dev, reps=20):
     cb = torch.from_numpy(kb.codebook_nf(K)).to(dev)
     q = torch.from_numpy(kb.dynamic_map8()).to(dev)
     res = []
-    for M, N, Kd, page_us in LINEAR_SHAPES:
+    for M, N, Kd, page_us in (LINEAR_SHAPES if shapes is None else [(*sh, None) for sh in shapes]):
         nb = N * Kd // BLOCK
         nbytes = linear_bytes(M, N, Kd)
         sets = int(min(64, max(2, -(-(400 << 20) // nbytes))))
@@ -411,9 +488,22 @@ def bench_linear(torch, kb, synth, dev, reps=20):
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) * 1e3 / (reps * len(items))
 
-        us = timed(bufs)
-        warm = timed([bufs[0]] * sets)
-        res.append({"M": M, "N": N, "K": Kd, "avg_us": round(us, 3), "warm_avg_us": round(warm, 3),
+        if eager:
+            # plain launches (what the side profile traces)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                for b in bufs:
+                    call(b)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(bufs))
+            warm = None
+        else:
+            us = timed(bufs)
+            warm = timed([bufs[0]] * sets)
+        warm = None if warm is None else round(warm, 3)
+        res.append({"M": M, "N": N, "K": Kd, "avg_us": round(us, 3), "warm_avg_us": warm,
                     "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
                     "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                     "TFLOP/s": round(2.0 * M * N * Kd / (us * 1e-6) / 1e12, 3),
@@ -426,10 +516,37 @@ def bench_linear(torch, kb, synth, dev, reps=20):
             "note": "page_candidate_us: the page's fused dequantize + linear medians on its own GPU, context only"}
 
 
+def side_only(args):
+    """The side profile's workload: the activation cases, then the linear
+    shapes, eagerly launched; then the calibration copies if asked."""
+    import torch
+    import blockwise_bit_codebook_amd as kb
+    from blockwise_bit_codebook_amd import synth
+    dev = torch.device("cuda:0")
+    out = {"act": [], "linear": None}
+    for rows, d, perm in SIDE_ACT_CASES:
+        r = bench_act(torch, kb, synth, dev, args.side_reps, rows=rows, d=d, perm=perm)
+        out["act"].append(r)
+        print(f"[side] act {rows}x{d} perm={perm}: {r['avg_us']} us", file=sys.stderr, flush=True)
+    out["linear"] = bench_linear(torch, kb, synth, dev, reps=args.side_reps, shapes=SIDE_LINEAR_SHAPES, eager=True)
+    print("[side] linear done", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        src = torch.zeros(CAL_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(CAL_COPIES):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps(out))
+    return 0
+
+
 def main(argv=None):
     args = parse(argv)
     if args.summarize:
         return summarize(*args.summarize)
+    if args.summarize_side:
+        return summarize_side(*args.summarize_side)
     if args.steps % args.sets:
         print(f"--steps ({args.steps}) must be a multiple of --sets ({args.sets})", file=sys.stderr)
         return 2
@@ -437,6 +554,9 @@ def main(argv=None):
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the hot path has no "
               "cross-GPU step to measure here.", file=sys.stderr)
         return 2
+
+    if args.side_only:
+        return side_only(args)
 
     # the CPU oracle runs first: its workers are forked before any GPU work
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
