@@ -143,7 +143,8 @@ __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, flo
 #pragma unroll
     for (int t = 7; t >= 0; --t) {
         const Decision d = decide(x[t], __builtin_fmaf(x[t], r, kBase), s64, tab, lane_off);
-        out.acc = (out.acc << 1) | (d.up ? d.e[3] : d.e[2]);
+        const uint32_t sel = d.up ? d.e[3] : d.e[2];
+        out.acc = t == 7 ? sel : shl1_or(out.acc, sel);
         if constexpr (K == 5) out.acc4 = (out.acc4 << 1) | ((d.e[0] >> (d.up ? 1 : 0)) & 1u);
     }
     return out;
