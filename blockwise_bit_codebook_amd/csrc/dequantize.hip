@@ -35,12 +35,14 @@ namespace {
 // Per-lane block scale in two steps, so that its global loads can be issued
 // a step ahead: load() gathers what the block's scale is built from,
 // finish() builds it.
+// load(b, g): b is the lane's block, g the group of 256 blocks of the wave's
+// tile (wave-uniform: a tile's 512 elements never straddle a group for B >= 2).
 struct PlainScale {
     const float* absmax;
     struct Raw {
         float a;
     };
-    __device__ Raw load(int64_t b) const { return Raw{absmax[b]}; }
+    __device__ Raw load(int64_t b, int64_t) const { return Raw{absmax[b]}; }
     __device__ float finish(const Raw& r) const { return r.a; }
 };
 
@@ -50,11 +52,12 @@ struct E4m4Scale {
     struct Raw {
         uint32_t c;
     };
-    __device__ Raw load(int64_t b) const { return Raw{code[b]}; }
+    __device__ Raw load(int64_t b, int64_t) const { return Raw{code[b]}; }
     __device__ float finish(const Raw& r) const { return e4m4_decode(r.c); }
 };
 
-// Nested scale rebuild.  qmap2 is staged in LDS by the kernel prologue.
+// Nested scale rebuild.  qmap2 is staged in LDS by the kernel prologue; the
+// group absmax is one scalar load per tile.
 struct NestedScale {
     const uint8_t* code;
     const float* absmax2;
@@ -64,7 +67,14 @@ struct NestedScale {
         uint32_t code;
         float a2;
     };
-    __device__ Raw load(int64_t b) const { return Raw{code[b], absmax2[b >> 8]}; }
+    // The group absmax, one per step, goes through a buffer load (a vector
+    // memory op counted by vmcnt).  As a scalar load it would share lgkmcnt
+    // with the LDS reads, and their waits would also wait for the prefetch.
+    __amdgpu_buffer_rsrc_t absmax2_rsrc;
+    __device__ Raw load(int64_t b, int64_t g) const {
+        const uint32_t a = __builtin_amdgcn_raw_buffer_load_b32(absmax2_rsrc, 0, static_cast<int>(g) * 4, 0);
+        return Raw{code[b], __uint_as_float(a)};
+    }
     __device__ float finish(const Raw& r) const {
 #pragma clang fp contract(off)
         const float prod = qmap_lds[r.code] * r.a2;
@@ -81,9 +91,10 @@ struct TileIn {
     typename Scale::Raw sc;
 };
 
+// g: the tile's group of 256 blocks (wave-uniform).
 template <int K, class Scale, bool FULL>
 __device__ __forceinline__ TileIn<K, Scale> load_tile(const uint32_t* __restrict__ packed, const Scale& scale,
-                                                      int64_t tile, int64_t n, int log2B, int lane) {
+                                                      int64_t tile, int64_t g2, int64_t n, int log2B, int lane) {
     TileIn<K, Scale> in;
     const int64_t base = tile * kWaveTile;
     const int64_t g = base / kGroup + (lane >> 2);
@@ -94,7 +105,7 @@ __device__ __forceinline__ TileIn<K, Scale> load_tile(const uint32_t* __restrict
     if constexpr (K == 5) {
         if (l == 0 && g_ok) in.w4 = packed[g * K + 4];
     }
-    in.sc = scale.load((FULL || e0 < n ? e0 : 0) >> log2B);
+    in.sc = scale.load((FULL || e0 < n ? e0 : 0) >> log2B, g2);
     return in;
 }
 
@@ -145,15 +156,19 @@ __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packe
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerGroup;
     const int64_t nfull = n / (static_cast<int64_t>(kWaveTile) * U);  // full steps
     int64_t st = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    // a step's U tiles (2048 elements) lie in one group of 256 blocks (B >= 8)
+    auto step_group = [&](int64_t step) { return (step * U * kWaveTile) >> (log2B + 8); };
     if (st < nfull) {
         TileIn<K, Scale> cur[U];
+        const int64_t g0 = step_group(st);
 #pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = load_tile<K, Scale, true>(packed, scale, st * U + u, n, log2B, lane);
+        for (int u = 0; u < U; ++u) cur[u] = load_tile<K, Scale, true>(packed, scale, st * U + u, g0, n, log2B, lane);
         for (; st < nfull; st += nwaves) {
             const int64_t sn = min(st + nwaves, nfull - 1);
+            const int64_t gn = step_group(sn);
             TileIn<K, Scale> nxt[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) nxt[u] = load_tile<K, Scale, true>(packed, scale, sn * U + u, n, log2B, lane);
+            for (int u = 0; u < U; ++u) nxt[u] = load_tile<K, Scale, true>(packed, scale, sn * U + u, gn, n, log2B, lane);
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 decode_tile<E, K, Scale, true, NTS>(cur[u], scale, cb_lds, pair_lds, out, st * U + u, n, lane);
@@ -165,7 +180,8 @@ __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packe
     const int64_t ntiles = (n + kWaveTile - 1) / kWaveTile;
     for (int64_t t = nfull * U + static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave; t < ntiles;
          t += nwaves) {
-        const TileIn<K, Scale> in = load_tile<K, Scale, false>(packed, scale, t, n, log2B, lane);
+        const TileIn<K, Scale> in =
+            load_tile<K, Scale, false>(packed, scale, t, (t * kWaveTile) >> (log2B + 8), n, log2B, lane);
         decode_tile<E, K, Scale, false, false>(in, scale, cb_lds, pair_lds, out, t, n, lane);
     }
 }
@@ -208,8 +224,12 @@ __global__ __launch_bounds__(kThreads) void dequantize_nested_kernel(
     stage_codebook<4>(cb, cb_lds, pair_lds);
     qmap_lds[threadIdx.x] = qmap2[threadIdx.x];
     __syncthreads();
+    // buffer descriptor over the ceil(ceil(n / B) / 256) group scales
+    const int64_t ng = (((n + (int64_t(1) << log2B) - 1) >> log2B) + 255) >> 8;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(absmax2), 0, static_cast<int>(ng * 4), 0x00020000);
     dequant_tiles<E, 4, NestedScale, U, NTS>(packed, cb_lds, pair_lds,
-                                                        NestedScale{code, absmax2, offset, qmap_lds}, out, n,
+                                                        NestedScale{code, absmax2, offset, qmap_lds, rsrc}, out, n,
                                                         log2B);
 }
 
