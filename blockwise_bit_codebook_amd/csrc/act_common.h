@@ -155,7 +155,8 @@ __device__ __forceinline__ void assign16(const float (&v)[16], float norm, const
                 const float z = v[8 * h + k];
                 const float q = __builtin_amdgcn_fmed3f(__builtin_fmaf(z, r, kActBase), 2.0f, kQMax);
                 const Decision d = decide(z, q, d64, tab, lane_off);
-                acc[h] = (acc[h] << 1) | (d.up ? d.e[3] : d.e[2]);
+                const uint32_t sel = d.up ? d.e[3] : d.e[2];
+                acc[h] = k == 7 ? sel : shl1_or(acc[h], sel);
             }
         }
     } else {
