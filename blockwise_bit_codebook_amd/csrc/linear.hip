@@ -18,10 +18,16 @@
 // operand of v_mfma_f32_16x16x32_bf16 (lane l: 8 consecutive k of channel
 // n0 + l % 16, which are one byte of each of the group's 4 plane words), and
 // runs one MFMA per 16 rows of X with that operand (1, 2 or 4 row tiles per
-// pass, from M).  The loads of four steps are issued together, and the
-// next four steps' loads go out before the current ones are decoded.  The 16 partial tiles are added in LDS in wave order, so the
-// result does not depend on scheduling.  The kernel is bound by reading the
-// packed weights when M is small.
+// pass, from M).  Weights come four steps at a time: lane (nn, q) loads the
+// 16 bytes of step s + q of its channel, so each channel's 64 bytes are one
+// contiguous piece of the load (per-step loads would touch every channel's
+// cache line four times for 16 bytes each, and the address unit, not HBM,
+// would set the pace).  A byte transpose in each lane and two cross-row swaps
+// (v_permlane32_swap, v_permlane16_swap) then give lane (nn, q) byte q of
+// each plane word of every step.  The next four steps' loads go out before
+// the current ones are decoded, and the first four steps' before the
+// prologue's barrier.  The 16 partial tiles are added in LDS in wave order,
+// so the result does not depend on scheduling.
 #include "device.h"
 #include "kbit_internal.h"
 #include "launch.h"
@@ -63,21 +69,43 @@ struct LinNested {
     }
 };
 
-// The loads of one chunk of kU = 4 consecutive k steps: the 4 plane words of
-// each step's group, the raw scale of step s + q of channel nn (lane (nn,
-// q); the lanes take each step's scale from there), and, for a single row
-// tile, the step's 8 values of X.
+// The loads of one chunk of kU = 4 consecutive k steps, all for step s + q
+// of channel nn in lane (nn, q): the 4 plane words of that step's group and
+// its raw scale; and, for a single row tile, each step's 8 values of X.
 constexpr int kU = 4;
 template <class Scale, bool XAHEAD>
 struct Chunk {
-    u32x4 wd[kU];
+    u32x4 wd;
     typename Scale::Raw raw;
     u32x4 xa[XAHEAD ? kU : 1];
 };
 
-// MT: 16-row tiles of X per pass.  Chunks are double-buffered: the next
-// chunk's loads are issued before the current one is decoded, and the
-// first chunk's before the prologue's barrier.
+// Lane (nn, q) holds the plane words w[0..3] of step s + q.  Returns in t[u]
+// the plane bytes of its own 8 k of step s + u: byte j = byte q of plane
+// word j of that step.  All 64 lanes must take part.
+__device__ __forceinline__ void chunk_plane_bytes(const u32x4& w, uint32_t (&t)[kU]) {
+    // in-lane 4 x 4 byte transpose: o[c] = byte c of w[0], w[1], w[2], w[3]
+    const uint32_t a01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+    const uint32_t b01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+    const uint32_t a23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t b23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    uint32_t o0 = __builtin_amdgcn_perm(a23, a01, 0x05040100u);
+    uint32_t o1 = __builtin_amdgcn_perm(a23, a01, 0x07060302u);
+    uint32_t o2 = __builtin_amdgcn_perm(b23, b01, 0x05040100u);
+    uint32_t o3 = __builtin_amdgcn_perm(b23, b01, 0x07060302u);
+    // across the rows of 16 lanes (row = q): row r, register c -> row c,
+    // register r (swap row halves, then odd/even rows)
+    auto s02 = __builtin_amdgcn_permlane32_swap(o0, o2, false, false);
+    auto s13 = __builtin_amdgcn_permlane32_swap(o1, o3, false, false);
+    auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    t[0] = s01[0];
+    t[1] = s01[1];
+    t[2] = s23[0];
+    t[3] = s23[1];
+}
+
+// MT: 16-row tiles of X per pass.  Chunks are double-buffered (see above).
 template <class Scale, int MT>
 __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __restrict__ X, int64_t M, int K,
                                                               const uint32_t* __restrict__ packed,
@@ -98,17 +126,18 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
     const bool n_ok = n < N;
     const int T = K / kGroup;  // 32-wide k steps
     const int s_begin = wave * T / kLinWaves, s_end = (wave + 1) * T / kLinWaves;
-    const uint32_t sh = 8u * static_cast<uint32_t>(q);
 
     auto load_chunk = [&](int s, int64_t m0, C& c) {
         c.raw = typename Scale::Raw{};
-        if (n_ok && s + q < s_end) c.raw = sc.load((static_cast<int64_t>(n) * K + (s + q) * kGroup) >> log2B);
+        c.wd = u32x4{0u, 0u, 0u, 0u};
+        if (n_ok && s + q < s_end) {
+            c.raw = sc.load((static_cast<int64_t>(n) * K + (s + q) * kGroup) >> log2B);
+            c.wd = load16<false>(packed + (static_cast<int64_t>(n) * T + s + q) * 4);
+        }
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int step = s + u;
             const bool live = step < s_end;  // wave-uniform
-            c.wd[u] = u32x4{0u, 0u, 0u, 0u};
-            if (live && n_ok) c.wd[u] = load16<false>(packed + (static_cast<int64_t>(n) * T + step) * 4);
             if constexpr (kXAhead) {
                 const int64_t row = m0 + nn;
                 c.xa[u] = u32x4{0u, 0u, 0u, 0u};
@@ -136,13 +165,12 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
 
         auto compute = [&](int s, const C& c) {
             const float my_scale = n_ok ? sc.finish(c.raw, qmap_lds) : 0.0f;
+            uint32_t planes[kU];
+            chunk_plane_bytes(c.wd, planes);
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 if (s + u >= s_end) break;  // wave-uniform
-                // byte q of each plane word -> plane bytes of the lane's 8 k
-                const uint32_t p = ((c.wd[u][0] >> sh) & 0xFFu) | (((c.wd[u][1] >> sh) & 0xFFu) << 8) |
-                                   (((c.wd[u][2] >> sh) & 0xFFu) << 16) | (((c.wd[u][3] >> sh) & 0xFFu) << 24);
-                const uint32_t pr = planes_to_pairs(p);
+                const uint32_t pr = planes_to_pairs(planes[u]);
                 const float scale = __shfl(my_scale, u * 16 + nn);
                 u32x4 wv;
 #pragma unroll
