@@ -133,7 +133,13 @@ __device__ __forceinline__ Codes classify_exact(const float* c, const float (&x)
 }
 
 
-template <int K>
+// Whether the table holds switching points in the fp32 pair form (decide32):
+// 16-bit inputs, whose values and block maxima have at most 11 significant
+// bits.  K = 5 keeps the fp64 form, whose low bits carry the plane-4 flags.
+template <class E, int K>
+constexpr bool kPairForm = !std::is_same<E, Fp32>::value && K <= 4;
+
+template <class E, int K>
 __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, float r, const char* tab,
                                                uint32_t lane_off) {
     Codes out;
@@ -142,7 +148,8 @@ __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, flo
     // so element t ends at bit t of every plane byte.
 #pragma unroll
     for (int t = 7; t >= 0; --t) {
-        const Decision d = decide(x[t], __builtin_fmaf(x[t], r, kBase), s64, tab, lane_off);
+        const float q = __builtin_fmaf(x[t], r, kBase);
+        const Decision d = kPairForm<E, K> ? decide32(x[t], q, s, tab, lane_off) : decide(x[t], q, s64, tab, lane_off);
         const uint32_t sel = d.up ? d.e[3] : d.e[2];
         out.acc = t == 7 ? sel : shl1_or(out.acc, sel);
         if constexpr (K == 5) out.acc4 = (out.acc4 << 1) | ((d.e[0] >> (d.up ? 1 : 0)) & 1u);
@@ -158,9 +165,14 @@ __device__ __forceinline__ void encode_row(bool fast, const Tables& T, const cha
                                            uint32_t lane_off, int lane, const float (&x)[8], float m,
                                            int64_t row_base, int64_t n, uint32_t* __restrict__ packed) {
     const float s = __builtin_elementwise_maximum(m, kAbsmaxEps);  // NaN stays NaN (exact path)
+    // The pair form needs s = m (a 16-bit value); a clamped s = 1e-8f is
+    // fine only for an all-zero block, whose x = 0 decides every threshold
+    // by a wide margin.
+    const bool lane_ok = kPairForm<E, K> ? (s < kMaxFastScale && (m >= kAbsmaxEps || m == 0.0f))
+                                         : (s < kMaxFastScale);
     Codes cd;
-    if (fast && !__builtin_amdgcn_ballot_w64(!(s < kMaxFastScale))) {
-        cd = classify_fast<K>(x, s, __builtin_amdgcn_rcpf(s) * kSlope, tab, lane_off);
+    if (fast && !__builtin_amdgcn_ballot_w64(!lane_ok)) {
+        cd = classify_fast<E, K>(x, s, __builtin_amdgcn_rcpf(s) * kSlope, tab, lane_off);
     } else {
         cd = classify_exact<K>(T.code, x, s);
     }
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     for (int i = wave + 1; i < C; i += kWaves_) {
         const float lo = cb[i - 1], hi = cb[i];  // wave-uniform
         uint64_t m = 0;
-        if (fast && lo != hi && !threshold_mid_wave(lo, hi, m)) m = kNoMid;
+        if (fast && lo != hi && !threshold_mid_wave<kPairForm<E, K>>(lo, hi, m)) m = kNoMid;
         if (lane == 0) T.mid[i] = m;
     }
     if (threadIdx.x == 0) T.mid[0] = 0;

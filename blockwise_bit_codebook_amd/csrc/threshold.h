@@ -69,6 +69,25 @@ __device__ inline uint64_t mid_bits(float u, float p) {
     return b & ~static_cast<uint64_t>(3u);
 }
 
+// The same switching point as two fp32 values {Mh, Ml'} (low word Mh): M =
+// Mh + Ml exactly with Mh = p and Ml = (u - p) / 2 (a power of two), and
+// Ml' = Ml nudged by one fp32 ulp the way mid_bits nudges M.  For x and s
+// with at most 11 significant bits (bf16 and fp16 values) the sign of
+// fma(-Ml', s, fma(-Mh, s, x)) is the sign of x - M*s: the inner fma is
+// exact whenever |x - Mh*s| is small enough to matter, and otherwise that
+// difference is far larger than Ml*s.  (Exact ties x/s == M cannot occur
+// for such x and s, since M has 25 significant bits.)  Returns kNoMid when
+// Ml would fall below 2^-100.
+__device__ inline uint64_t pair_bits(float u, float p) {
+    const float ml = static_cast<float>((static_cast<double>(u) - static_cast<double>(p)) * 0.5);
+    if (!(ml >= 0x1p-100f)) return kNoMid;
+    const double M = (static_cast<double>(u) + static_cast<double>(p)) * 0.5;
+    const bool tie_up = static_cast<float>(M) == u;
+    const uint32_t mlb = __float_as_uint(ml);
+    const uint32_t ml2 = tie_up ? mlb - 1u : mlb + 1u;  // M down (ties up) or up (ties down)
+    return static_cast<uint64_t>(__float_as_uint(p)) | (static_cast<uint64_t>(ml2) << 32);
+}
+
 // M for the threshold between codes lo < hi, found by a group of G lanes
 // (G = 32 or 64; lane group lane / G searches its own lo, hi).  The choice
 // is monotone in x_n on [lo, hi], so u is found by searching the fp32
@@ -81,7 +100,7 @@ __device__ inline uint64_t mid_bits(float u, float p) {
 // until every group of the wave is done, so all lanes of the wave must
 // call it; each lane gets its group's result.  Returns false if the bracket
 // is not as expected.
-template <int G>
+template <int G, bool PAIR32 = false>
 __device__ inline bool threshold_mid_group(float lo, float hi, uint64_t& bits) {
     static_assert(G == 32 || G == 64, "lane groups of 32 or 64");
     const uint32_t lane = __lane_id();
@@ -133,13 +152,19 @@ __device__ inline bool threshold_mid_group(float lo, float hi, uint64_t& bits) {
             }
         }
     }
-    bits = mid_bits(from_key(R), from_key(L));
-    return ok;
+    if constexpr (PAIR32) {
+        bits = pair_bits(from_key(R), from_key(L));
+        return ok && bits != kNoMid;
+    } else {
+        bits = mid_bits(from_key(R), from_key(L));
+        return ok;
+    }
 }
 
 // The same with the whole wave on one threshold.
+template <bool PAIR32 = false>
 __device__ inline bool threshold_mid_wave(float lo, float hi, uint64_t& bits) {
-    return threshold_mid_group<64>(lo, hi, bits);
+    return threshold_mid_group<64, PAIR32>(lo, hi, bits);
 }
 
 // Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
@@ -191,6 +216,17 @@ __device__ __forceinline__ Decision decide(float x, float q, double s64, const c
     d.e = *reinterpret_cast<const u32x4*>(tab + entry_addr(q, lane_off));
     const double M = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(d.e[1]) << 32) | d.e[0]));
     d.up = __builtin_fma(-M, s64, static_cast<double>(x)) > 0.0;
+    return d;
+}
+
+// The same with entries in the pair form (pair_bits), for x and s of at
+// most 11 significant bits: two fp32 fmas instead of a conversion, an fp64
+// fma and an fp64 compare.
+__device__ __forceinline__ Decision decide32(float x, float q, float s, const char* tab, uint32_t lane_off) {
+    Decision d;
+    d.e = *reinterpret_cast<const u32x4*>(tab + entry_addr(q, lane_off));
+    const float t1 = __builtin_fmaf(-__uint_as_float(d.e[0]), s, x);
+    d.up = __builtin_fmaf(-__uint_as_float(d.e[1]), s, t1) > 0.0f;
     return d;
 }
 
