@@ -5,9 +5,10 @@ blocksize 64) followed by the nested 4-bit dequantize of those planes back to
 bf16 (per-block scales rebuilt from 8-bit codes over groups of 256 plus a
 mean offset), on an 8192 x 8192 weight drawn from N(0, 0.02).  Inputs live in
 HBM before timing starts.  Several buffer sets are rotated so that the
-256 MB last-level cache cannot hold a step's working set.  One step per
-buffer set is captured into a single HIP graph and the timed loop replays
-it (steps must be a multiple of the number of sets).
+256 MB last-level cache cannot hold a step's working set.  Rounds of steps
+over the buffer sets (up to 32 steps) are captured into a HIP graph, a
+second graph holds the remainder, and the timed loop replays them: exactly
+--steps steps, warmed up by --warmup eager steps.
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (read +
 written by both kernels) divided by the wall time per step, in GB/s.
@@ -547,8 +548,8 @@ def main(argv=None):
         return summarize(*args.summarize)
     if args.summarize_side:
         return summarize_side(*args.summarize_side)
-    if args.steps % args.sets:
-        print(f"--steps ({args.steps}) must be a multiple of --sets ({args.sets})", file=sys.stderr)
+    if args.steps < 1 or args.sets < 1 or args.warmup < 0:
+        print("--steps and --sets must be positive, --warmup non-negative", file=sys.stderr)
         return 2
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the hot path has no "
@@ -631,11 +632,16 @@ def main(argv=None):
                 fn(s_)
         return g
 
-    # One graph holds one step per buffer set (quantize, nested dequantize,
-    # then the next set), so a replay is args.sets steps.
-    g_steps = capture(step, sets)
-    for i in range(-(-args.warmup // args.sets)):
-        g_steps.replay()
+    # A graph holds whole rounds over the buffer sets (quantize, nested
+    # dequantize, then the next set), up to 32 steps, so that one replay
+    # covers many steps; a second graph holds the remaining steps (starting
+    # again at set 0).  Exactly args.steps steps are timed.
+    per_graph = min(args.steps // args.sets, max(1, 32 // args.sets)) * args.sets
+    full, rest = (args.steps // per_graph, args.steps % per_graph) if per_graph else (0, args.steps)
+    g_steps = capture(step, [sets[i % args.sets] for i in range(per_graph)]) if full else None
+    g_rest = capture(step, [sets[i % args.sets] for i in range(rest)]) if rest else None
+    for i in range(args.warmup):
+        step(sets[i % args.sets])
     torch.cuda.synchronize()
 
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -643,8 +649,10 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps // args.sets):
+    for i in range(full):
         g_steps.replay()
+    if g_rest is not None:
+        g_rest.replay()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
