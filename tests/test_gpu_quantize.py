@@ -120,6 +120,61 @@ def test_near_thresholds_fp32(cbname, K, B):
     check_quantize(x, "fp32", cb, K, B, f"near {cbname}")
 
 
+def _near_threshold_16bit(cb, B, nblocks, dtype, seed, jitter=3):
+    """16-bit blocks whose first element is the absmax a (a 16-bit value)
+    and whose other elements are the 16-bit values within a few steps of
+    (midpoint of neighbouring codes) * a: the inputs that decide each
+    threshold by the narrowest margins."""
+    rng = np.random.default_rng(seed)
+    c = np.unique(cb.astype(np.float64))
+    mids = (c[:-1] + c[1:]) / 2
+
+    def to16(v):
+        return numerics.to_bf16_bits(v) if dtype == "bf16" else numerics.to_fp16(v).view(np.uint16)
+
+    out = np.empty(nblocks * B, np.uint16)
+    for b in range(nblocks):
+        a16 = to16(np.float32(rng.uniform(0.01, 100.0)))
+        a = numerics.widen(np.array([a16], np.uint16) if dtype == "bf16" else np.array([a16]).view(np.float16),
+                           dtype)[0]
+        m = mids[rng.integers(0, mids.size, B - 1)]
+        v = to16((m * np.float64(a)).astype(np.float32)).astype(np.int64)
+        # step through neighbouring 16-bit values (sign-magnitude bits)
+        steps = rng.integers(-jitter, jitter + 1, B - 1)
+        mag = np.clip((v & 0x7FFF) + steps, 0, int(a16) & 0x7FFF)
+        blk = ((v & 0x8000) | mag).astype(np.uint16)
+        sign = 0x8000 if rng.random() < 0.5 else 0
+        out[b * B] = np.uint16(int(a16) | sign)
+        out[b * B + 1:(b + 1) * B] = blk
+    return out if dtype == "bf16" else out.view(np.float16)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("cbname,K", [("nf", 2), ("nf", 3), ("nf", 4), ("nf", 5), ("fp4", 4), ("pages", 4),
+                                      ("linspace", 4)])
+def test_near_thresholds_16bit(dtype, cbname, K):
+    # the fp32 two-fma threshold decision (16-bit inputs, K <= 4) and the fp64
+    # one (K = 5) against the oracle's division, at the narrowest margins
+    cb = _cb(cbname, K)
+    x = _near_threshold_16bit(cb, 64, 600, dtype, seed=K * 7 + len(cbname))
+    check_quantize(x, dtype, cb, K, 64, f"near16 {cbname}")
+
+
+def test_tiny_blocks_16bit():
+    # blocks with 0 < absmax < 1e-8 divide by the clamp 1e-8f (24 significant
+    # bits), which the fp32 decision does not cover: they take the exact path;
+    # all-zero blocks stay on the fast path
+    cb = codebooks.nf(4)
+    x = synth.normal(64 * 64, seed=5, dtype="fp32")
+    for b in range(0, 64, 4):
+        x[b * 64:(b + 1) * 64] *= np.float32(10.0 ** -(9 + b / 8))
+    x[3 * 64:4 * 64] = 0.0
+    xb = numerics.to_bf16_bits(x)
+    check_quantize(xb, "bf16", cb, 4, 64, "tiny bf16")
+    xh = numerics.to_fp16(x * np.float32(1e4))    # fp16 cannot hold 1e-9: scale into its subnormals
+    check_quantize(xh, "fp16", cb, 4, 64, "tiny fp16")
+
+
 def test_special_values():
     cb = codebooks.nf(4)
     x = synth.normal(64 * 40, seed=3, dtype="fp32")
