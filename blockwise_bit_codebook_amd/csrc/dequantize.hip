@@ -109,13 +109,13 @@ __device__ __forceinline__ TileIn<K, Scale> load_tile(const uint32_t* __restrict
     return in;
 }
 
+// s: the lane's block scale (Scale::finish of in.sc).
 template <class E, int K, class Scale, bool FULL, bool NTS>
-__device__ __forceinline__ void decode_tile(const TileIn<K, Scale>& in, const Scale& scale, const float* cb_lds,
+__device__ __forceinline__ void decode_tile(const TileIn<K, Scale>& in, float s, const float* cb_lds,
                                             const float2* pair_lds, typename E::storage* __restrict__ out,
                                             int64_t tile, int64_t n, int lane) {
     const int64_t e0 = tile * kWaveTile + static_cast<int64_t>(lane) * kElemsPerLane;
     const uint32_t p = quad_transpose_bytes(in.w, lane);
-    const float s = scale.finish(in.sc);
     float v[kElemsPerLane];
     if constexpr (K <= 4) {
         const uint32_t pr = planes_to_pairs(p);
@@ -158,11 +158,17 @@ __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packe
     int64_t st = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave;
     // a step's U tiles (2048 elements) lie in one group of 256 blocks (B >= 8)
     auto step_group = [&](int64_t step) { return (step * U * kWaveTile) >> (log2B + 8); };
+    // Each step's block scales are built right after the previous step's
+    // stores go out, so that their lookups (the nested map in LDS) are off
+    // the next step's critical path.
     if (st < nfull) {
         TileIn<K, Scale> cur[U];
+        float cs[U];
         const int64_t g0 = step_group(st);
 #pragma unroll
         for (int u = 0; u < U; ++u) cur[u] = load_tile<K, Scale, true>(packed, scale, st * U + u, g0, n, log2B, lane);
+#pragma unroll
+        for (int u = 0; u < U; ++u) cs[u] = scale.finish(cur[u].sc);
         for (; st < nfull; st += nwaves) {
             const int64_t sn = min(st + nwaves, nfull - 1);
             const int64_t gn = step_group(sn);
@@ -171,9 +177,12 @@ __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packe
             for (int u = 0; u < U; ++u) nxt[u] = load_tile<K, Scale, true>(packed, scale, sn * U + u, gn, n, log2B, lane);
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                decode_tile<E, K, Scale, true, NTS>(cur[u], scale, cb_lds, pair_lds, out, st * U + u, n, lane);
+                decode_tile<E, K, Scale, true, NTS>(cur[u], cs[u], cb_lds, pair_lds, out, st * U + u, n, lane);
 #pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+            for (int u = 0; u < U; ++u) {
+                cur[u] = nxt[u];
+                cs[u] = scale.finish(nxt[u].sc);
+            }
         }
     }
     // tiles after the last full step: one wave tile per wave
@@ -182,7 +191,7 @@ __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packe
          t += nwaves) {
         const TileIn<K, Scale> in =
             load_tile<K, Scale, false>(packed, scale, t, (t * kWaveTile) >> (log2B + 8), n, log2B, lane);
-        decode_tile<E, K, Scale, false, false>(in, scale, cb_lds, pair_lds, out, t, n, lane);
+        decode_tile<E, K, Scale, false, false>(in, scale.finish(in.sc), cb_lds, pair_lds, out, t, n, lane);
     }
 }
 
