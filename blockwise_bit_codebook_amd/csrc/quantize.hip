@@ -283,7 +283,9 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) load_row<E, NT>(src + u * kWaveTile, lane_e, n, true, r[u]);
     };
+    // The first two steps' loads go out before the table build.
     if (LOG2B != 0 && st < nfull) load_full(st, ra);
+    if (LOG2B != 0 && PFD == 1 && st < nfull) load_full(min(st + nwaves, nfull - 1), rb);
 
     float c[C];
 #pragma unroll
@@ -357,8 +359,10 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
         };
         if (st < nfull) {
             if constexpr (PFD == 1) {
+                bool first = true;  // rb already holds the second step
                 while (true) {
-                    load_full(min(st + nwaves, nfull - 1), rb);
+                    if (!first) load_full(min(st + nwaves, nfull - 1), rb);
+                    first = false;
                     do_step(st, ra, std::true_type{});
                     st += nwaves;
                     if (st >= nfull) break;
