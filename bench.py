@@ -5,16 +5,16 @@ blocksize 64) followed by the nested 4-bit dequantize of those planes back to
 bf16 (per-block scales rebuilt from 8-bit codes over groups of 256 plus a
 mean offset), on an 8192 x 8192 weight drawn from N(0, 0.02).  Inputs live in
 HBM before timing starts.  Several buffer sets are rotated so that the
-256 MB last-level cache cannot hold a step's working set.  Rounds of steps
-over the buffer sets (up to 32 steps) are captured into a HIP graph, a
-second graph holds the remainder, and the timed loop replays them: exactly
---steps steps, warmed up by --warmup eager steps.
+256 MB last-level cache cannot hold a step's working set.  The timed region
+is exactly --steps steps (after --warmup untimed ones), launched eagerly,
+with a fence-free HIP event after each kernel on the kernels' stream.
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (read +
 written by both kernels) divided by the wall time per step, in GB/s.
-Per-kernel launch times (the ``roofline`` object) come from HIP events
-around eager launches of one kernel over all buffer sets, the kernels taken
-in round robin, on the stream the kernels run on.  The same line also reports, as side measurements, the
+Per-kernel times (``quantize``, ``nested_dequantize`` and the ``roofline``
+object) come from those events, i.e. from the timed steps.  Side kernels
+are timed with events around eager launches over all buffer sets, in round
+robin.  The same line also reports, as side measurements, the
 quantize / dequantize pair with one-byte E4M4 block scales and the plain
 fp32-scale dequantize on the same tensor, the FP4 codebook, warm-cache
 numbers and the W4A4 activation path (4096 x 4096 bf16).  ``cpu_baseline`` times the CPU oracle on a bounded sample of
@@ -517,6 +517,51 @@ def bench_linear(torch, kb, synth, dev, reps=20, shapes=None, eager=False):
             "note": "page_candidate_us: the page's fused dequantize + linear medians on its own GPU, context only"}
 
 
+class HipEvents:
+    """Timing events recorded on a HIP stream, created with
+    hipEventDisableSystemFence (no system-scope cache flush per record)."""
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, stream):
+        import ctypes
+        self.ct = ctypes
+        try:
+            hip = ctypes.CDLL("libamdhip64.so")
+        except OSError:
+            hip = ctypes.CDLL(os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib", "libamdhip64.so"))
+        vp = ctypes.c_void_p
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [vp, vp]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        hip.hipEventDestroy.argtypes = [vp]
+        self.hip = hip
+        self.stream = vp(stream)
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def create(self, k):
+        out = []
+        for _ in range(k):
+            e = self.ct.c_void_p()
+            self._ok(self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.FLAGS), "hipEventCreateWithFlags")
+            out.append(e)
+        return out
+
+    def record(self, e):
+        self._ok(self.hip.hipEventRecord(e, self.stream), "hipEventRecord")
+
+    def elapsed_ms(self, a, b):
+        m = self.ct.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self.ct.byref(m), a, b), "hipEventElapsedTime")
+        return m.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
 def side_only(args):
     """The side profile's workload: the activation cases, then the linear
     shapes, eagerly launched; then the calibration copies if asked."""
@@ -622,47 +667,11 @@ def main(argv=None):
         step(s_)
     torch.cuda.synchronize()
 
-    # The steps are captured into a HIP graph, so the timed loop measures the
-    # GPU rather than Python's launch path (the kernels allocate nothing and
-    # take the capture stream).
-    def capture(fn, items):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for s_ in items:
-                fn(s_)
-        return g
 
-    # A graph holds whole rounds over the buffer sets (quantize, nested
-    # dequantize, then the next set), up to 32 steps, so that one replay
-    # covers many steps; a second graph holds the remaining steps (starting
-    # again at set 0).  Exactly args.steps steps are timed.
-    per_graph = min(args.steps // args.sets, max(1, 32 // args.sets)) * args.sets
-    full, rest = (args.steps // per_graph, args.steps % per_graph) if per_graph else (0, args.steps)
-    g_steps = capture(step, [sets[i % args.sets] for i in range(per_graph)]) if full else None
-    g_rest = capture(step, [sets[i % args.sets] for i in range(rest)]) if rest else None
-    for i in range(args.warmup):
-        step(sets[i % args.sets])
-    torch.cuda.synchronize()
-
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(full):
-        g_steps.replay()
-    if g_rest is not None:
-        g_rest.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-
-    # Per-kernel launch time, from HIP events on the stream the kernels run
-    # on (torch's current stream, which the binding passes to every launch).
-    # Round robin over the kernels: each round launches every kernel once per
-    # buffer set, with an event before and after each kernel's launches, so
-    # that all of them are timed under the same clock and power state.
+    # Side kernels: per-kernel launch time from events on the same stream, in
+    # round robin: each round launches every kernel once per buffer set, with
+    # an event before and after each kernel's launches, so that all of them
+    # are timed under the same clock and power state.
     def round_robin(fns, reps, warm=3, bufs=None):
         bufs = sets if bufs is None else bufs
         for _ in range(warm):
@@ -688,10 +697,7 @@ def main(argv=None):
     rr = round_robin({"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only,
                       "quantize_kbit_e4m4_bf16_k4": quant_e4m4, "dequantize_kbit_e4m4_bf16_k4": dequant_e4m4,
                       "dequantize_kbit_bf16_k4": dequant_plain, "quantize_nested_absmax": encode_nested}, reps)
-    tq, tn = rr["quantize_kbit_bf16_k4"], rr["dequantize_4bit_nested_bf16"]
     qbytes, nbytes = algorithmic_bytes(n)
-    ms_step = wall * 1e3 / args.steps
-    value = (qbytes + nbytes) / (ms_step * 1e-3) / 1e9
 
     def kstats(ts, nbytes_, elems=n):
         ts = np.array(ts)
@@ -703,8 +709,6 @@ def main(argv=None):
                 "min_us": round(float(ts.min()) * 1e3, 3), "max_us": round(float(ts.max()) * 1e3, 3),
                 "bytes": nbytes_, "GB/s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                 "elements_per_s": round(elems / (avg * 1e-3), 1)}
-
-    kq, kn = kstats(tq, qbytes), kstats(tn, nbytes)
 
     # One-byte E4M4 scales on the same tensor, and the plain fp32-scale
     # dequantize (distinct kernels, so they do not mix into the step's
@@ -738,6 +742,51 @@ def main(argv=None):
             act_block = [bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp)
                          for r, dd, pp in ACT_BLOCK_CASES]
         lin = bench_linear(torch, kb, synth, dev)
+
+    # The timed region (after the side measurements, which also bring the
+    # GPU to its working clocks): args.steps steps, launched eagerly (Python issues a
+    # step in far less time than the GPU runs it), with a HIP event after
+    # each kernel on the stream the kernels run on.  The events are created
+    # without the system-scope fence (hipEventDisableSystemFence): default
+    # events add a cache flush per record, about 3 us per step.  The
+    # per-kernel times of the roofline come from these events, i.e. from
+    # the timed steps themselves.
+    # The timed steps call the two C entry points directly with arguments
+    # prepared once per buffer set: the same calls quant_only and nested_only
+    # make, without the wrappers' per-call checks, so that Python stays well
+    # ahead of the GPU.
+    stream_ptr = torch.cuda.current_stream(dev).cuda_stream
+    qfn, dfn = kb.lib().quantize_kbit_bf16_k4, kb.lib().dequantize_4bit_nested_bf16
+    qargs = [(cb.data_ptr(), s_["A"].data_ptr(), s_["absmax"].data_ptr(), s_["packed"].data_ptr(), n, BLOCK,
+              stream_ptr) for s_ in sets]
+    dargs = [(s_["packed"].data_ptr(), cb.data_ptr(), s_["code"].data_ptr(), qmap.data_ptr(),
+              s_["absmax2"].data_ptr(), float(offset), s_["out"].data_ptr(), n, BLOCK, stream_ptr) for s_ in sets]
+    for i in range(args.warmup):
+        step(sets[i % args.sets])
+    torch.cuda.synchronize()
+    hev = HipEvents(stream_ptr)
+    marks = hev.create(2 * args.steps + 1)
+    rc = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hev.record(marks[0])
+    for i in range(args.steps):
+        j = i % args.sets
+        rc |= qfn(*qargs[j])
+        hev.record(marks[2 * i + 1])
+        rc |= dfn(*dargs[j])
+        hev.record(marks[2 * i + 2])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if rc:
+        raise RuntimeError(f"a timed launch failed: {kb.lib().kbit_strerror(rc)}")
+    gpu_ms = hev.elapsed_ms(marks[0], marks[-1])
+    tq = [hev.elapsed_ms(marks[2 * i], marks[2 * i + 1]) for i in range(args.steps)]
+    tn = [hev.elapsed_ms(marks[2 * i + 1], marks[2 * i + 2]) for i in range(args.steps)]
+    hev.destroy(marks)
+    ms_step = wall * 1e3 / args.steps
+    value = (qbytes + nbytes) / (ms_step * 1e-3) / 1e9
+    kq, kn = kstats(tq, qbytes), kstats(tn, nbytes)
 
     dom_name, dom = ("quantize_kbit_bf16_k4", kq) if kq["avg_us"] >= kn["avg_us"] else \
         ("dequantize_4bit_nested_bf16", kn)
