@@ -20,7 +20,7 @@ fp32-scale dequantize on the same tensor, the FP4 codebook, warm-cache
 numbers and the W4A4 activation path (4096 x 4096 bf16).  ``cpu_baseline`` times the CPU oracle on a bounded sample of
 the same workload (N = 1 only).
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 10] [--sets 4]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 300] [--sets 4]
                     [--no-cpu-baseline] [--copy-calibration]
     python bench.py --summarize TRACE_DIR FETCH_DIR WRITE_DIR   (no GPU)
 """
@@ -74,7 +74,9 @@ def parse(argv=None):
     ap = argparse.ArgumentParser(description="k-bit codec hot-path throughput (one GPU)")
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps right before the timed ones (about 18 ms at 8192^2; the GPU needs "
+                         "some milliseconds of sustained load to reach its working clocks)")
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--rr-reps", type=int, default=0,
                     help="rounds of the per-kernel timing (default: steps / sets, at least 5)")
@@ -131,7 +133,7 @@ def _matches(pat, name):
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o trace -- "
-    "python3 $R/bench.py --steps 200 --warmup 10 --rr-reps 5 --no-cpu-baseline --headline-only --copy-calibration",
+    "python3 $R/bench.py --steps 200 --warmup 300 --rr-reps 5 --no-cpu-baseline --headline-only --copy-calibration",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o fetch -- "
     "python3 $R/bench.py --steps 8 --warmup 4 --no-cpu-baseline --headline-only --copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o write -- "
