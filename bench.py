@@ -693,6 +693,10 @@ def main(argv=None):
         return {name: [ev[r * len(fns) + j][0].elapsed_time(ev[r * len(fns) + j][1]) / len(bufs)
                        for r in range(reps)] for j, name in enumerate(fns)}
 
+    # bring the GPU to its working clocks before the side measurements too
+    for i in range(args.warmup):
+        step(sets[i % args.sets])
+    torch.cuda.synchronize()
     reps = args.rr_reps or max(5, args.steps // args.sets)
     # quant_e4m4 before dequant_e4m4 and quant_only before dequant_plain in
     # every round: each dequantize reads scales written by its own quantize.
