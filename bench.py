@@ -130,6 +130,7 @@ KERNELS = {
 
 def _matches(pat, name):
     return all(p in name for p in pat)
+PROFILE_STEPS = 200  # --steps of the trace command below
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o trace -- "
@@ -161,13 +162,15 @@ def _csv_rows(d, suffix):
         return list(csv.DictReader(f))
 
 
-def _summarize_into(table, trace_dir, fetch_dir, write_dir, header, commands, md_name):
+def _summarize_into(table, trace_dir, fetch_dir, write_dir, header, commands, md_name, timed_last=None):
     """Per-kernel average duration (kernel trace) and HBM bytes per dispatch
     (FETCH_SIZE / WRITE_SIZE in KiB, each scaled by what the same counter
     reads for the calibration copies of known size).  table: name ->
     (substrings of the demangled kernel name, grid size in threads or None,
     sources, algorithmic bytes per launch).  The entries are merged into
-    profiles/traffic.json and written as a table to profiles/<md_name>."""
+    profiles/traffic.json and written as a table to profiles/<md_name>.
+    timed_last: name -> number of final dispatches that are the timed steps
+    (their average is reported beside the overall one)."""
     trace = _csv_rows(trace_dir, "kernel_trace.csv")
     counters = {c: _csv_rows(d, "counter_collection.csv") for c, d in (("FETCH_SIZE", fetch_dir),
                                                                         ("WRITE_SIZE", write_dir))}
@@ -205,10 +208,12 @@ def _summarize_into(table, trace_dir, fetch_dir, write_dir, header, commands, md
                          "| kernel | dispatches | avg us | min us | max us | HBM read MB | HBM write MB "
                          "| algorithmic MB | traffic / algorithmic | GB/s (algorithmic) |",
                          "|---|---|---|---|---|---|---|---|---|---|"]
+    timed_notes = []
     for name, entry in table.items():
         srcs, ab = entry[2], entry[3]
-        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
-                if hit(entry, r["Kernel_Name"], r["Grid_Size_X"])]
+        hits = sorted((r for r in trace if hit(entry, r["Kernel_Name"], r["Grid_Size_X"])),
+                      key=lambda r: int(r["Start_Timestamp"]))
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in hits]
         if not durs or per_kernel[name]["FETCH_SIZE"] is None or per_kernel[name]["WRITE_SIZE"] is None:
             continue
         avg = sum(durs) / len(durs) / 1e3
@@ -216,19 +221,27 @@ def _summarize_into(table, trace_dir, fetch_dir, write_dir, header, commands, md
         w_kib = per_kernel[name]["WRITE_SIZE"]
         rd = f_kib * 1024 * scale["FETCH_SIZE"]
         wr = w_kib * 1024 * scale["WRITE_SIZE"]
+        last = (timed_last or {}).get(name)
+        timed_avg = sum(durs[-last:]) / min(last, len(durs)) / 1e3 if last else None
         out["kernels"][name] = {"avg_us": round(avg, 3), "dispatches": len(durs),
+                                "timed_steps_avg_us": None if timed_avg is None else round(timed_avg, 3),
                                 "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
                                 "read_bytes": int(rd), "write_bytes": int(wr), "traffic": int(rd + wr),
                                 "algorithmic_bytes": ab, "source_sha256_16": source_digest(srcs),
                                 "profile": md_name}
         ratio = f"{(rd + wr) / ab:.3f}" if ab else "—"
         gbs = f"{ab / (avg * 1e-6) / 1e9:.0f}" if ab else "—"
+        if timed_avg is not None:
+            timed_notes.append(f"{name}: {timed_avg:.2f} us over the last {last} dispatches (the timed steps)")
         lines.append(f"| {name} | {len(durs)} | {avg:.2f} | {min(durs) / 1e3:.2f} | {max(durs) / 1e3:.2f} | "
                      f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {ab / 1e6 if ab else 0:.1f} | {ratio} | {gbs} |")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(tj, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
+    if timed_notes:
+        lines += ["", "Average duration over the timed steps alone (the warmup runs before the GPU reaches its "
+                      "working clocks):", ""] + [f"* {t}" for t in timed_notes]
     with open(os.path.join(ROOT, "profiles", md_name), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -243,7 +256,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
               "the plain fp32-scale dequantize and the nested-state encoder (quantize_nested_absmax: "
               "nested_bins/offset/encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements."]
     return _summarize_into(table, trace_dir, fetch_dir, write_dir, header, PROFILE_COMMANDS,
-                           "kbit_kernels_8192sq_bf16_nf4_b64.md")
+                           "kbit_kernels_8192sq_bf16_nf4_b64.md",
+                           timed_last={"quantize_kbit_bf16_k4": PROFILE_STEPS,
+                                       "dequantize_4bit_nested_bf16": PROFILE_STEPS})
 
 
 def summarize_side(trace_dir, fetch_dir, write_dir):
@@ -408,7 +423,8 @@ _A_SRC = ["blockwise_bit_codebook_amd/csrc/act_fwht.hip", "blockwise_bit_codeboo
 _AB_SRC = ["blockwise_bit_codebook_amd/csrc/act_block.hip", "blockwise_bit_codebook_amd/csrc/act_common.h",
            "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/device.h"]
 _L_SRC = ["blockwise_bit_codebook_amd/csrc/linear.hip", "blockwise_bit_codebook_amd/csrc/device.h"]
-SIDE_PROFILE_COMMANDS = [
+SIDE_PROFILE_STEPS = 200  # --steps of the trace command below
+PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/side_trace -o trace -- "
     "python3 $R/bench.py --side-only --side-reps 20 --copy-calibration",
