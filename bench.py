@@ -402,6 +402,62 @@ def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, s
             "rows_per_s": round(rows / (avg * 1e-3), 1)}
 
 
+def bench_sweep(torch, kb, dev, reps, sets=4):
+    """Quantize and plain dequantize of the 8192 x 8192 N(0, 0.02) weight for
+    every input type and K = 2..5 (NF_K codebook, blocksize 64), each pair in
+    round robin over rotated buffer sets."""
+    n = ROWS * COLS
+    nb = n // BLOCK
+    tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+    esz = {"fp32": 4, "fp16": 2, "bf16": 2}
+    res = []
+    for name, dt in tdt.items():
+        g = torch.Generator(device="cpu").manual_seed(7)
+        base = (torch.randn(n, generator=g) * 0.02).to(dt).to(dev)
+        bufs = [(base if i == 0 else base.clone(), torch.empty(nb, dtype=torch.float32, device=dev),
+                 torch.empty(n, dtype=dt, device=dev)) for i in range(sets)]
+        for Kk in (2, 3, 4, 5):
+            cbk = torch.from_numpy(kb.codebook_nf(Kk)).to(dev)
+            packed = [torch.empty(kb.n_words(n, Kk), dtype=torch.int32, device=dev) for _ in range(sets)]
+
+            def q(i):
+                kb.quantize_kbit(bufs[i][0], cbk, Kk, BLOCK, absmax=bufs[i][1], packed=packed[i])
+
+            def d(i):
+                kb.dequantize_kbit(packed[i], cbk, bufs[i][1], Kk, n, dt, BLOCK, out=bufs[i][2])
+
+            for _ in range(3):
+                for i in range(sets):
+                    q(i)
+                for i in range(sets):
+                    d(i)
+            torch.cuda.synchronize()
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+            for r in range(reps):
+                ev[r][0].record()
+                for i in range(sets):
+                    q(i)
+                ev[r][1].record()
+                for i in range(sets):
+                    d(i)
+                ev[r][2].record()
+            torch.cuda.synchronize()
+            tq = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / sets * 1e3
+            td = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / sets * 1e3
+            bq = esz[name] * n + 4 * (n // 32) * Kk + 4 * nb + 4 * (1 << Kk)
+            res.append({"dtype": name, "K": Kk, "quantize_us": round(tq, 3),
+                        "quantize_frac_of_hbm_peak": round(bq / (tq * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "dequantize_us": round(td, 3),
+                        "dequantize_frac_of_hbm_peak": round(bq / (td * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "bytes": bq})
+            del packed
+        del bufs, base
+        torch.cuda.empty_cache()
+    return {"workload": "8192x8192 N(0,0.02) weight, NF_K, blocksize 64, fp32 scales; quantize and plain "
+                        "dequantize per input type and K, 4 rotated buffer sets",
+            "cases": res}
+
+
 # Block-Hadamard activation cases: (rows, d, permutation).
 ACT_BLOCK_CASES = [(4096, 3840, False), (4096, 3840, True), (4096, 12288, False), (4096, 12288, True),
                    (4096, 4096, True)]
@@ -746,7 +802,7 @@ def main(argv=None):
 
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
-    fp4 = warm = act = act_block = lin = None
+    fp4 = warm = act = act_block = lin = sweep = None
     if not args.headline_only:
         pair = {"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only}
         cb_nf = cb
@@ -764,6 +820,7 @@ def main(argv=None):
             act_block = [bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp)
                          for r, dd, pp in ACT_BLOCK_CASES]
         lin = bench_linear(torch, kb, synth, dev)
+        sweep = bench_sweep(torch, kb, dev, reps)
 
     # The timed region (after the side measurements, which also bring the
     # GPU to its working clocks): args.steps steps, launched eagerly (Python issues a
@@ -861,6 +918,7 @@ def main(argv=None):
         "act_fwht": act,
         "act_block_hadamard": act_block,
         "linear_4bit": lin,
+        "dtype_k_sweep": sweep,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -135,7 +135,7 @@ __device__ __forceinline__ void decode_tile(const TileIn<K, Scale>& in, float s,
         }
     }
     if (FULL) {
-        E::template store8<NTS>(out + e0, v);
+        E::template store_row<NTS>(out + tile * kWaveTile, lane, v);
     } else {
 #pragma unroll
         for (int t = 0; t < kElemsPerLane; ++t)

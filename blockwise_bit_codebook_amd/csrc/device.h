@@ -112,9 +112,17 @@ __host__ __device__ __forceinline__ int pair_index(int b, int s0) {
 }
 
 // ---------------------------------------------------------------------------
-// Element types.  Each trait loads the 8 consecutive elements of one lane
-// (16 bytes for 16-bit types, 32 bytes for fp32) widened exactly to float,
-// and stores 8 floats narrowed with round-to-nearest-even.
+// Element types.  Data move in wave rows of 512 elements: lane l owns the
+// 8 consecutive elements 8l .. 8l+7 of the row, loaded as E::kVec 16-byte
+// vectors (raw, in memory order) and widened exactly to float by unpack;
+// store_row narrows 8 floats with round-to-nearest-even and writes them.
+// 16-bit types: the lane's one vector is its own 16 bytes.  fp32: lane l's
+// vector v holds the 4 elements at 256v + 8(l & 31) + 4(l >> 5), so that each
+// 16-byte-per-lane load or store covers 1 KiB of contiguous memory; one
+// v_permlane32_swap per element pair moves them to their owners (lanes
+// l < 32 keep vector 0 and take vector 1 from lane l + 32, which keeps
+// vector 1: the swap is its own inverse).  unpack, load_partial and
+// store_row must be executed by all 64 lanes of the wave for fp32.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float float8 __attribute__((ext_vector_type(8)));
@@ -136,16 +144,6 @@ __device__ __forceinline__ void store16(void* p, const u32x4& v) {
 }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-
-// Largest magnitude (sign bit cleared) of the 8 16-bit values in r[0], as an
-// integer.  For IEEE-style formats the magnitude order of finite values and
-// infinities equals the integer order of their bits, and NaNs sort above.
-__device__ __forceinline__ uint32_t max_mag16x8(const u32x4& r) {
-    auto h = [](uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu); };
-    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(h(r[0]), h(r[1])),
-                                              __builtin_elementwise_max(h(r[2]), h(r[3])));
-    return max(static_cast<uint32_t>(m[0]), static_cast<uint32_t>(m[1]));
-}
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -153,41 +151,43 @@ struct Fp32 {
     using storage = float;
     static constexpr int kBytes = 4;
     static constexpr int kVec = 2;  // 16-byte vectors per 8 elements
-    __device__ static void unpack(const u32x4* r, float* x) {
+    // element offset (from the row start) of the lane's vector v
+    __device__ static int vec_offset(int lane, int v) { return 256 * v + 8 * (lane & 31) + 4 * (lane >> 5); }
+    // vector 0 of lanes 32..63 <-> vector 1 of lanes 0..31
+    __device__ static void swap_halves(u32x4& a, u32x4& b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = __uint_as_float(r[0][i]);
-            x[4 + i] = __uint_as_float(r[1][i]);
+            const auto s = __builtin_amdgcn_permlane32_swap(a[i], b[i], false, false);
+            a[i] = s[0];
+            b[i] = s[1];
         }
     }
-    __device__ static uint32_t max_mag(const u32x4* r) {
-        uint32_t m = 0;
+    __device__ static void unpack(const u32x4* r, float* x) {
+        u32x4 a = r[0], b = r[1];
+        swap_halves(a, b);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, max(r[0][i] & 0x7FFFFFFFu, r[1][i] & 0x7FFFFFFFu));
-        return m;
+        for (int i = 0; i < 4; ++i) {
+            x[i] = __uint_as_float(a[i]);
+            x[4 + i] = __uint_as_float(b[i]);
+        }
     }
-    __device__ static float mag_to_float(uint32_t m) { return __uint_as_float(m); }
-    // Elements e0 .. e0+7 with zeros past n.
-    __device__ static void load_partial(const storage* A, int64_t e0, int64_t n, u32x4* r) {
+    // The raw vectors of a partial row: `rem` elements from `row` on are
+    // valid, the rest read as 0.
+    __device__ static void load_partial(const storage* row, int lane, int64_t rem, u32x4* r) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            r[s >> 2][s & 3] = (e0 + s < n) ? __float_as_uint(A[e0 + s]) : 0u;
+        for (int v = 0; v < 2; ++v) {
+            const int o = vec_offset(lane, v);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[v][i] = (o + i < rem) ? __float_as_uint(row[o + i]) : 0u;
+        }
     }
-    __device__ static void load8(const storage* p, float* x) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
-        const uint4 b = *reinterpret_cast<const uint4*>(p + 4);
-        x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
-        x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
-        x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
-        x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
-    }
-    __device__ static float load1(const storage* p) { return *p; }
     template <bool NT = false>
-    __device__ static void store8(storage* p, const float* v) {
-        const u32x4 a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
-        const u32x4 b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
-        store16<NT>(p, a);
-        store16<NT>(p + 4, b);
+    __device__ static void store_row(storage* row, int lane, const float* v) {
+        u32x4 a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        u32x4 b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+        swap_halves(a, b);
+        store16<NT>(row + vec_offset(lane, 0), a);
+        store16<NT>(row + vec_offset(lane, 1), b);
     }
     __device__ static void store1(storage* p, float v) { *p = v; }
 };
@@ -231,29 +231,19 @@ struct Bf16 {
             x[2 * i + 1] = __uint_as_float(r[0][i] & 0xFFFF0000u);
         }
     }
-    __device__ static uint32_t max_mag(const u32x4* r) { return max_mag16x8(r[0]); }
-    __device__ static void load_partial(const storage* A, int64_t e0, int64_t n, u32x4* r) {
+    __device__ static int vec_offset(int lane, int) { return 8 * lane; }
+    __device__ static void load_partial(const storage* row, int lane, int64_t rem, u32x4* r) {
+        const int o = 8 * lane;
         uint32_t h[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) h[s] = (e0 + s < n) ? static_cast<uint32_t>(A[e0 + s]) : 0u;
+        for (int s = 0; s < 8; ++s) h[s] = (o + s < rem) ? static_cast<uint32_t>(row[o + s]) : 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[0][i] = h[2 * i] | (h[2 * i + 1] << 16);
     }
-    __device__ static float mag_to_float(uint32_t m) { return __uint_as_float(m << 16); }
-    __device__ static void load8(const storage* p, float* x) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-    }
-    __device__ static float load1(const storage* p) { return __uint_as_float(static_cast<uint32_t>(*p) << 16); }
     template <bool NT = false>
-    __device__ static void store8(storage* p, const float* v) {
-        store16<NT>(p, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                             pack_bf16x2(v[6], v[7])});
+    __device__ static void store_row(storage* row, int lane, const float* v) {
+        store16<NT>(row + 8 * lane, u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])});
     }
     __device__ static void store1(storage* p, float v) {
         *p = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xFFFFu);
@@ -274,29 +264,19 @@ struct Fp16 {
             x[2 * i + 1] = h2f(r[0][i] >> 16);
         }
     }
-    __device__ static uint32_t max_mag(const u32x4* r) { return max_mag16x8(r[0]); }
-    __device__ static void load_partial(const storage* A, int64_t e0, int64_t n, u32x4* r) {
+    __device__ static int vec_offset(int lane, int) { return 8 * lane; }
+    __device__ static void load_partial(const storage* row, int lane, int64_t rem, u32x4* r) {
+        const int o = 8 * lane;
         uint32_t h[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) h[s] = (e0 + s < n) ? static_cast<uint32_t>(A[e0 + s]) : 0u;
+        for (int s = 0; s < 8; ++s) h[s] = (o + s < rem) ? static_cast<uint32_t>(row[o + s]) : 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[0][i] = h[2 * i] | (h[2 * i + 1] << 16);
     }
-    __device__ static float mag_to_float(uint32_t m) { return h2f(m); }
-    __device__ static void load8(const storage* p, float* x) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[2 * i] = h2f(w[i] & 0xFFFFu);
-            x[2 * i + 1] = h2f(w[i] >> 16);
-        }
-    }
-    __device__ static float load1(const storage* p) { return h2f(*p); }
     template <bool NT = false>
-    __device__ static void store8(storage* p, const float* v) {
-        store16<NT>(p, u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]),
-                             pack_f16x2(v[6], v[7])});
+    __device__ static void store_row(storage* row, int lane, const float* v) {
+        store16<NT>(row + 8 * lane, u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]),
+                                          pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])});
     }
     __device__ static void store1(storage* p, float v) {
         *p = static_cast<uint16_t>(pack_f16x2(v, 0.0f) & 0xFFFFu);

@@ -197,17 +197,17 @@ __device__ __forceinline__ void encode_row(bool fast, const Tables& T, const cha
     }
 }
 
-// The 8 elements of lane offset `off` from a wave-uniform row pointer; for
-// partial rows `rem` is the number of valid elements from `p` on (elements
-// past it read as 0).
+// The raw vectors of the lane's 8 elements of the wave row at `p`
+// (wave-uniform); for partial rows `rem` is the number of valid elements from
+// `p` on (elements past it read as 0).
 template <class E, bool NT>
-__device__ __forceinline__ void load_row(const typename E::storage* __restrict__ p, int off, int64_t rem, bool full,
+__device__ __forceinline__ void load_row(const typename E::storage* __restrict__ p, int lane, int64_t rem, bool full,
                                          u32x4 (&raw)[E::kVec]) {
     if (full) {
 #pragma unroll
-        for (int v = 0; v < E::kVec; ++v) raw[v] = load16<NT>(p + off + v * (16 / E::kBytes));
+        for (int v = 0; v < E::kVec; ++v) raw[v] = load16<NT>(p + E::vec_offset(lane, v));
     } else {
-        E::load_partial(p, off, rem, raw);
+        E::load_partial(p, lane, rem, raw);
     }
 }
 
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     auto load_full = [&](int64_t i, u32x4 (&r)[ROWS][kV]) {
         const typename E::storage* src = A + i * kStep;  // wave-uniform
 #pragma unroll
-        for (int u = 0; u < ROWS; ++u) load_row<E, NT>(src + u * kWaveTile, lane_e, n, true, r[u]);
+        for (int u = 0; u < ROWS; ++u) load_row<E, NT>(src + u * kWaveTile, lane, n, true, r[u]);
     };
     // The first two steps' loads go out before the table build.
     if (LOG2B != 0 && st < nfull) load_full(st, ra);
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
         if (st == nfull && nfull < nsteps) {
             u32x4 r[ROWS][kV];
 #pragma unroll
-            for (int u = 0; u < ROWS; ++u) load_row<E, false>(A + st * kStep + u * kWaveTile, lane_e, n - (st * kStep + u * kWaveTile), false, r[u]);
+            for (int u = 0; u < ROWS; ++u) load_row<E, false>(A + st * kStep + u * kWaveTile, lane, n - (st * kStep + u * kWaveTile), false, r[u]);
             do_step(st, r, std::false_type{});
         }
     } else {
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
             for (int u = 0; u < rows; ++u) {
                 const int64_t rb = base + u * kWaveTile;
                 u32x4 raw[kV];
-                load_row<E, false>(A + rb, lane * kElemsPerLane, n - rb, rb + kWaveTile <= n, raw);
+                load_row<E, false>(A + rb, lane, n - rb, rb + kWaveTile <= n, raw);
                 float x[8];
                 E::unpack(raw, x);
                 ml = __builtin_elementwise_maximum(ml, lane_max_abs(x));
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
                 const int64_t rb = base + u * kWaveTile;
                 if (rb >= n) break;
                 u32x4 raw[kV];
-                load_row<E, false>(A + rb, lane * kElemsPerLane, n - rb, rb + kWaveTile <= n, raw);
+                load_row<E, false>(A + rb, lane, n - rb, rb + kWaveTile <= n, raw);
                 float x[8];
                 E::unpack(raw, x);
                 encode_row<E, K, false>(fast, T, tab, lane_off, lane, x, m, rb, n, packed);
