@@ -197,14 +197,16 @@ struct Fp32 {
 // multiply into the conversion (v_fma_mix*), rounding once instead of twice.
 __device__ __forceinline__ void fence_f32(float& a, float& b) { asm("" : "+v"(a), "+v"(b)); }
 
-// (a << 1) | b as one v_lshl_or_b32.  Left to itself the compiler turns a
+// (a << S) | b as one v_lshl_or_b32.  Left to itself the compiler turns a
 // chain of these into separate shifts and three-input ors, which costs more
 // instructions than the chain.
-__device__ __forceinline__ uint32_t shl1_or(uint32_t a, uint32_t b) {
+template <int S>
+__device__ __forceinline__ uint32_t shl_or(uint32_t a, uint32_t b) {
     uint32_t r;
-    asm("v_lshl_or_b32 %0, %1, 1, %2" : "=v"(r) : "v"(a), "v"(b));
+    asm("v_lshl_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "i"(S), "v"(b));
     return r;
 }
+__device__ __forceinline__ uint32_t shl1_or(uint32_t a, uint32_t b) { return shl_or<1>(a, b); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     fence_f32(lo, hi);

@@ -135,24 +135,37 @@ __device__ __forceinline__ Codes classify_exact(const float* c, const float (&x)
 
 // Whether the table holds switching points in the fp32 pair form (decide32):
 // 16-bit inputs, whose values and block maxima have at most 11 significant
-// bits.  K = 5 keeps the fp64 form, whose low bits carry the plane-4 flags.
+// bits.
 template <class E, int K>
-constexpr bool kPairForm = !std::is_same<E, Fp32>::value && K <= 4;
+constexpr bool kPairForm = !std::is_same<E, Fp32>::value;
 
 template <class E, int K>
 __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, float r, const char* tab,
                                                uint32_t lane_off) {
     Codes out;
     const double s64 = static_cast<double>(s);
-    // Elements 7..0: each step shifts the accumulated plane bits up by one,
-    // so element t ends at bit t of every plane byte.
-#pragma unroll
-    for (int t = 7; t >= 0; --t) {
+    auto sel = [&](int t) {
         const float q = __builtin_fmaf(x[t], r, kBase);
         const Decision d = kPairForm<E, K> ? decide32(x[t], q, s, tab, lane_off) : decide(x[t], q, s64, tab, lane_off);
-        const uint32_t sel = d.up ? d.e[3] : d.e[2];
-        out.acc = t == 7 ? sel : shl1_or(out.acc, sel);
-        if constexpr (K == 5) out.acc4 = (out.acc4 << 1) | ((d.e[0] >> (d.up ? 1 : 0)) & 1u);
+        return d.up ? d.e[3] : d.e[2];
+    };
+    if constexpr (K <= 4) {
+        // Elements 7..0: each step shifts the accumulated plane bits up by
+        // one, so element t ends at bit t of every plane byte.
+#pragma unroll
+        for (int t = 7; t >= 0; --t) out.acc = t == 7 ? sel(t) : shl1_or(out.acc, sel(t));
+    } else {
+        // Even and odd elements in two chains shifting by two: element 2m
+        // (2m + 1) ends with plane p at bit 8p + 2m of ev (od) and plane 4
+        // (bit 1 of the entry's byte 0) at bit 2m + 1.
+        uint32_t ev = 0, od = 0;
+#pragma unroll
+        for (int m = 3; m >= 0; --m) {
+            ev = m == 3 ? sel(2 * m) : shl_or<2>(ev, sel(2 * m));
+            od = m == 3 ? sel(2 * m + 1) : shl_or<2>(od, sel(2 * m + 1));
+        }
+        out.acc = (ev & 0x55555555u) | ((od << 1) & 0xAAAAAAAAu);
+        out.acc4 = ((ev >> 1) & 0x55u) | (od & 0xAAu);
     }
     return out;
 }
@@ -283,38 +296,53 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) load_row<E, NT>(src + u * kWaveTile, lane, n, true, r[u]);
     };
-    // The first two steps' loads go out before the table build.
-    if (LOG2B != 0 && st < nfull) load_full(st, ra);
-    if (LOG2B != 0 && PFD == 1 && st < nfull) load_full(min(st + nwaves, nfull - 1), rb);
-
+    // The codebook's scalar loads go out first (behind the first steps' loads
+    // they would wait for the memory queue), then the first two steps' loads,
+    // whose latency overlaps the table build.
     float c[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) c[i] = cb[i];
+    if (LOG2B != 0 && st < nfull) load_full(st, ra);
+    if (LOG2B != 0 && PFD == 1 && st < nfull) load_full(min(st + nwaves, nfull - 1), rb);
+
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
     if (threadIdx.x < C) T.code[threadIdx.x] = c[threadIdx.x];
-    // One wave per threshold (the search is wave-cooperative); a failed
-    // search leaves the sentinel, which fails the table below.
-    for (int i = wave + 1; i < C; i += kWaves_) {
-        const float lo = cb[i - 1], hi = cb[i];  // wave-uniform
-        uint64_t m = 0;
-        if (fast && lo != hi && !threshold_mid_wave<kPairForm<E, K>>(lo, hi, m)) m = kNoMid;
-        if (lane == 0) T.mid[i] = m;
+    // The switching points: one wave per threshold, or one half-wave where
+    // there are more thresholds than waves (the search is cooperative); a
+    // failed search leaves the sentinel, which fails the table below.
+    if constexpr (C - 1 <= kWaves_) {
+        for (int i = wave + 1; i < C; i += kWaves_) {  // wave-uniform
+            const float lo = cb[i - 1], hi = cb[i];
+            uint64_t m = 0;
+            if (fast && lo != hi && !threshold_mid_wave<kPairForm<E, K>>(lo, hi, m)) m = kNoMid;
+            if (lane == 0) T.mid[i] = m;
+        }
+    } else {
+        for (int i0 = 1; i0 < C; i0 += 2 * kWaves_) {  // uniform trip count
+            // the wave's two thresholds ib and ib + 1 from three uniform loads
+            const int ib = i0 + 2 * wave;
+            const float a = cb[min(ib - 1, C - 1)], b = cb[min(ib, C - 1)], d = cb[min(ib + 1, C - 1)];
+            const bool upper = lane >= 32;
+            const int i = ib + (upper ? 1 : 0);
+            const bool real = i < C;
+            const float lo = real ? (upper ? b : a) : 0.0f, hi = real ? (upper ? d : b) : 0.0f;
+            uint64_t m = 0;
+            const bool ok = threshold_mid_group<32, kPairForm<E, K>>(lo, hi, m);  // every lane calls it
+            if (real && (lane & 31) == 0) T.mid[i] = (fast && lo != hi) ? (ok ? m : kNoMid) : 0u;
+        }
     }
     if (threadIdx.x == 0) T.mid[0] = 0;
     __syncthreads();
+    // One thread per bucket builds its entry and writes all its copies.
     if (threadIdx.x < C && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
         if (!build_entry<C, K == 5>(c, T.mid, threadIdx.x, kSlope, kBase, e)) T.fail = 1;
-        T.master[threadIdx.x] = e;
+        store_bucket_copies(T, threadIdx.x, e);
     }
     __syncthreads();
     fast = fast && (T.fail == 0);
-    if (fast) {
-        for (int i = threadIdx.x; i < kBuckets * kCopies; i += THREADS) T.row[i] = T.master[i / kCopies];
-    }
-    __syncthreads();
 
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
     const char* tab = reinterpret_cast<const char*>(T.row);
@@ -458,10 +486,11 @@ int launch_cfg(const float* cb, const void* A, void* absmax, uint32_t* packed, i
 template <class E, class S, int K>
 int launch_k(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
              void* stream) {
-    // Two wave rows per step for bf16 (32 bytes per lane in flight plus the
-    // prefetched step) where that still fits 64 VGPRs; one row otherwise.
-    // K = 5 needs about 80 VGPRs: 512-thread groups keep 6 waves per SIMD.
-    constexpr int R = (std::is_same<E, Bf16>::value && K <= 4) ? 2 : 1;
+    // Two wave rows per step for 16-bit inputs (32 bytes per lane in flight
+    // plus the prefetched step, within 64 VGPRs); one row for fp32.  K = 5
+    // runs 512-thread groups: its kernels need 60..70 VGPRs, and smaller
+    // groups fill the SIMDs' remaining wave slots.
+    constexpr int R = std::is_same<E, Fp32>::value ? 1 : 2;
     constexpr int TH = K == 5 ? 512 : kQThreads;
     switch (log2B) {
         case 5: return launch_cfg<E, S, K, 5, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);

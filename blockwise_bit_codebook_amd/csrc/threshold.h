@@ -29,11 +29,10 @@ constexpr int kCopies = 16;
 constexpr float kDelta = 0x1p-18f;  // bucket window half-width in q
 constexpr uint64_t kNoMid = ~uint64_t(0);  // marks a failed search (never an M: bits 1:0 of M are 0)
 
-// Bucket rows, their master copy, and the per-threshold M (fp64 bits).
+// Bucket rows and the per-threshold M (fp64 bits).
 template <int C>
 struct ThresholdTables {
     u32x4 row[kBuckets * kCopies];  // {M, planes(below), planes(above)} per copy
-    u32x4 master[kBuckets];
     uint64_t mid[C];                // mid[i]: threshold between codes i-1 and i
     float code[C];                  // the codebook (exact path)
     int fail;
@@ -61,7 +60,7 @@ __device__ inline uint64_t mid_bits(float u, float p) {
     const double M = (static_cast<double>(u) + static_cast<double>(p)) * 0.5;  // exact
     // An exact tie x/s == M rounds to the even one of pred(u), u: to u means
     // "upper" at equality, so M moves down by 4 fp64 ulps; otherwise it moves
-    // up (or stays).  Bits 1:0 stay free for the plane-4 flags of K = 5.
+    // up (or stays); bits 1:0 are then cleared.
     const bool tie_up = static_cast<float>(M) == u;
     uint64_t b = static_cast<uint64_t>(__double_as_longlong(M));
     if (M > 0.0) b = tie_up ? b - 4u : b;
@@ -168,35 +167,43 @@ __device__ inline bool threshold_mid_wave(float lo, float hi, uint64_t& bits) {
 }
 
 // Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
-// threshold whose window meets the bucket (mid[i] from threshold_mid_group), the
-// plane bytes of the indices below and above it, and with PLANE4 their
-// plane-4 bits in bits 0 and 1 of M.  Returns false if two windows meet
-// the bucket.
+// threshold whose window meets the bucket (mid[i] from threshold_mid_group)
+// and the plane bytes of the indices below and above it (bit 0 of byte p =
+// plane p), with PLANE4 plane 4 in bit 1 of byte 0.  Returns false if two
+// windows meet the bucket.
 template <int C, bool PLANE4>
 __device__ bool build_entry(const float (&c)[C], const uint64_t* mid, int j, float slope, float base,
                             u32x4& e) {
     const float lo = 2.0f + static_cast<float>(j) * (2.0f / kBuckets);
     const float hi = lo + (2.0f / kBuckets);
-    uint32_t below = 0;
-    int cand = -1;
-    bool ok = true;
+    // The thresholds rise with i (the codebook is sorted): below = the last
+    // one whose window lies under the bucket, cand = the first whose window
+    // meets it (0: none).  Selects only, no branches.
+    int below = 0, cand = 0, meets = 0;
 #pragma unroll
     for (int i = 1; i < C; ++i) {
-        if (c[i] != c[i - 1]) {
-            const float t = base + ((c[i - 1] + c[i]) * 0.5f) * slope;
-            if (t + kDelta <= lo) {
-                below = i;
-            } else if (t - kDelta < hi) {
-                if (cand < 0) cand = i;
-                else ok = false;
-            }
-        }
+        const bool distinct = c[i] != c[i - 1];
+        const float t = base + ((c[i - 1] + c[i]) * 0.5f) * slope;
+        const bool under = distinct && t + kDelta <= lo;
+        const bool meet = distinct && !under && t - kDelta < hi;
+        below = under ? i : below;
+        cand = (meet && cand == 0) ? i : cand;
+        meets += meet ? 1 : 0;
     }
-    const uint32_t above = cand < 0 ? below : static_cast<uint32_t>(cand);
-    uint64_t m = cand < 0 ? 0u : mid[cand];
-    if constexpr (PLANE4) m |= ((below >> 4) & 1u) | (((above >> 4) & 1u) << 1);
-    e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), spread4(below & 15u), spread4(above & 15u)};
-    return ok;
+    const uint32_t above = cand == 0 ? static_cast<uint32_t>(below) : static_cast<uint32_t>(cand);
+    const uint64_t m = cand == 0 ? 0u : mid[cand];
+    auto planes = [](uint32_t i) { return spread4(i & 15u) | (PLANE4 ? ((i >> 4) & 1u) << 1 : 0u); };
+    e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), planes(static_cast<uint32_t>(below)),
+              planes(above)};
+    return meets <= 1;
+}
+
+// Writes bucket j's entry into its kCopies rows, starting at copy j mod
+// kCopies, so that the lanes of one store cover all banks.
+template <int C>
+__device__ __forceinline__ void store_bucket_copies(ThresholdTables<C>& T, int j, const u32x4& e) {
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) T.row[j * kCopies + ((k + j) & (kCopies - 1))] = e;
 }
 
 // Byte address of the lane's copy of q's bucket entry: byte 1 <- bits

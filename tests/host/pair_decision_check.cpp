@@ -67,12 +67,13 @@ static long long check(const Thr& t, bool half, const std::vector<float>& svals)
 int main(int argc, char** argv) {
     const bool quick = argc > 1 && std::strcmp(argv[1], "quick") == 0;  // the random codebooks only
     std::vector<std::vector<float>> books;
-    for (int K = 2; K <= 4; ++K) { std::vector<float> c(1 << K); kbit_codebook_nf(K, c.data()); books.push_back(c); }
+    for (int K = 2; K <= 5; ++K) { std::vector<float> c(1 << K); kbit_codebook_nf(K, c.data()); books.push_back(c); }
     { std::vector<float> c(16); kbit_codebook_fp4(c.data()); books.push_back(c); }
     { std::vector<float> c(16); kbit_codebook_lloyd_max_normal(16, c.data()); for (auto& v : c) v /= 2.7326f; books.push_back(c); }
+    const size_t fixed = books.size();
     std::mt19937 rng(1);
-    for (int r = 0; r < 4; ++r) {
-        std::vector<float> c(16);
+    for (int r = 0; r < 6; ++r) {
+        std::vector<float> c(r < 4 ? 16 : 32);
         std::uniform_real_distribution<float> U(-1.f, 1.f);
         for (auto& v : c) v = U(rng);
         std::sort(c.begin(), c.end());
@@ -84,7 +85,7 @@ int main(int argc, char** argv) {
     for (int m = 0; m < 128; m += 7) { sb.push_back(std::ldexp(1.0f + m / 128.0f, -26)); sb.push_back(std::ldexp(1.0f + m / 128.0f, 100)); }
     for (int m = 0; m < 1024; ++m) sh.push_back(1.0f + m / 1024.0f);
     for (int m = 0; m < 1024; m += 37) { sh.push_back(std::ldexp(1.0f + m / 1024.0f, -14)); sh.push_back(std::ldexp(1.0f + m / 1024.0f, 15)); }
-    if (quick) books.erase(books.begin(), books.begin() + 5);  // drop NF2..4, FP4, Lloyd-Max
+    if (quick) books.erase(books.begin(), books.begin() + fixed);  // drop NF2..5, FP4, Lloyd-Max
     std::vector<Thr> thr;
     int notok = 0;
     for (auto& c : books) {

@@ -1,7 +1,7 @@
 """Exhaustive host check of the quantize kernel's fp32 threshold decision for
 16-bit inputs (no GPU): every bf16 / fp16 x in [-s, s] against every 16-bit
-significand of s, for the NF2..NF4, FP4, Lloyd-Max and random codebooks'
-switching points.  A planted one-ulp shift of the threshold must be caught.
+significand of s, for the NF2..NF5, FP4, Lloyd-Max and random 16- and
+32-entry codebooks' switching points.  A planted one-ulp shift of the threshold must be caught.
 """
 
 import os
