@@ -479,8 +479,7 @@ _A_SRC = ["blockwise_bit_codebook_amd/csrc/act_fwht.hip", "blockwise_bit_codeboo
 _AB_SRC = ["blockwise_bit_codebook_amd/csrc/act_block.hip", "blockwise_bit_codebook_amd/csrc/act_common.h",
            "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/device.h"]
 _L_SRC = ["blockwise_bit_codebook_amd/csrc/linear.hip", "blockwise_bit_codebook_amd/csrc/device.h"]
-SIDE_PROFILE_STEPS = 200  # --steps of the trace command below
-PROFILE_COMMANDS = [
+SIDE_PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/side_trace -o trace -- "
     "python3 $R/bench.py --side-only --side-reps 20 --copy-calibration",

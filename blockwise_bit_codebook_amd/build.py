@@ -43,18 +43,43 @@ CXX_FLAGS = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-ffp-contract=off", "-fno-f
              "-I", os.path.join(ROCM, "include")]
 
 
+USAGE_REMARK = "-Rpass-analysis=kernel-resource-usage"
+
+
+def _scratch_kernels(lines):
+    """(function, bytes per lane) for every function whose resource-usage
+    remark reports a nonzero ScratchSize."""
+    bad, fn = [], None
+    for l in lines:
+        if "Function Name:" in l:
+            fn = l.split("Function Name:", 1)[1].split("[-R", 1)[0].strip()
+        elif "ScratchSize [bytes/lane]:" in l:
+            n = int(l.split("ScratchSize [bytes/lane]:", 1)[1].split()[0])
+            if n:
+                bad.append((fn, n))
+    return bad
+
+
 def _compile(src, verbose):
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
-    flags = HIP_FLAGS if src.endswith(".hip") else CXX_FLAGS
+    hip = src.endswith(".hip")
+    flags = HIP_FLAGS + [USAGE_REMARK] if hip else CXX_FLAGS
     cmd = [HIPCC] + COMMON + flags + ["-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in l and "unused during compilation" not in l)
+    lines = (r.stdout + r.stderr).splitlines()
+    out = "\n".join(l for l in lines if "packed-fp32-ops" not in l and "unused during compilation" not in l
+                    and "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+    # Every kernel keeps its state in registers and LDS: a spill to scratch
+    # (private memory) is a build error, not a silent slowdown.
+    spills = _scratch_kernels(lines) if hip else []
+    if spills:
+        raise RuntimeError(f"{src}: kernels use scratch memory: " +
+                           ", ".join(f"{f} ({n} B/lane)" for f, n in spills))
     if out.strip() and verbose:
         print(out)
     return obj

@@ -75,8 +75,8 @@ struct ActPlan {
 
 // Builds T for the codebook cb.  Every thread of the workgroup calls it
 // (nthreads = blockDim.x, a multiple of 64 and at least 128); it holds
-// barriers, and every thread's later reads of T follow the last one.
-__device__ inline ActPlan build_act_tables(ActTables& T, const float* __restrict__ cb, int nthreads) {
+// barriers.
+__device__ __forceinline__ ActPlan build_act_tables(ActTables& T, const float* __restrict__ cb, int nthreads) {
     const int lane = __lane_id();
     float c[16];
 #pragma unroll
@@ -122,10 +122,14 @@ __device__ inline ActPlan build_act_tables(ActTables& T, const float* __restrict
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
         if (!build_entry<16, false>(c, T.mid, threadIdx.x, slope, kActBase, e)) T.fail = 1;
-        store_bucket_copies(T, threadIdx.x, e);
+        T.master[threadIdx.x] = e;
     }
     __syncthreads();
     fast = fast && (T.fail == 0);
+    if (fast) {
+        for (int i = threadIdx.x; i < kBuckets * kCopies; i += nthreads) T.row[i] = T.master[i / kCopies];
+    }
+    __syncthreads();
     return ActPlan{fast, slope};
 }
 

@@ -296,14 +296,13 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) load_row<E, NT>(src + u * kWaveTile, lane, n, true, r[u]);
     };
-    // The codebook's scalar loads go out first (behind the first steps' loads
-    // they would wait for the memory queue), then the first two steps' loads,
-    // whose latency overlaps the table build.
+    // The first two steps' loads go out before the table build.
+    if (LOG2B != 0 && st < nfull) load_full(st, ra);
+    if (LOG2B != 0 && PFD == 1 && st < nfull) load_full(min(st + nwaves, nfull - 1), rb);
+
     float c[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) c[i] = cb[i];
-    if (LOG2B != 0 && st < nfull) load_full(st, ra);
-    if (LOG2B != 0 && PFD == 1 && st < nfull) load_full(min(st + nwaves, nfull - 1), rb);
 
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
@@ -334,15 +333,18 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     }
     if (threadIdx.x == 0) T.mid[0] = 0;
     __syncthreads();
-    // One thread per bucket builds its entry and writes all its copies.
     if (threadIdx.x < C && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
     if (fast && threadIdx.x < kBuckets) {
         u32x4 e;
         if (!build_entry<C, K == 5>(c, T.mid, threadIdx.x, kSlope, kBase, e)) T.fail = 1;
-        store_bucket_copies(T, threadIdx.x, e);
+        T.master[threadIdx.x] = e;
     }
     __syncthreads();
     fast = fast && (T.fail == 0);
+    if (fast) {
+        for (int i = threadIdx.x; i < kBuckets * kCopies; i += THREADS) T.row[i] = T.master[i / kCopies];
+    }
+    __syncthreads();
 
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
     const char* tab = reinterpret_cast<const char*>(T.row);

@@ -29,10 +29,11 @@ constexpr int kCopies = 16;
 constexpr float kDelta = 0x1p-18f;  // bucket window half-width in q
 constexpr uint64_t kNoMid = ~uint64_t(0);  // marks a failed search (never an M: bits 1:0 of M are 0)
 
-// Bucket rows and the per-threshold M (fp64 bits).
+// Bucket rows, their master copy, and the per-threshold M (fp64 bits).
 template <int C>
 struct ThresholdTables {
     u32x4 row[kBuckets * kCopies];  // {M, planes(below), planes(above)} per copy
+    u32x4 master[kBuckets];
     uint64_t mid[C];                // mid[i]: threshold between codes i-1 and i
     float code[C];                  // the codebook (exact path)
     int fail;
@@ -196,14 +197,6 @@ __device__ bool build_entry(const float (&c)[C], const uint64_t* mid, int j, flo
     e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), planes(static_cast<uint32_t>(below)),
               planes(above)};
     return meets <= 1;
-}
-
-// Writes bucket j's entry into its kCopies rows, starting at copy j mod
-// kCopies, so that the lanes of one store cover all banks.
-template <int C>
-__device__ __forceinline__ void store_bucket_copies(ThresholdTables<C>& T, int j, const u32x4& e) {
-#pragma unroll
-    for (int k = 0; k < kCopies; ++k) T.row[j * kCopies + ((k + j) & (kCopies - 1))] = e;
 }
 
 // Byte address of the lane's copy of q's bucket entry: byte 1 <- bits
