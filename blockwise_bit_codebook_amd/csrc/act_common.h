@@ -106,11 +106,16 @@ __device__ __forceinline__ ActPlan build_act_tables(ActTables& T, const float* _
     // leaves the sentinel, which fails the table below.
     {
         const int groups = 2 * nthreads / kWave;
-        const int gid = 2 * static_cast<int>(threadIdx.x / kWave) + (lane >> 5);
+        const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
         for (int i0 = 1; i0 < 16; i0 += groups) {  // uniform trip count
-            const int i = i0 + gid;
+            // the wave's thresholds ib and ib + 1 from three uniform (scalar)
+            // loads: per-lane loads would wait behind the first row's loads
+            const int ib = i0 + 2 * wave;
+            const float a = cb[min(ib - 1, 15)], b = cb[min(ib, 15)], d = cb[min(ib + 1, 15)];
+            const bool upper = lane >= 32;
+            const int i = ib + (upper ? 1 : 0);
             const bool real = i < 16;
-            const float lo = real ? cb[i - 1] : 0.0f, hi = real ? cb[i] : 0.0f;
+            const float lo = real ? (upper ? b : a) : 0.0f, hi = real ? (upper ? d : b) : 0.0f;
             uint64_t m = 0;
             const bool ok = threshold_mid_group<32>(lo, hi, m);  // every lane calls it
             if (real && (lane & 31) == 0) T.mid[i] = (fast && lo != hi) ? (ok ? m : kNoMid) : 0u;
