@@ -205,6 +205,15 @@ def test_k_sweep_bf16_full(K):
     check_quantize(x, "bf16", codebooks.nf(K), K, 32, "k sweep")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+@pytest.mark.parametrize("K", [2, 3, 5])
+def test_k_sweep_fp16_fp32_blocksize64(dtype, K):
+    # 2^22 + 77 N(0,1) elements, blocksize 64 (the configuration of the
+    # input-type x K measurements); every word checked
+    x = synth.normal((1 << 22) + 77, seed=500 + K, dtype=dtype)
+    check_quantize(x, dtype, codebooks.nf(K), K, 64, f"k sweep {dtype}")
+
+
 def test_determinism_and_input_immutability():
     import torch
     x = synth.k_sweep_bf16(n=(1 << 20) + 5)
