@@ -125,7 +125,6 @@ __host__ __device__ __forceinline__ int pair_index(int b, int s0) {
 // store_row must be executed by all 64 lanes of the wave for fp32.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float float8 __attribute__((ext_vector_type(8)));
 
 // 16-byte global load, optionally marked non-temporal (streamed once).
 template <bool NT>
@@ -143,13 +142,11 @@ __device__ __forceinline__ void store16(void* p, const u32x4& v) {
     else *q = v;
 }
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct Fp32 {
     using storage = float;
-    static constexpr int kBytes = 4;
     static constexpr int kVec = 2;  // 16-byte vectors per 8 elements
     // element offset (from the row start) of the lane's vector v
     __device__ static int vec_offset(int lane, int v) { return 256 * v + 8 * (lane & 31) + 4 * (lane >> 5); }
@@ -224,7 +221,6 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 
 struct Bf16 {
     using storage = uint16_t;
-    static constexpr int kBytes = 2;
     static constexpr int kVec = 1;
     __device__ static void unpack(const u32x4* r, float* x) {
 #pragma unroll
@@ -254,7 +250,6 @@ struct Bf16 {
 
 struct Fp16 {
     using storage = uint16_t;
-    static constexpr int kBytes = 2;
     static constexpr int kVec = 1;
     __device__ static float h2f(uint32_t bits16) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
