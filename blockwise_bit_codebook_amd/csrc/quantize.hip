@@ -11,8 +11,10 @@
 //
 // How (this kernel's own design, not the pages' warp-per-32 layout):
 //   * Each lane owns 8 consecutive elements (one 16-byte load for 16-bit
-//     types), so a wave covers 512 elements = 16 groups of 32 and a lane
-//     produces one byte of each plane word of its group.  The four lanes of
+//     types; for fp32 two 16-byte loads, each covering 1 KiB of the wave
+//     row, put in place with v_permlane32_swap), so a wave covers 512
+//     elements = 16 groups of 32 and a lane produces one byte of each plane
+//     word of its group.  The four lanes of
 //     a quad exchange bytes (DPP + v_perm) and store their group's K words
 //     as consecutive dwords: one coalesced store per wave.
 //   * Block absmax as an integer max of the magnitude bits (16-bit types two
@@ -30,12 +32,17 @@
 //     encode the round-to-even direction of an exact tie.  M*s has at most
 //     49 significant bits, so one fp64 fma gives the sign of x - M*s
 //     exactly, and the nudge is far below the smallest nonzero |x - M*s|.
+//     For 16-bit inputs (values and block maxima of at most 11 significant
+//     bits) M is held as an fp32 pair and two fp32 fmas give that sign
+//     (threshold.h, pair_bits).
 //     To know which threshold to test, each element computes
 //     q = fma(x, 0.99*rcp(s), 2.99 + 2^-10), an approximation of an affine
 //     image of x_n inside (2, 4); bits 16..22 of q pick one of 128 buckets.
 //     A bucket's entry holds the M of the one threshold whose window
 //     [t - 2^-18, t + 2^-18] (in q) meets the bucket (q's error is below
-//     2^-21) and the plane bytes of the indices on either side.  Codebooks
+//     2^-21) and the plane bytes of the indices on either side (K = 5:
+//     plane 4 in bit 1 of byte 0, gathered by two accumulation chains of
+//     even and odd elements).  Codebooks
 //     that are unsorted, leave [-1, 1], have close distinct neighbours, or
 //     put two windows into one bucket, and blocks whose scale is not finite
 //     or above 2^125, take the exact path: IEEE division and the full
@@ -49,8 +56,9 @@
 //     entry points ([QLORA-2] PATCH 005), as its one-byte E4M4 code; the
 //     indices come from the fp32 absmax either way.
 //   * Persistent grid of 1024-thread workgroups (16 waves, at most 64 VGPRs
-//     so two groups share a CU); each wave walks its tiles with the next
-//     tile's load in flight while the current one is classified.
+//     so two groups share a CU; 512 threads for K = 5); each wave walks its
+//     steps (two wave rows for 16-bit inputs, one for fp32) with the next
+//     step's loads in flight while the current one is classified.
 #include "device.h"
 #include "e4m4.h"
 #include "kbit_internal.h"
