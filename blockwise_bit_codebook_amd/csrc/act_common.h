@@ -73,14 +73,28 @@ struct ActPlan {
     float slope;
 };
 
-// Builds T for the codebook cb.  Every thread of the workgroup calls it
-// (nthreads = blockDim.x, a multiple of 64 and at least 128); it holds
-// barriers.
-__device__ __forceinline__ ActPlan build_act_tables(ActTables& T, const float* __restrict__ cb, int nthreads) {
+// The table build in three stages, for kernels that interleave it with
+// other work between their own barriers.  Every thread of the workgroup
+// (nthreads = blockDim.x, a multiple of 64 and at least 128) runs each
+// stage, and a workgroup barrier separates stage 1 from 2, 2 from 3, and 3
+// from the first use of the tables.
+struct ActBuild {
+    float c[16];
+    bool fast;
+    float slope;
+};
+
+// Stage 1: codebook checks, bucket slope, and the switching points (T.mid).
+__device__ __forceinline__ void act_tables_search(ActTables& T, const float* __restrict__ cb, int nthreads,
+                                                  ActBuild& B) {
     const int lane = __lane_id();
+    // A local copy for the indexed store into T.code below (indexing the
+    // struct's array would put it in scratch memory).
     float c[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = cb[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) B.c[i] = c[i];
     bool fast = true;
 #pragma unroll
     for (int i = 1; i < 16; ++i) fast = fast && (c[i] == c[i - 1] || c[i] - c[i - 1] >= kActMinGap);
@@ -103,7 +117,7 @@ __device__ __forceinline__ ActPlan build_act_tables(ActTables& T, const float* _
     if (threadIdx.x == 0) T.fail = 0;
     if (threadIdx.x < 16) T.code[threadIdx.x] = c[threadIdx.x];
     // One half-wave per threshold, all searched at once; a failed search
-    // leaves the sentinel, which fails the table below.
+    // leaves the sentinel, which fails the table.
     {
         const int groups = 2 * nthreads / kWave;
         const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x / kWave));
@@ -122,20 +136,39 @@ __device__ __forceinline__ ActPlan build_act_tables(ActTables& T, const float* _
         }
     }
     if (threadIdx.x == 0) T.mid[0] = 0;
-    __syncthreads();
+    B.fast = fast;
+    B.slope = slope;
+}
+
+// Stage 2: failed searches, and the bucket entries (T.master).
+__device__ __forceinline__ void act_tables_entries(ActTables& T, const ActBuild& B) {
     if (threadIdx.x < 16 && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
-    if (fast && threadIdx.x < kBuckets) {
+    if (B.fast && threadIdx.x < kBuckets) {
         u32x4 e;
-        if (!build_entry<16, false>(c, T.mid, threadIdx.x, slope, kActBase, e)) T.fail = 1;
+        if (!build_entry<16, false>(B.c, T.mid, threadIdx.x, B.slope, kActBase, e)) T.fail = 1;
         T.master[threadIdx.x] = e;
     }
-    __syncthreads();
-    fast = fast && (T.fail == 0);
+}
+
+// Stage 3: whether the fast path applies, and the bank-spread copies.
+__device__ __forceinline__ ActPlan act_tables_copies(ActTables& T, const ActBuild& B, int nthreads) {
+    const bool fast = B.fast && (T.fail == 0);
     if (fast) {
         for (int i = threadIdx.x; i < kBuckets * kCopies; i += nthreads) T.row[i] = T.master[i / kCopies];
     }
+    return ActPlan{fast, B.slope};
+}
+
+// Builds T for the codebook cb: the three stages with their barriers.
+__device__ __forceinline__ ActPlan build_act_tables(ActTables& T, const float* __restrict__ cb, int nthreads) {
+    ActBuild B;
+    act_tables_search(T, cb, nthreads, B);
     __syncthreads();
-    return ActPlan{fast, slope};
+    act_tables_entries(T, B);
+    __syncthreads();
+    const ActPlan plan = act_tables_copies(T, B, nthreads);
+    __syncthreads();
+    return plan;
 }
 
 // Indices of the 16 transformed values v of a row with norm `norm`, as two

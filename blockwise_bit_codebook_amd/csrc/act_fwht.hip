@@ -82,8 +82,13 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     uint4 cur_a, cur_b;
     load_raw(static_cast<int64_t>(blockIdx.x) * kSlots + slot, cur_a, cur_b);
 
-    // ---- table build (once per workgroup) ---------------------------------
-    const ActPlan plan = build_act_tables(T, cb, kActThreads);
+    // The table build (once per workgroup) runs in the first iteration, its
+    // three stages between the butterfly passes, so that it shares their
+    // barriers and overlaps their work.  Every workgroup has at least one
+    // row (the grid is at most ceil(rows / kSlots)).
+    ActBuild tb;
+    ActPlan plan{false, 0.0f};
+    bool first = true;  // uniform
 
     // Sign flips as XOR masks on the raw bf16 words: element 2i is the low
     // half of word i (sign bit 15), element 2i+1 the high half (bit 31).
@@ -130,6 +135,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
             S = S + shfl_xor_f32(S, 32);
             if (lane == 0) ws[wave] = S;
         }
+        if (first) act_tables_search(T, cb, kActThreads, tb);
         // --- pass 1 (bits 0-3), to LDS -----------------------------------------
         fwht_pts<16>(v);
 #pragma unroll
@@ -137,6 +143,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
             *reinterpret_cast<float4*>(rb + seg + 4 * (k ^ sw)) = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2],
                                                                               v[4 * k + 3]);
         __syncthreads();
+        if (first) act_tables_entries(T, tb);
         const float norm = sqrtf((ws[0] + ws[1]) + (ws[2] + ws[3]));
         // --- pass 2 (bits 4-7): elements hi4*256 + i*16 + lo4 ---------------
         {
@@ -147,6 +154,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
             for (int i = 0; i < kPer; ++i) rb[swz(hi4, i, lo4)] = v[i];
         }
         __syncthreads();
+        if (first) plan = act_tables_copies(T, tb, kActThreads);
         // --- pass 3 (bits 8-11): elements i*256 + t --------------------------
         {
 #pragma unroll
@@ -181,6 +189,7 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
             }
         }
         __syncthreads();  // the row buffer and wave sums are reused
+        first = false;
     }
 }
 
