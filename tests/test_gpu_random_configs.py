@@ -1,0 +1,60 @@
+"""GPU parity over seeded random configurations: input type, K, blocksize,
+ragged length, magnitude and codebook kind (NF, random sorted, sorted with a
+repeated entry, unsorted) drawn per seed.  Quantize (words and absmax) and
+the dequantize of the kernel's own words are compared bit for bit with the
+oracle."""
+
+import numpy as np
+import pytest
+
+import blockwise_bit_codebook_amd as kb
+from blockwise_bit_codebook_amd import synth
+from oracle import codebooks, kbit, numerics
+from tests.gpu_util import assert_bits_equal, bits, case, np_bits, to_dev
+from tests.test_gpu_dequantize import _tdt
+
+pytestmark = pytest.mark.gpu
+
+
+def _codebook(rng, kind, K):
+    C = 1 << K
+    if kind == "nf":
+        return codebooks.nf(K)
+    c = np.sort(rng.uniform(-1.0, 1.0, C)).astype(np.float32)
+    if kind == "sorted":
+        return c
+    if kind == "repeat":                       # two equal neighbours
+        j = int(rng.integers(1, C))
+        c[j] = c[j - 1]
+        return c
+    return rng.permutation(c).astype(np.float32)  # unsorted: the exact path
+
+
+def _config(seed):
+    rng = np.random.default_rng(seed)
+    dtype = ["fp32", "fp16", "bf16"][int(rng.integers(3))]
+    K = int(rng.integers(2, 6))
+    B = 1 << int(rng.integers(5, 13))
+    n = int(rng.integers(1, 300_000))
+    kind = ["nf", "nf", "sorted", "repeat", "unsorted"][int(rng.integers(5))]
+    sigma = float(10.0 ** rng.uniform(-3, 1))
+    return rng, dtype, K, B, n, kind, sigma
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_config(seed):
+    import torch
+    rng, dtype, K, B, n, kind, sigma = _config(seed)
+    cb = _codebook(rng, kind, K)
+    x = synth.normal(n, seed=9000 + seed, dtype=dtype, sigma=sigma)
+    case(f"random config seed={seed} dtype={dtype} K={K} B={B} n={n} codebook={kind} sigma={sigma:.3g}")
+    packed, absmax = kb.quantize_kbit(to_dev(x, dtype), to_dev(cb), K, B)
+    torch.cuda.synchronize()
+    words, am = bits(packed), bits(absmax)
+    want_w, want_a = kbit.quantize_packed(numerics.widen(x, dtype), cb, K, B)
+    assert_bits_equal(am, np_bits(want_a), "absmax")
+    assert_bits_equal(words, want_w, "words")
+    out = kb.dequantize_kbit(packed, to_dev(cb), absmax, K, n, _tdt(dtype), B)
+    torch.cuda.synchronize()
+    want = kbit.dequantize_packed(want_w, want_a, cb, K, n, B, dtype)
+    assert_bits_equal(bits(out), np_bits(want), "dequantize")
