@@ -2,14 +2,14 @@
 ragged length, magnitude and codebook kind (NF, random sorted, sorted with a
 repeated entry, unsorted) drawn per seed.  Quantize (words and absmax) and
 the dequantize of the kernel's own words are compared bit for bit with the
-oracle."""
+oracle, with fp32 and with E4M4 block scales."""
 
 import numpy as np
 import pytest
 
 import blockwise_bit_codebook_amd as kb
 from blockwise_bit_codebook_amd import synth
-from oracle import codebooks, kbit, numerics
+from oracle import codebooks, e4m4, kbit, numerics
 from tests.gpu_util import assert_bits_equal, bits, case, np_bits, to_dev
 from tests.test_gpu_dequantize import _tdt
 
@@ -41,7 +41,7 @@ def _config(seed):
     return rng, dtype, K, B, n, kind, sigma
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(96))
 def test_random_config(seed):
     import torch
     rng, dtype, K, B, n, kind, sigma = _config(seed)
@@ -57,4 +57,22 @@ def test_random_config(seed):
     out = kb.dequantize_kbit(packed, to_dev(cb), absmax, K, n, _tdt(dtype), B)
     torch.cuda.synchronize()
     want = kbit.dequantize_packed(want_w, want_a, cb, K, n, B, dtype)
+    assert_bits_equal(bits(out), np_bits(want), "dequantize")
+
+
+@pytest.mark.parametrize("seed", range(1000, 1048))
+def test_random_config_e4m4_scales(seed):
+    import torch
+    rng, dtype, K, B, n, kind, sigma = _config(seed)
+    cb = _codebook(rng, kind, K)
+    x = synth.normal(n, seed=9000 + seed, dtype=dtype, sigma=sigma)
+    case(f"random config e4m4 seed={seed} dtype={dtype} K={K} B={B} n={n} codebook={kind} sigma={sigma:.3g}")
+    packed, code = kb.quantize_kbit(to_dev(x, dtype), to_dev(cb), K, B, absmax_format="e4m4")
+    torch.cuda.synchronize()
+    want_w, want_c = e4m4.quantize_packed(numerics.widen(x, dtype), cb, K, B)
+    assert_bits_equal(bits(code), want_c, "e4m4 codes")
+    assert_bits_equal(bits(packed), want_w, "words")
+    out = kb.dequantize_kbit(packed, to_dev(cb), code, K, n, _tdt(dtype), B)
+    torch.cuda.synchronize()
+    want = e4m4.dequantize(kbit.unpack(want_w, K, n), want_c, cb, B, dtype)
     assert_bits_equal(bits(out), np_bits(want), "dequantize")
