@@ -76,3 +76,31 @@ def test_random_config_e4m4_scales(seed):
     torch.cuda.synchronize()
     want = e4m4.dequantize(kbit.unpack(want_w, K, n), want_c, cb, B, dtype)
     assert_bits_equal(bits(out), np_bits(want), "dequantize")
+
+
+@pytest.mark.parametrize("seed", range(2000, 2032))
+def test_random_config_nested(seed):
+    # quantize (K = 4) -> nested state of the block absmax -> fused nested
+    # dequantize, all on the GPU; every stage against the oracle
+    import torch
+    from oracle import nested
+    rng, dtype, _, B, n, kind, sigma = _config(seed)
+    cb = codebooks.nf(4) if kind in ("nf", "unsorted") else _codebook(rng, "sorted", 4)
+    q = codebooks.dynamic_map8()
+    x = synth.normal(n, seed=9000 + seed, dtype=dtype, sigma=sigma)
+    case(f"random config nested seed={seed} dtype={dtype} B={B} n={n} sigma={sigma:.3g}")
+    packed, absmax = kb.quantize_kbit(to_dev(x, dtype), to_dev(cb), 4, B)
+    code, a2, off = kb.quantize_nested_absmax(absmax, to_dev(q))
+    torch.cuda.synchronize()
+    want_w, want_a = kbit.quantize_packed(numerics.widen(x, dtype), cb, 4, B)
+    assert_bits_equal(bits(packed), want_w, "words")
+    assert_bits_equal(bits(absmax), np_bits(want_a), "absmax")
+    wc, wa2, woff = nested.encode(want_a, q)
+    assert bits(off)[0] == np.float32(woff).view(np.uint32), "offset"
+    assert_bits_equal(bits(a2), np_bits(wa2), "absmax2")
+    assert_bits_equal(bits(code), wc, "codes")
+    out = kb.dequantize_4bit_nested(packed, to_dev(cb), code, to_dev(q), a2, float(np.float32(woff)), n,
+                                    _tdt(dtype), B)
+    torch.cuda.synchronize()
+    want = nested.dequantize_packed(want_w, wc, wa2, np.float32(woff), q, cb, n, B, dtype)
+    assert_bits_equal(bits(out), np_bits(want), "nested dequantize")
