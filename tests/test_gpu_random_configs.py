@@ -2,7 +2,9 @@
 ragged length, magnitude and codebook kind (NF, random sorted, sorted with a
 repeated entry, unsorted) drawn per seed.  Quantize (words and absmax) and
 the dequantize of the kernel's own words are compared bit for bit with the
-oracle, with fp32 and with E4M4 block scales."""
+oracle, with fp32 and with E4M4 block scales; the nested chain (quantize,
+nested-state encode, fused nested dequantize) and the activation
+assignment (random width, rows, codebook scale, permutation) likewise."""
 
 import numpy as np
 import pytest
@@ -104,3 +106,18 @@ def test_random_config_nested(seed):
     torch.cuda.synchronize()
     want = nested.dequantize_packed(want_w, wc, wa2, np.float32(woff), q, cb, n, B, dtype)
     assert_bits_equal(bits(out), np_bits(want), "nested dequantize")
+
+
+@pytest.mark.parametrize("seed", range(3000, 3040))
+def test_random_config_activation(seed):
+    # random width (a multiple of 256 up to 16384, so Hadamard blocks of
+    # 256 .. 16384), row count, codebook scale and optional permutation
+    from tests.test_gpu_act import check_act
+    rng = np.random.default_rng(seed)
+    d = 256 * int(rng.integers(1, 65))
+    rows = int(rng.integers(1, 48))
+    scale = float(2.0 ** rng.uniform(-6, 3))
+    cb = (codebooks.lloyd_max_normal(16) * np.float32(scale)).astype(np.float32)
+    x, s = synth.activations_bf16(tokens=rows, d=d, seed=seed)
+    perm = rng.permutation(d) if rng.integers(2) else None
+    check_act(x, s, cb, f"random seed={seed} scale={scale:.3g}", perm=perm)
