@@ -4,7 +4,8 @@ repeated entry, unsorted) drawn per seed.  Quantize (words and absmax) and
 the dequantize of the kernel's own words are compared bit for bit with the
 oracle, with fp32 and with E4M4 block scales; the nested chain (quantize,
 nested-state encode, fused nested dequantize) and the activation
-assignment (random width, rows, codebook scale, permutation) likewise."""
+assignment (random width, rows, codebook scale, permutation) likewise; the
+fused 4-bit linear (random M, N, K, blocksize) within its fp32-sum bound."""
 
 import numpy as np
 import pytest
@@ -121,3 +122,23 @@ def test_random_config_activation(seed):
     x, s = synth.activations_bf16(tokens=rows, d=d, seed=seed)
     perm = rng.permutation(d) if rng.integers(2) else None
     check_act(x, s, cb, f"random seed={seed} scale={scale:.3g}", perm=perm)
+
+
+@pytest.mark.parametrize("seed", range(4000, 4024))
+def test_random_config_linear(seed):
+    # random M, N, K (a multiple of 32) and blocksize; the fp32-sum bound of
+    # the fused 4-bit linear against the exact products
+    from oracle import linear
+    from tests.test_gpu_linear import _check, _state, run_plain
+    rng = np.random.default_rng(seed)
+    M = int(rng.integers(1, 81))
+    N = int(rng.integers(1, 201))
+    K = 32 * int(rng.integers(1, 65))
+    B = 1 << int(rng.integers(5, 9))
+    case(f"random config linear seed={seed} M={M} N={N} K={K} B={B}")
+    cb, words, absmax = _state(N, K, B, seed=seed)
+    xb = synth.normal(M * K, seed=seed, dtype="bf16").reshape(M, K)
+    got = run_plain(xb, words, cb, absmax, N, K, B)
+    wb = linear.weights_bf16(words, cb, N, K, B, absmax=absmax)
+    ref, absum = linear.reference(xb, wb)
+    _check(got, ref, absum, K, f"random linear seed={seed}")
