@@ -64,3 +64,54 @@ def test_graph_replays_match_eager_and_oracle():
         assert np.array_equal(bits(packed), ref[0]), r
         assert np.array_equal(bits(absmax), ref[1]), r
         assert np.array_equal(bits(out), ref[2]), r
+
+
+@pytest.mark.parametrize("dtype,K", [("fp16", 5), ("fp32", 5), ("fp32", 3), ("bf16", 2), ("fp16", 4)])
+def test_graph_replays_other_types(dtype, K):
+    # quantize + plain dequantize of other input types and K (two-row
+    # 16-bit steps, the fp32 wave-row layout, K = 5's plane-4 chains)
+    # captured once and replayed; every replay equals the eager run and the
+    # oracle
+    import torch
+    from oracle import numerics
+    from tests.test_gpu_dequantize import _tdt
+    B = 64
+    x = synth.weight(1024, 1024, dtype, seed=synth.SEED_WEIGHT_SHAPES, extra=synth.TAIL_EXTRA)
+    n = x.size
+    nb = kb.n_blocks(n, B)
+    cb = to_dev(codebooks.nf(K))
+    A = to_dev(x, dtype)
+    packed = torch.empty(kb.n_words(n, K), dtype=torch.int32, device="cuda")
+    absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
+    out = torch.empty(n, dtype=_tdt(dtype), device="cuda")
+
+    def step():
+        kb.quantize_kbit(A, cb, K, B, absmax=absmax, packed=packed)
+        kb.dequantize_kbit(packed, cb, absmax, K, n, _tdt(dtype), B, out=out)
+
+    case(f"graph {dtype} K={K}: eager reference")
+    step()
+    torch.cuda.synchronize()
+    ref = (bits(packed), bits(absmax), bits(out))
+    want_w, want_a = kbit.quantize_packed(numerics.widen(x, dtype), codebooks.nf(K), K, B)
+    assert np.array_equal(ref[0], want_w)
+    assert np.array_equal(ref[1], np_bits(want_a))
+    assert np.array_equal(ref[2], np_bits(kbit.dequantize_packed(want_w, want_a, codebooks.nf(K), K, n, B, dtype)))
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    scratch = torch.empty_like(packed)
+    for r in range(3):
+        case(f"graph {dtype} K={K}: replay {r}")
+        packed.zero_()
+        absmax.zero_()
+        out.zero_()
+        kb.quantize_kbit(A, cb, K, B, packed=scratch)     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(packed), ref[0]), r
+        assert np.array_equal(bits(absmax), ref[1]), r
+        assert np.array_equal(bits(out), ref[2]), r
