@@ -278,14 +278,9 @@ int launch_block_t(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_
     const int rt = slots == 1 ? 1024 : slots == 2 ? 512 : kRowThreads;
     const int threads = slots * rt;
     const size_t dyn = static_cast<size_t>(slots) * row_bytes;
-    // workgroups per CU, by d / 256 (same answer for every caller)
-    static int per_cu_cache[kMaxChunks + 1] = {};
-    int per_cu = per_cu_cache[d >> 8];
-    if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, dyn) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        per_cu_cache[d >> 8] = per_cu;
-    }
+    // workgroups per CU, by d / 256 and device (same answer for every caller)
+    static std::atomic<int> per_cu_cache[kMaxChunks + 1][kMaxDevices];
+    const int per_cu = cached_blocks_per_cu(kern, threads, per_cu_cache[d >> 8], dyn);
     int64_t grid = (rows + slots - 1) / slots;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     if (grid > cap) grid = cap;

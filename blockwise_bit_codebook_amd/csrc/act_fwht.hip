@@ -198,12 +198,8 @@ int launch_act_slots(const uint16_t* X, int64_t rows, const uint32_t* sign_bits,
                      float* row_norm, uint32_t* packed, void* stream) {
     constexpr int kActThreads = kRowThreads * kSlots;
     auto kern = act_fwht_kernel<kSlots>;
-    static int blocks_per_cu = 0;
-    if (blocks_per_cu == 0) {
-        int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, kActThreads, 0) != hipSuccess || b < 1) b = 1;
-        blocks_per_cu = b;
-    }
+    static std::atomic<int> occupancy[kMaxDevices];
+    const int blocks_per_cu = cached_blocks_per_cu(kern, kActThreads, occupancy);
     int64_t grid = (rows + kSlots - 1) / kSlots;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
     if (grid > cap) grid = cap;

@@ -15,8 +15,6 @@ namespace kbit {
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
-constexpr int kMaxDevices = 64;
-
 // Per-device CU count; 0 = not probed, -1 = not a gfx950 device.
 std::atomic<int> g_cus[kMaxDevices];
 
@@ -130,6 +128,12 @@ constexpr int64_t kMaxNestedBlocks = int64_t(1) << 36;
 int device_cu_count() {
     const int v = current_device_cus();
     return v > 0 ? v : 1;
+}
+
+int current_device_index() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    return dev;
 }
 
 }  // namespace kbit

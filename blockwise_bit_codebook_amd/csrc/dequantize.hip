@@ -246,8 +246,8 @@ template <class E, int K, class Scale>
 int launch_plain(const uint32_t* packed, const float* cb, Scale scale, void* out, int64_t n, int log2B,
                  void* stream) {
     auto kern = dequantize_kernel<E, K, Scale>;
-    static int blocks_per_cu = 0;
-    const int64_t grid = persistent_grid(kern, blocks_per_cu, (n + kWaveTile * kSteps - 1) / (kWaveTile * kSteps));
+    static std::atomic<int> occupancy[kMaxDevices];
+    const int64_t grid = persistent_grid(kern, occupancy, (n + kWaveTile * kSteps - 1) / (kWaveTile * kSteps));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), packed, cb, scale,
                        static_cast<typename E::storage*>(out), n, log2B);
@@ -258,8 +258,8 @@ template <class E, int U = kSteps, bool NTS = kNtStore>
 int launch_nested(const uint32_t* packed, const float* cb, const uint8_t* code, const float* qmap2,
                   const float* absmax2, float offset, void* out, int64_t n, int log2B, void* stream) {
     auto kern = dequantize_nested_kernel<E, U, NTS>;
-    static int blocks_per_cu = 0;
-    const int64_t grid = persistent_grid(kern, blocks_per_cu, (n + kWaveTile * U - 1) / (kWaveTile * U));
+    static std::atomic<int> occupancy[kMaxDevices];
+    const int64_t grid = persistent_grid(kern, occupancy, (n + kWaveTile * U - 1) / (kWaveTile * U));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), packed, cb, code, qmap2, absmax2, offset,
                        static_cast<typename E::storage*>(out), n, log2B);

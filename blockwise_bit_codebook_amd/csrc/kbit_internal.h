@@ -43,8 +43,13 @@ bool act_block_supported(int d);
 int launch_act_block(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits, const int32_t* perm,
                      const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
 
-// Number of workgroups that fill the current device for a kernel whose
-// per-CU residency is `blocks_per_cu`.  Returns 0 if no device is usable.
+// CU count of the current device (at least 1).
 int device_cu_count();
+
+// Ordinal of the current device, or -1 if none can be queried.
+int current_device_index();
+
+// Largest device ordinal + 1 that the per-device caches hold.
+constexpr int kMaxDevices = 64;
 
 }  // namespace kbit

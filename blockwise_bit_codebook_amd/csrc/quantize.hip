@@ -62,8 +62,10 @@
 #include "device.h"
 #include "e4m4.h"
 #include "kbit_internal.h"
+#include "launch.h"
 #include "threshold.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace kbit {
@@ -75,6 +77,7 @@ constexpr float kSlope = 0.99f;                          // q = kBase + kSlope *
 constexpr float kBase = 2.0f + kSlope + 0x1p-10f;        // keeps q inside (2, 4)
 constexpr float kMinGap = 0x1p-16f;                      // closest distinct neighbours (fast path)
 constexpr float kMaxFastScale = 0x1p125f;
+constexpr int kBufNonTemporal = 2;                      // cache policy of streamed loads (nt)
 
 using Tables = ThresholdTables<32>;
 // First-index nearest code by a full scan.  c is the codebook in LDS; the
@@ -141,21 +144,41 @@ __device__ __forceinline__ Codes classify_exact(const float* c, const float (&x)
 }
 
 
-// Whether the table holds switching points in the fp32 pair form (decide32):
-// 16-bit inputs, whose values and block maxima have at most 11 significant
-// bits.
-template <class E, int K>
-constexpr bool kPairForm = !std::is_same<E, Fp32>::value;
+// The form of the switching points in the table (threshold.h): one fp32 T
+// for bf16 (values and block maxima with 8 significant bits), the fp32 pair
+// for fp16 (11 bits), fp64 M for fp32 inputs.
+template <class E>
+constexpr int kForm = std::is_same<E, Bf16>::value ? kT32 : (std::is_same<E, Fp16>::value ? kPair32 : kMid64);
+
+// All ones if the decision value is negative ("lower code"), else zero.  The
+// value is never -0 for the inputs of its form, and +0 (possible only in the
+// T form, where x = T*s exactly) means "upper", so the sign bit decides.
+__device__ __forceinline__ uint32_t lower_mask(float t) { return static_cast<uint32_t>(__float_as_int(t) >> 31); }
+__device__ __forceinline__ uint32_t lower_mask(double t) {
+    return static_cast<uint32_t>(static_cast<int32_t>(__double_as_longlong(t) >> 32) >> 31);
+}
 
 template <class E, int K>
 __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, float r, const char* tab,
                                                uint32_t lane_off) {
     Codes out;
     const double s64 = static_cast<double>(s);
+    // Plane bytes of the entry's lower or upper index, picked by the sign of
+    // x - M*s (bit operations, no compare-and-select).
     auto sel = [&](int t) {
         const float q = __builtin_fmaf(x[t], r, kBase);
-        const Decision d = kPairForm<E, K> ? decide32(x[t], q, s, tab, lane_off) : decide(x[t], q, s64, tab, lane_off);
-        return d.up ? d.e[3] : d.e[2];
+        const u32x4 e = *reinterpret_cast<const u32x4*>(tab + entry_addr(q, lane_off));
+        uint32_t lower;
+        if constexpr (kForm<E> == kT32) {
+            lower = lower_mask(__builtin_fmaf(-__uint_as_float(e[0]), s, x[t]));
+        } else if constexpr (kForm<E> == kPair32) {
+            const float t1 = __builtin_fmaf(-__uint_as_float(e[0]), s, x[t]);
+            lower = lower_mask(__builtin_fmaf(-__uint_as_float(e[1]), s, t1));
+        } else {
+            const double M = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(e[1]) << 32) | e[0]));
+            lower = lower_mask(__builtin_fma(-M, s64, static_cast<double>(x[t])));
+        }
+        return (lower & e[2]) | (~lower & e[3]);
     };
     if constexpr (K <= 4) {
         // Elements 7..0: each step shifts the accumulated plane bits up by
@@ -178,42 +201,48 @@ __device__ __forceinline__ Codes classify_fast(const float (&x)[8], float s, flo
     return out;
 }
 
-// Classify one lane row (8 elements) against the block's max magnitude m
-// and store the quad's plane words.  FULL: all 512 elements of the wave row
-// are below n (no masking, every store unconditional).
-template <class E, int K, bool FULL>
-__device__ __forceinline__ void encode_row(bool fast, const Tables& T, const char* tab,
-                                           uint32_t lane_off, int lane, const float (&x)[8], float m,
-                                           int64_t row_base, int64_t n, uint32_t* __restrict__ packed) {
+// Classify one lane row (8 elements) against the block's max magnitude m.
+template <class E, int K>
+__device__ __forceinline__ Codes classify_row(bool fast, const Tables& T, const char* tab, uint32_t lane_off,
+                                              const float (&x)[8], float m) {
     const float s = __builtin_elementwise_maximum(m, kAbsmaxEps);  // NaN stays NaN (exact path)
-    // The pair form needs s = m (a 16-bit value); a clamped s = 1e-8f is
+    // The fp32 forms need s = m (a 16-bit value); a clamped s = 1e-8f is
     // fine only for an all-zero block, whose x = 0 decides every threshold
     // by a wide margin.
-    const bool lane_ok = kPairForm<E, K> ? (s < kMaxFastScale && (m >= kAbsmaxEps || m == 0.0f))
-                                         : (s < kMaxFastScale);
-    Codes cd;
-    if (fast && !__builtin_amdgcn_ballot_w64(!lane_ok)) {
-        cd = classify_fast<E, K>(x, s, __builtin_amdgcn_rcpf(s) * kSlope, tab, lane_off);
-    } else {
-        cd = classify_exact<K>(T.code, x, s);
-    }
-    bool live = true;
-    if constexpr (!FULL) {
-        const int64_t rem = n - (row_base + static_cast<int64_t>(lane) * kElemsPerLane);
-        const uint32_t valid = rem >= kElemsPerLane ? 0xFFu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
-        cd.acc &= valid * 0x01010101u;
-        cd.acc4 &= valid;
-        live = row_base + (lane >> 2) * kGroup < n;
-    }
+    const bool lane_ok = kForm<E> != kMid64 ? (s < kMaxFastScale && (m >= kAbsmaxEps || m == 0.0f))
+                                            : (s < kMaxFastScale);
+    if (fast && !__builtin_amdgcn_ballot_w64(!lane_ok))
+        return classify_fast<E, K>(x, s, __builtin_amdgcn_rcpf(s) * kSlope, tab, lane_off);
+    return classify_exact<K>(T.code, x, s);
+}
+
+// The plane-4 word of the lane's group (K = 5): the quad's four plane-4
+// bytes gathered into every lane of the quad.
+__device__ __forceinline__ uint32_t plane4_word(uint32_t acc4, int lane) {
+    uint32_t w4 = acc4 << (8 * (lane & 3));
+    w4 |= dpp_u32<kDppXor1>(w4);
+    w4 |= dpp_u32<kDppXor2>(w4);
+    return w4;
+}
+
+// Classify a row that ends past n and store the quad's plane words (masked:
+// plane bits of positions past n are 0, groups past n are not stored).
+template <class E, int K>
+__device__ __forceinline__ void encode_partial_row(bool fast, const Tables& T, const char* tab,
+                                                   uint32_t lane_off, int lane, const float (&x)[8], float m,
+                                                   int64_t row_base, int64_t n, uint32_t* __restrict__ packed) {
+    Codes cd = classify_row<E, K>(fast, T, tab, lane_off, x, m);
+    const int64_t rem = n - (row_base + static_cast<int64_t>(lane) * kElemsPerLane);
+    const uint32_t valid = rem >= kElemsPerLane ? 0xFFu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
+    cd.acc &= valid * 0x01010101u;
+    cd.acc4 &= valid;
+    const bool live = row_base + (lane >> 2) * kGroup < n;
     const uint32_t word = quad_transpose_bytes(cd.acc, lane);
-    uint32_t* dst_row = packed + (row_base / kGroup) * K;  // wave-uniform
-    uint32_t* dst = dst_row + (lane >> 2) * K;
+    uint32_t* dst = packed + (row_base / kGroup) * K + (lane >> 2) * K;  // row part wave-uniform
     const int l = lane & 3;
-    if (K == 4 ? live : (l < K && live)) dst[l] = word;
+    if (l < K && live) dst[l] = word;
     if constexpr (K == 5) {
-        uint32_t w4 = cd.acc4 << (8 * l);
-        w4 |= dpp_u32<kDppXor1>(w4);
-        w4 |= dpp_u32<kDppXor2>(w4);
+        const uint32_t w4 = plane4_word(cd.acc4, lane);
         if (l == 0 && live) dst[4] = w4;
     }
 }
@@ -276,9 +305,21 @@ struct E4m4Scale {
     __device__ static uint8_t encode(float m) { return static_cast<uint8_t>(e4m4_encode(m)); }
 };
 
+// Raw buffer resource over `bytes` bytes at p: loads past it read 0 and
+// stores past it are dropped, without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
+// Wave rows kept in flight per wave: 4 KB of input per wave, i.e. 4 rows of
+// 16-bit values or 2 rows of fp32.  With 32 waves per CU and 32 CUs per XCD
+// that is the 4 MB of one XCD's L2; deeper rings measured far slower.
+template <class E>
+constexpr int kRing = E::kVec == 1 ? 4 : 2;
+
 // LOG2B = log2(B) for B <= 512 (blocks inside a wave row); LOG2B = 0 for
 // B = 1024..4096 (blocks spanning rows; log2B from the argument).
-template <class E, class S, int K, int LOG2B, int ROWS, bool NT, int THREADS, int PFD>
+template <class E, class S, int K, int LOG2B, int THREADS>
 __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restrict__ cb,
                                                              const typename E::storage* __restrict__ A,
                                                              typename S::type* __restrict__ absmax,
@@ -286,43 +327,58 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     constexpr int C = 1 << K;
     constexpr int kV = E::kVec;
     constexpr int kWaves_ = THREADS / kWave;
+    constexpr int D = LOG2B != 0 ? kRing<E> : 1;
+    constexpr int kRowBytes = kWaveTile * static_cast<int>(sizeof(typename E::storage));
     __shared__ Tables T;
 
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWaves_;
+    const int64_t vwave = static_cast<int64_t>(blockIdx.x) * kWaves_ + wave;  // this wave's first row
 
-    // Row-tile geometry (B <= 512) and the wave's first loads, issued before
-    // the table build so that their latency overlaps it.
-    constexpr int kStep = kWaveTile * ROWS;
-    const int64_t nfull = LOG2B != 0 ? n / kStep : 0;
+    // Full wave rows (B <= 512).  Wave v takes rows v, v + nwaves, ..., so at
+    // any moment the whole grid works through one narrow window of memory.
+    // Each row's loads and stores go through a buffer resource of the row's
+    // bytes, or of 0 bytes for a row index past the last full row: those
+    // loads and stores are issued like any other but touch nothing, so every
+    // pass of the ring below runs the same straight-line code.
+    const int64_t nfull = LOG2B != 0 ? n / kWaveTile : 0;
     const int lane_e = lane * kElemsPerLane;
-    int64_t st = static_cast<int64_t>(blockIdx.x) * kWaves_ + wave;
-    u32x4 ra[ROWS][kV], rb[ROWS][kV];
-    auto load_full = [&](int64_t i, u32x4 (&r)[ROWS][kV]) {
-        const typename E::storage* src = A + i * kStep;  // wave-uniform
+    u32x4 buf[D][kV];
+    int64_t row[D];
+    auto load_full_row = [&](int64_t r, u32x4 (&raw)[kV]) {
+        const bool valid = r < nfull;
+        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(A + (valid ? r : 0) * kWaveTile, valid ? kRowBytes : 0);
 #pragma unroll
-        for (int u = 0; u < ROWS; ++u) load_row<E, NT>(src + u * kWaveTile, lane, n, true, r[u]);
+        for (int v = 0; v < kV; ++v)
+            raw[v] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs, E::vec_offset(lane, v) * static_cast<int>(sizeof(typename E::storage)),
+                                                   0, kBufNonTemporal));
     };
-    // The first two steps' loads go out before the table build.
-    if (LOG2B != 0 && st < nfull) load_full(st, ra);
-    if (LOG2B != 0 && PFD == 1 && st < nfull) load_full(min(st + nwaves, nfull - 1), rb);
+    if constexpr (LOG2B != 0) {
+        // the ring's first rows go out before the table build
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            row[d] = vwave + d * nwaves;
+            load_full_row(row[d], buf[d]);
+        }
+    }
 
+    // Codebook, switching points and the bucket table.
     float c[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) c[i] = cb[i];
-
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
     if (threadIdx.x < C) T.code[threadIdx.x] = c[threadIdx.x];
-    // The switching points: one wave per threshold, or one half-wave where
-    // there are more thresholds than waves (the search is cooperative); a
-    // failed search leaves the sentinel, which fails the table below.
+    // One wave per threshold, or one half-wave where there are more
+    // thresholds than waves (the search is cooperative); a failed search
+    // leaves the sentinel, which fails the table below.
     if constexpr (C - 1 <= kWaves_) {
         for (int i = wave + 1; i < C; i += kWaves_) {  // wave-uniform
             const float lo = cb[i - 1], hi = cb[i];
             uint64_t m = 0;
-            if (fast && lo != hi && !threshold_mid_wave<kPairForm<E, K>>(lo, hi, m)) m = kNoMid;
+            if (fast && lo != hi && !threshold_mid_wave<kForm<E>>(lo, hi, m)) m = kNoMid;
             if (lane == 0) T.mid[i] = m;
         }
     } else {
@@ -335,112 +391,86 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
             const bool real = i < C;
             const float lo = real ? (upper ? b : a) : 0.0f, hi = real ? (upper ? d : b) : 0.0f;
             uint64_t m = 0;
-            const bool ok = threshold_mid_group<32, kPairForm<E, K>>(lo, hi, m);  // every lane calls it
+            const bool ok = threshold_mid_group<32, kForm<E>>(lo, hi, m);  // every lane calls it
             if (real && (lane & 31) == 0) T.mid[i] = (fast && lo != hi) ? (ok ? m : kNoMid) : 0u;
         }
     }
     if (threadIdx.x == 0) T.mid[0] = 0;
     __syncthreads();
-    if (threadIdx.x < C && T.mid[threadIdx.x] == kNoMid) T.fail = 1;
-    if (fast && threadIdx.x < kBuckets) {
-        u32x4 e;
-        if (!build_entry<C, K == 5>(c, T.mid, threadIdx.x, kSlope, kBase, e)) T.fail = 1;
-        T.master[threadIdx.x] = e;
-    }
+    if (fast && !build_entries_parallel<C, K == 5, THREADS>(T.code, T.mid, kSlope, kBase, T.row)) T.fail = 1;
     __syncthreads();
     fast = fast && (T.fail == 0);
-    if (fast) {
-        for (int i = threadIdx.x; i < kBuckets * kCopies; i += THREADS) T.row[i] = T.master[i / kCopies];
-    }
-    __syncthreads();
 
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
     const char* tab = reinterpret_cast<const char*>(T.row);
 
     if constexpr (LOG2B != 0) {
         static_assert(LOG2B >= 5 && LOG2B <= 9, "rows hold whole blocks of 32..512");
-        // Steps of ROWS wave rows (512 elements each); blocks of B <= 512
-        // lie inside a row.  Full steps alternate between two register
-        // buffers: the next step's rows load while this step's are
-        // classified (the prefetch index is clamped, so the load is always
-        // issued and the loop has no data-dependent branches).  The one
-        // partial step, if any, goes last.
         constexpr int kLpb = (1 << LOG2B) / kElemsPerLane;  // lanes per block
-        const int64_t nsteps = (n + kStep - 1) / kStep;
-        // Encoded scales of a full two-row step are encoded once for both
-        // rows: even lanes carry row 0's block max, odd lanes row 1's (each
-        // block spans at least 4 lanes), and every lane stores its byte.
-        constexpr bool kPairScales = ROWS == 2 && S::kEncoded;
-        auto do_step = [&](int64_t i, const u32x4 (&r)[ROWS][kV], auto full_tag) {
-            constexpr bool kFull = decltype(full_tag)::value;
-            float m_prev = 0.0f;
+        constexpr int kBlocksPerRow = kWaveTile >> LOG2B;
+        constexpr int kScaleBytes = static_cast<int>(sizeof(typename S::type));
+        constexpr int kWordsPerRow = kWaveTile / kGroup * K;
+        const int l = lane & 3;
+        // byte offsets of the lane's stores inside its row; lanes without a
+        // word to store aim past the resource, so their store is dropped
+        const int scale_off = (lane_e >> LOG2B) * kScaleBytes;
+        const int word_off = l < K ? ((lane >> 2) * K + l) * 4 : (1 << 30);
+        const int w4_off = l == 0 ? ((lane >> 2) * K + 4) * 4 : (1 << 30);
+        auto do_row = [&](int64_t r, const u32x4 (&raw)[kV]) {
+            const bool valid = r < nfull;
+            const int64_t rr = valid ? r : 0;
+            const __amdgpu_buffer_rsrc_t am_rs =
+                buf_rsrc(absmax + rr * kBlocksPerRow, valid ? kBlocksPerRow * kScaleBytes : 0);
+            const __amdgpu_buffer_rsrc_t pk_rs = buf_rsrc(packed + rr * kWordsPerRow, valid ? kWordsPerRow * 4 : 0);
+            float x[8];
+            E::unpack(raw, x);
+            const float m = block_max_abs<kLpb>(x);
+            if constexpr (S::kEncoded)
+                __builtin_amdgcn_raw_buffer_store_b8(S::encode(m), am_rs, scale_off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), am_rs, scale_off, 0, 0);
+            const Codes cd = classify_row<E, K>(fast, T, tab, lane_off, x, m);
+            __builtin_amdgcn_raw_buffer_store_b32(quad_transpose_bytes(cd.acc, lane), pk_rs, word_off, 0, 0);
+            if constexpr (K == 5)
+                __builtin_amdgcn_raw_buffer_store_b32(plane4_word(cd.acc4, lane), pk_rs, w4_off, 0, 0);
+        };
+        // One pass over the ring: each slot's row is classified and the slot
+        // reloaded with the wave's row D rows later.  The first pass is
+        // peeled, so that the loop is entered with the same memory
+        // operations outstanding from both sides and the compiler's wait
+        // counts stay exact (a merge of differing states makes it wait for
+        // nearly every load).
+        auto ring_pass = [&]() {
 #pragma unroll
-            for (int u = 0; u < ROWS; ++u) {
-                const int64_t base = i * kStep + u * kWaveTile;
-                float x[8];
-                E::unpack(r[u], x);
-                const float m = block_max_abs<kLpb>(x);
-                if constexpr (kFull && kPairScales) {
-                    if (u == 0) {
-                        m_prev = m;
-                    } else {
-                        const int odd = lane & 1;
-                        typename S::type* am = absmax + ((i * kStep) >> LOG2B);  // wave-uniform
-                        am[odd * (kWaveTile >> LOG2B) + (lane_e >> LOG2B)] = S::encode(odd ? m : m_prev);
-                    }
-                } else {
-                    typename S::type* am = absmax + (base >> LOG2B);  // wave-uniform
-                    if (kFull || ((lane & (kLpb - 1)) == 0 && base + lane_e < n)) am[lane_e >> LOG2B] = S::encode(m);
-                }
-                encode_row<E, K, kFull>(fast, T, tab, lane_off, lane, x, m, base, n, packed);
+            for (int d = 0; d < D; ++d) {
+                do_row(row[d], buf[d]);
+                row[d] += D * nwaves;
+                load_full_row(row[d], buf[d]);
             }
         };
-        if (st < nfull) {
-            if constexpr (PFD == 1) {
-                bool first = true;  // rb already holds the second step
-                while (true) {
-                    if (!first) load_full(min(st + nwaves, nfull - 1), rb);
-                    first = false;
-                    do_step(st, ra, std::true_type{});
-                    st += nwaves;
-                    if (st >= nfull) break;
-                    load_full(min(st + nwaves, nfull - 1), ra);
-                    do_step(st, rb, std::true_type{});
-                    st += nwaves;
-                    if (st >= nfull) break;
-                }
-            } else {
-                // two steps in flight: three buffers in rotation
-                u32x4 rc[ROWS][kV];
-                load_full(min(st + nwaves, nfull - 1), rb);
-                while (true) {
-                    load_full(min(st + 2 * nwaves, nfull - 1), rc);
-                    do_step(st, ra, std::true_type{});
-                    st += nwaves;
-                    if (st >= nfull) break;
-                    load_full(min(st + 2 * nwaves, nfull - 1), ra);
-                    do_step(st, rb, std::true_type{});
-                    st += nwaves;
-                    if (st >= nfull) break;
-                    load_full(min(st + 2 * nwaves, nfull - 1), rb);
-                    do_step(st, rc, std::true_type{});
-                    st += nwaves;
-                    if (st >= nfull) break;
-                }
-            }
+        if (row[0] < nfull) {
+            ring_pass();
+            while (row[0] < nfull) ring_pass();
         }
-        if (st == nfull && nfull < nsteps) {
-            u32x4 r[ROWS][kV];
-#pragma unroll
-            for (int u = 0; u < ROWS; ++u) load_row<E, false>(A + st * kStep + u * kWaveTile, lane, n - (st * kStep + u * kWaveTile), false, r[u]);
-            do_step(st, r, std::false_type{});
+        // The one partial row, if any, goes to the wave whose sequence
+        // reaches it.
+        if (nfull * kWaveTile < n && vwave == nfull % nwaves) {
+            const int64_t base = nfull * kWaveTile;
+            u32x4 raw[kV];
+            load_row<E, false>(A + base, lane, n - base, false, raw);
+            float x[8];
+            E::unpack(raw, x);
+            const float m = block_max_abs<kLpb>(x);
+            typename S::type* am = absmax + (base >> LOG2B);  // wave-uniform
+            if ((lane & (kLpb - 1)) == 0 && base + lane_e < n) am[lane_e >> LOG2B] = S::encode(m);
+            encode_partial_row<E, K>(fast, T, tab, lane_off, lane, x, m, base, n, packed);
         }
     } else {
-        // One block of B = 1024..4096 per step: max over its rows, then
+        // One block of B = 1024..4096 per wave step: max over its rows, then
         // re-read each row (an L2 hit) to classify.
         const int rows = 1 << (log2B - 9);
         const int64_t nblocks = (n + (1LL << log2B) - 1) >> log2B;
-        for (int64_t b = static_cast<int64_t>(blockIdx.x) * kWaves_ + wave; b < nblocks; b += nwaves) {
+        for (int64_t b = vwave; b < nblocks; b += nwaves) {
             const int64_t base = b << log2B;
             float ml = 0.0f;
             for (int u = 0; u < rows; ++u) {
@@ -460,30 +490,24 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
                 load_row<E, false>(A + rb, lane, n - rb, rb + kWaveTile <= n, raw);
                 float x[8];
                 E::unpack(raw, x);
-                encode_row<E, K, false>(fast, T, tab, lane_off, lane, x, m, rb, n, packed);
+                encode_partial_row<E, K>(fast, T, tab, lane_off, lane, x, m, rb, n, packed);
             }
         }
     }
 }
 
-// grid_mult > 1 launches that many times the resident number of
-// workgroups (each then walks fewer steps).
-template <class E, class S, int K, int LOG2B, int ROWS = 1, bool NT = true, int THREADS = kQThreads,
-          int PFD = 1>
+// Launch over a persistent grid: the resident workgroups of the device,
+// fewer when there are fewer wave rows (or blocks) than waves.
+template <class E, class S, int K, int LOG2B, int THREADS>
 int launch_cfg(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
-               void* stream, int grid_mult = 1) {
-    auto kern = quantize_kernel<E, S, K, LOG2B, ROWS, NT, THREADS, PFD>;
-    static int blocks_per_cu = 0;
-    if (blocks_per_cu == 0) {
-        int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kern, THREADS, 0) != hipSuccess || b < 1) b = 1;
-        blocks_per_cu = b;
-    }
-    const int64_t units = LOG2B == 0 ? ((n + (1LL << log2B) - 1) >> log2B)
-                                     : (n + kWaveTile * ROWS - 1) / (kWaveTile * ROWS);
+               void* stream) {
+    auto kern = quantize_kernel<E, S, K, LOG2B, THREADS>;
+    static std::atomic<int> occupancy[kMaxDevices];
+    const int blocks_per_cu = cached_blocks_per_cu(kern, THREADS, occupancy);
+    const int64_t units = LOG2B == 0 ? ((n + (1LL << log2B) - 1) >> log2B) : (n + kWaveTile - 1) / kWaveTile;
     constexpr int waves = THREADS / kWave;
     int64_t grid = (units + waves - 1) / waves;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu * grid_mult;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(THREADS), 0,
@@ -496,19 +520,16 @@ int launch_cfg(const float* cb, const void* A, void* absmax, uint32_t* packed, i
 template <class E, class S, int K>
 int launch_k(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
              void* stream) {
-    // Two wave rows per step for 16-bit inputs (32 bytes per lane in flight
-    // plus the prefetched step, within 64 VGPRs); one row for fp32.  K = 5
-    // runs 512-thread groups: its kernels need 60..70 VGPRs, and smaller
-    // groups fill the SIMDs' remaining wave slots.
-    constexpr int R = std::is_same<E, Fp32>::value ? 1 : 2;
+    // K = 5 runs 512-thread groups: its kernels need up to 64 VGPRs only
+    // with the smaller group, whose waves fill the SIMDs' remaining slots.
     constexpr int TH = K == 5 ? 512 : kQThreads;
     switch (log2B) {
-        case 5: return launch_cfg<E, S, K, 5, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 6: return launch_cfg<E, S, K, 6, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 7: return launch_cfg<E, S, K, 7, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 8: return launch_cfg<E, S, K, 8, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 9: return launch_cfg<E, S, K, 9, R, true, TH>(cb, A, absmax, packed, n, log2B, stream);
-        default: return launch_cfg<E, S, K, 0, 1, false, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 5: return launch_cfg<E, S, K, 5, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 6: return launch_cfg<E, S, K, 6, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 7: return launch_cfg<E, S, K, 7, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 8: return launch_cfg<E, S, K, 8, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 9: return launch_cfg<E, S, K, 9, TH>(cb, A, absmax, packed, n, log2B, stream);
+        default: return launch_cfg<E, S, K, 0, TH>(cb, A, absmax, packed, n, log2B, stream);
     }
 }
 

@@ -88,19 +88,77 @@ __device__ inline uint64_t pair_bits(float u, float p) {
     return static_cast<uint64_t>(__float_as_uint(p)) | (static_cast<uint64_t>(ml2) << 32);
 }
 
+// One fp32 value T for the switching point u (predecessor p) of bf16
+// inputs, for the decision RN(x/s) >= u  <=>  x - T*s >= 0 (one fma, exact
+// sign).  x and s (a block maximum) are bf16 values, so x/s = (mx/ms) 2^d
+// with 8-bit significands mx, ms; two distinct such quotients differ by at
+// least 2^-17 relative, while [p, u] is at most 2^-23 wide, so at most one
+// of them, q*, lies in [p, u].  T = u classifies every quotient outside
+// [p, u] correctly, and so does T = p; the one q* picks: T = p if q* lies in
+// (M, u] (it must go up), or equals M = (p + u)/2 with the tie rounding to
+// u; T = u otherwise (q* in [p, M) must go down).  The lanes of the group
+// (G = 32 or 64) test the 128 significands ms of s: the only candidate
+// numerator is mx = round(M ms 2^-d) with d putting it into [128, 255],
+// checked exactly against [p, u] with fp64 products.  Returns kNoMid when
+// |M| is outside [2^-100, 2] (the exact path then applies).  Every lane of
+// the wave must call it.
+template <int G>
+__device__ inline uint64_t tform_bits_group(float u, float p) {
+    const uint32_t lane = __lane_id();
+    const uint32_t i = lane % G;
+    const uint32_t gshift = G == 64 ? 0u : (lane / G) * 32u;
+    auto group_any = [&](bool b) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(b);
+        return (G == 64 ? m : ((m >> gshift) & 0xFFFFFFFFull)) != 0;
+    };
+    const double M = (static_cast<double>(u) + static_cast<double>(p)) * 0.5;  // exact
+    const bool tie_up = static_cast<float>(M) == u;
+    const double A = fabs(M);
+    const bool ok = A >= 0x1p-100 && A <= 2.0;
+    const double au = fabs(static_cast<double>(u)), ap = fabs(static_cast<double>(p));
+    const double lo_m = au < ap ? au : ap, hi_m = au < ap ? ap : au;
+    const int kk = ok ? static_cast<int>((__double_as_longlong(A) >> 52) & 0x7FF) - 1023 : 0;
+    bool below = false, eq = false, above = false;
+#pragma unroll
+    for (int h = 0; h < 128 / G; ++h) {
+        const double ms = static_cast<double>(128 + i + G * h);
+        const double am = A * ms;                       // exact: 25 + 8 bits
+        int d = kk;
+        double P = ldexp(am, -d);                       // in [128, 512)
+        if (P >= 256.0) {
+            d += 1;
+            P *= 0.5;
+        }
+        double mx = floor(P + 0.5);                     // P + 0.5 is exact
+        if (mx == 256.0) {
+            mx = 128.0;
+            d += 1;
+        }
+        const double num = ldexp(mx, d);                // |x/s| * ms, exact
+        const bool in = ok && mx >= 128.0 && mx <= 255.0 && lo_m * ms <= num && num <= hi_m * ms;
+        below = below || (in && num < am);
+        eq = eq || (in && num == am);
+        above = above || (in && num > am);
+    }
+    below = group_any(below);
+    eq = group_any(eq);
+    above = group_any(above);
+    const bool q_above = M > 0.0 ? above : below;       // a quotient in (M, u]
+    const float T = eq ? (tie_up ? p : u) : (q_above ? p : u);
+    return ok ? static_cast<uint64_t>(__float_as_uint(T)) : kNoMid;
+}
+
+// Forms of a switching point in the tables (the entry's first two words):
+//   kMid64  - M as fp64 (any fp32 x and s): sign of fma(-M, s, x)
+//   kPair32 - {Mh, Ml'} (x, s with at most 11 significant bits: bf16, fp16):
+//             sign of fma(-Ml', s, fma(-Mh, s, x))
+//   kT32    - {T, 0} (bf16 x and s): sign of fma(-T, s, x)
+// In every form the decision value is never zero for the inputs it serves,
+// so "upper code" is exactly "sign bit clear".
+constexpr int kMid64 = 0, kPair32 = 1, kT32 = 2;
+
 // M for the threshold between codes lo < hi, found by a group of G lanes
-// (G = 32 or 64; lane group lane / G searches its own lo, hi).  The choice
-// is monotone in x_n on [lo, hi], so u is found by searching the fp32
-// values in between in key order (near a midpoint of 0, u can lie far from
-// the midpoint, where the rounded distances tie).  The first round tests
-// the G keys centred on the fp32 midpoint, where u almost always lies;
-// then every round the lanes test G evenly spaced keys of the bracket
-// [L, R], which shrinks to the two neighbouring tested keys where the
-// choice changes (2^32 keys take at most 7 rounds of 32).  The loop runs
-// until every group of the wave is done, so all lanes of the wave must
-// call it; each lane gets its group's result.  Returns false if the bracket
-// is not as expected.
-template <int G, bool PAIR32 = false>
+template <int G, int FORM = kMid64>
 __device__ inline bool threshold_mid_group(float lo, float hi, uint64_t& bits) {
     static_assert(G == 32 || G == 64, "lane groups of 32 or 64");
     const uint32_t lane = __lane_id();
@@ -152,7 +210,10 @@ __device__ inline bool threshold_mid_group(float lo, float hi, uint64_t& bits) {
             }
         }
     }
-    if constexpr (PAIR32) {
+    if constexpr (FORM == kT32) {
+        bits = tform_bits_group<G>(from_key(R), from_key(L));  // every lane of the wave calls it
+        return ok && bits != kNoMid;
+    } else if constexpr (FORM == kPair32) {
         bits = pair_bits(from_key(R), from_key(L));
         return ok && bits != kNoMid;
     } else {
@@ -162,9 +223,9 @@ __device__ inline bool threshold_mid_group(float lo, float hi, uint64_t& bits) {
 }
 
 // The same with the whole wave on one threshold.
-template <bool PAIR32 = false>
+template <int FORM = kMid64>
 __device__ inline bool threshold_mid_wave(float lo, float hi, uint64_t& bits) {
-    return threshold_mid_group<64, PAIR32>(lo, hi, bits);
+    return threshold_mid_group<64, FORM>(lo, hi, bits);
 }
 
 // Entry for bucket j (q in [2 + j/64, 2 + (j+1)/64)): the M of the one
@@ -197,6 +258,67 @@ __device__ bool build_entry(const float (&c)[C], const uint64_t* mid, int j, flo
     e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32), planes(static_cast<uint32_t>(below)),
               planes(above)};
     return meets <= 1;
+}
+
+// build_entry for all buckets at once, by every thread of a workgroup of
+// THREADS (512 or 1024) threads: THREADS / 128 consecutive lanes share a
+// bucket, each tests its slice of the thresholds, the slices combine with
+// DPP (below = max, cand = min, meets = sum), and each lane writes its share
+// of the kCopies copies of the entry into rows.  code and mid are the
+// codebook and the switching points in LDS (written before a barrier that
+// precedes this call).  Returns false in every lane of a bucket whose entry
+// is ambiguous (two windows meet it) or whose threshold search failed; the
+// caller folds that into the table's fail flag.
+template <int C, bool PLANE4, int THREADS>
+__device__ inline bool build_entries_parallel(const float* code, const uint64_t* mid, float slope, float base,
+                                              u32x4* rows) {
+    constexpr int kTpb = THREADS / kBuckets;                // threads per bucket
+    static_assert(kTpb == 4 || kTpb == 8, "512 or 1024 threads");
+    constexpr int kTpt = (C - 1 + kTpb - 1) / kTpb;          // thresholds per thread
+    const int j = threadIdx.x / kTpb, part = threadIdx.x % kTpb;
+    const float lo = 2.0f + static_cast<float>(j) * (2.0f / kBuckets);
+    const float hi = lo + (2.0f / kBuckets);
+    int below = 0, cand = C, meets = 0;
+    bool failed = false;
+#pragma unroll
+    for (int t = 0; t < kTpt; ++t) {
+        const int i = 1 + part * kTpt + t;
+        if (i < C) {
+            const float cl = code[i - 1], ch = code[i];
+            const bool distinct = ch != cl;
+            const float tp = base + ((cl + ch) * 0.5f) * slope;
+            const bool under = distinct && tp + kDelta <= lo;
+            const bool meet = distinct && !under && tp - kDelta < hi;
+            below = under ? i : below;                         // thresholds rise with i
+            cand = (meet && i < cand) ? i : cand;
+            meets += meet ? 1 : 0;
+            failed = failed || (distinct && mid[i] == kNoMid);
+        }
+    }
+    below = max(below, static_cast<int>(dpp_u32<kDppXor1>(below)));
+    below = max(below, static_cast<int>(dpp_u32<kDppXor2>(below)));
+    cand = min(cand, static_cast<int>(dpp_u32<kDppXor1>(cand)));
+    cand = min(cand, static_cast<int>(dpp_u32<kDppXor2>(cand)));
+    meets += static_cast<int>(dpp_u32<kDppXor1>(meets));
+    meets += static_cast<int>(dpp_u32<kDppXor2>(meets));
+    uint32_t f = failed ? 1u : 0u;
+    f |= dpp_u32<kDppXor1>(f);
+    f |= dpp_u32<kDppXor2>(f);
+    if constexpr (kTpb == 8) {
+        below = max(below, static_cast<int>(dpp_u32<kDppHalfMirror>(below)));
+        cand = min(cand, static_cast<int>(dpp_u32<kDppHalfMirror>(cand)));
+        meets += static_cast<int>(dpp_u32<kDppHalfMirror>(meets));
+        f |= dpp_u32<kDppHalfMirror>(f);
+    }
+    const uint32_t above = cand == C ? static_cast<uint32_t>(below) : static_cast<uint32_t>(cand);
+    const uint64_t m = cand == C ? 0u : mid[cand];
+    auto planes = [](uint32_t ix) { return spread4(ix & 15u) | (PLANE4 ? ((ix >> 4) & 1u) << 1 : 0u); };
+    const u32x4 e = u32x4{static_cast<uint32_t>(m), static_cast<uint32_t>(m >> 32),
+                          planes(static_cast<uint32_t>(below)), planes(above)};
+    constexpr int kCpt = kCopies / kTpb;                    // copies written per thread
+#pragma unroll
+    for (int k = 0; k < kCpt; ++k) rows[j * kCopies + kCpt * part + k] = e;
+    return meets <= 1 && f == 0;
 }
 
 // Byte address of the lane's copy of q's bucket entry: byte 1 <- bits
