@@ -121,9 +121,8 @@ KERNELS = {
     "quantize_kbit_e4m4_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "E4m4Scale, 4,"), _Q_SRC),
     "dequantize_kbit_e4m4_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "E4m4Scale>"), _D_SRC),
     "dequantize_kbit_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "PlainScale>"), _D_SRC),
-    # the nested-state encoder's three launches
+    # the nested-state encoder's two launches
     "nested_bins_kernel": (("::nested_bins_kernel",), _E_SRC),
-    "nested_offset_kernel": (("::nested_offset_kernel",), _E_SRC),
     "nested_encode_kernel": (("::nested_encode_kernel",), _E_SRC),
 }
 
@@ -796,8 +795,8 @@ def main(argv=None):
     e4["note"] = ("same 8192x8192 bf16 tensor and NF4 codebook; scales as one E4M4 byte per block "
                   "(the last entry: fp32 scales, for comparison)")
     enc = kstats(rr["quantize_nested_absmax"], kbytes["quantize_nested_absmax"], elems=nb)
-    enc["note"] = ("nested-state encoder on the 1,048,576 fp32 block absmax of the same tensor: three launches "
-                   "(significand sums, exact mean, codes); elements_per_s counts blocks")
+    enc["note"] = ("nested-state encoder on the 1,048,576 fp32 block absmax of the same tensor: two launches "
+                   "(exact significand sums; mean and codes); elements_per_s counts blocks")
 
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).

@@ -174,7 +174,8 @@ def dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offs
 def quantize_nested_absmax(absmax, qmap2, absmax_code=None, absmax2=None, offset=None, workspace=None):
     """Nested state of fp32 per-block absmax -> (absmax_code u8, absmax2 fp32, offset fp32[1]).
 
-    offset stays on the device; the workspace is allocated here unless given."""
+    offset stays on the device; the workspace (scratch) is allocated here
+    unless given."""
     torch = _torch()
     nb = absmax.numel()
     dev = absmax.device

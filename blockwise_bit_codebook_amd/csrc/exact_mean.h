@@ -1,7 +1,8 @@
 // Exact mean of fp32 values, rounded once to fp32 (round to nearest, ties
 // to even, gradual underflow).  Host and device code: the reduction kernels
-// produce per-(sign, exponent) sums of the values' integer significands;
-// this header turns them into the rounded mean.
+// add the values' integer significands, shifted by their exponents, into
+// 32-bit-limb accumulators of the positive and the negative values; this
+// header turns those into the rounded mean.
 //
 // A finite fp32 value with biased exponent e and fraction f is m * 2^-149
 // times 2^(max(e, 1) - 1), with m = f + 2^23 for e > 0 and m = f for e = 0.
@@ -36,108 +37,85 @@ KBIT_HD inline WidePieces wide_pieces(uint64_t v, int shift) {
     return WidePieces{shift >> 5, lo & 0xFFFFFFFFull, (lo >> 32) + (hi & 0xFFFFFFFFull), hi >> 32};
 }
 
-// X += v * 2^shift into uint64 limb accumulators (carries resolved later).
-KBIT_HD inline void wide_add_shifted(uint64_t (&acc)[kWideLimbs + 2], uint64_t v, int shift) {
-    const WidePieces q = wide_pieces(v, shift);
-    acc[q.w] += q.p0;
-    acc[q.w + 1] += q.p1;
-    acc[q.w + 2] += q.p2;
-}
-
-// All loops below have constant trip counts and constant limb indices, so
-// device code keeps the limbs in registers.
-
-// Propagates carries so that every limb is below 2^32.
-KBIT_HD inline void wide_normalize(uint64_t (&acc)[kWideLimbs + 2]) {
-    uint64_t carry = 0;
-#pragma unroll
-    for (int i = 0; i < kWideLimbs + 2; ++i) {
-        const uint64_t t = acc[i] + carry;
-        acc[i] = t & 0xFFFFFFFFull;
-        carry = t >> 32;
-    }
-}
-
-// a - b for a >= b (normalized limbs).
-KBIT_HD inline void wide_sub(uint64_t (&a)[kWideLimbs + 2], const uint64_t (&b)[kWideLimbs + 2]) {
-    int64_t borrow = 0;
-#pragma unroll
-    for (int i = 0; i < kWideLimbs + 2; ++i) {
-        const int64_t t = static_cast<int64_t>(a[i]) - static_cast<int64_t>(b[i]) - borrow;
-        borrow = t < 0 ? 1 : 0;
-        a[i] = static_cast<uint64_t>(t + (borrow << 32));
-    }
-}
-
-// -1, 0, +1 as a < b, a == b, a > b (normalized limbs).
-KBIT_HD inline int wide_cmp(const uint64_t (&a)[kWideLimbs + 2], const uint64_t (&b)[kWideLimbs + 2]) {
-    int r = 0;
-#pragma unroll
-    for (int i = 0; i < kWideLimbs + 2; ++i) {  // the highest differing limb decides
-        if (a[i] != b[i]) r = a[i] < b[i] ? -1 : 1;
-    }
-    return r;
-}
-
 KBIT_HD inline int bit_length64(uint64_t v) { return v ? 64 - __builtin_clzll(v) : 0; }
 
-// Bits [pos, pos + 64) of X (bits past the top read as 0; pos may be
-// negative, then the low bits are 0).
-KBIT_HD inline uint64_t wide_bits64(const uint64_t (&x)[kWideLimbs + 2], int pos) {
-    uint64_t r = 0;
+// fp32 bits of RN32((P - N) * 2^-149 / nb), 1 <= nb <= 2^36, from the limb
+// accumulators of P (positive values) and N (negative values): limb i
+// weighs 2^(32 i), each limb is below 2^61 (carries not yet resolved), and
+// |P - N| < 2^320.  Straight-line code for one thread: every array index is
+// a constant after unrolling.
+KBIT_HD inline uint32_t mean_from_limbs(const uint64_t (&pos)[kWideLimbs + 2], const uint64_t (&neg)[kWideLimbs + 2],
+                                        uint64_t nb) {
+    constexpr int L = kWideLimbs + 2;
+    // D = P - N as 32-bit digits plus a final carry (floor division by 2^32
+    // at each limb keeps every intermediate within int64).
+    uint32_t d[L];
+    int64_t carry = 0;
 #pragma unroll
-    for (int i = 0; i < kWideLimbs; ++i) {
-        const int sh = 32 * i - pos;  // where limb i lands in the result
-        if (sh >= 64 || sh <= -32) continue;
-        r |= sh >= 0 ? (x[i] << sh) : (x[i] >> -sh);
+    for (int i = 0; i < L; ++i) {
+        const int64_t t = static_cast<int64_t>(pos[i]) - static_cast<int64_t>(neg[i]) + carry;
+        d[i] = static_cast<uint32_t>(t);
+        carry = t >> 32;  // arithmetic shift: floor
     }
-    return r;
-}
-
-// True if any bit of X below position pos is set.
-KBIT_HD inline bool wide_any_below(const uint64_t (&x)[kWideLimbs + 2], int pos) {
-    bool any = false;
+    // |D| < 2^320, so the carry is -1 exactly when D < 0; then the digits
+    // hold 2^(32 L) + D and their two's complement is |D|.
+    const bool negative = carry < 0;
+    if (negative) {
+        uint64_t c = 1;
 #pragma unroll
-    for (int i = 0; i < kWideLimbs; ++i) {
-        const int below = pos - 32 * i;  // bits of limb i below pos
-        if (below >= 32) any = any || x[i] != 0;
-        else if (below > 0) any = any || (x[i] & ((1ull << below) - 1ull)) != 0;
-    }
-    return any;
-}
-
-// fp32 bits of RN32(sign * X * 2^-149 / nb), 1 <= nb <= 2^36.
-KBIT_HD inline uint32_t wide_mean_bits(const uint64_t (&x)[kWideLimbs + 2], bool negative, uint64_t nb) {
-    int p = 0;  // bit length of X
-#pragma unroll
-    for (int i = 0; i < kWideLimbs; ++i) {
-        if (x[i]) p = 32 * i + bit_length64(x[i]);
+        for (int i = 0; i < L; ++i) {
+            const uint64_t t = static_cast<uint64_t>(~d[i]) + c;
+            d[i] = static_cast<uint32_t>(t);
+            c = t >> 32;
+        }
     }
     const uint32_t sign = negative ? 0x80000000u : 0u;
-    if (p == 0) return sign;
-    // N = X * 2^-s with 63 bits; Q = N / nb then has at least 27 bits.
-    const int s = p - 63;
-    const uint64_t N = wide_bits64(x, s);
-    bool sticky = s > 0 && wide_any_below(x, s);
-    const uint64_t Q = N / nb;
-    sticky = sticky || (N % nb) != 0;
-    // value = (Q + fraction) * 2^(s - 149); exponent of its leading bit
+    // Highest nonzero digit `top`, the two below it, and whether any digit
+    // further down is nonzero.
+    int top = -1;
+    uint32_t h0 = 0, h1 = 0, h2 = 0;
+    bool low = false;
+    uint32_t below = 0;  // OR of the digits under the current i - 2
+#pragma unroll
+    for (int i = 0; i < kWideLimbs; ++i) {
+        if (d[i] != 0) {
+            top = i;
+            h0 = d[i];
+            h1 = i >= 1 ? d[i - 1] : 0u;
+            h2 = i >= 2 ? d[i - 2] : 0u;
+            low = below != 0;
+        }
+        if (i >= 2) below |= d[i - 2];
+    }
+    if (top < 0) return sign;
+    // |D| = W * 2^(32 (top - 2)) + (the lower digits), W = h0:h1:h2 (96
+    // bits, 64 + b of them significant).  Its leading 63 bits are
+    // Nq = W >> (b + 1), scaled by 2^s with s = 32 (top - 2) + b + 1; the
+    // bits shifted out and the lower digits only decide the sticky bit.
+    const int b = bit_length64(h0);  // 1..32
+    const uint64_t mid = (static_cast<uint64_t>(h1) << 32) | h2;
+    const uint64_t Nq = (static_cast<uint64_t>(h0) << (63 - b)) | (mid >> (b + 1));
+    const int s = 32 * (top - 2) + b + 1;
+    bool sticky = low || (mid & ((1ull << (b + 1)) - 1ull)) != 0;
+    // Q = Nq / nb has at least 27 bits; the value is (Q + fraction) * 2^s.
+    const uint64_t Q = Nq / nb;
+    sticky = sticky || (Nq % nb) != 0;
     const int qb = bit_length64(Q);
-    int E = qb - 1 + s - 149;
-    // drop d low bits of Q: down to 24 significant bits, or to the 2^-149
+    int E = qb - 1 + s - 149;  // exponent of the leading bit
+    // drop dq low bits of Q: down to 24 significant bits, or to the 2^-149
     // quantum in the subnormal range
-    const int d = E >= -126 ? qb - 24 : -s;
+    const int dq = E >= -126 ? qb - 24 : -s;
     if (E < -126) E = -127;  // subnormal (exponent field 0)
     uint64_t mant;
     bool guard;
-    if (d >= 64) {
+    if (dq >= 64) {
         mant = 0;
-        guard = d == 64 && (Q >> 63) != 0;
-        sticky = sticky || (d == 64 ? (Q & ~(1ull << 63)) != 0 : Q != 0);
+        guard = dq == 64 && (Q >> 63) != 0;
+        sticky = sticky || (dq == 64 ? (Q & ~(1ull << 63)) != 0 : Q != 0);
     } else {
-        mant = Q >> d;
-        guard = d > 0 && ((Q >> (d - 1)) & 1ull);
-        sticky = sticky || (d > 1 && (Q & ((1ull << (d - 1)) - 1ull)) != 0);
+        mant = Q >> dq;
+        guard = dq > 0 && ((Q >> (dq - 1)) & 1ull);
+        sticky = sticky || (dq > 1 && (Q & ((1ull << (dq - 1)) - 1ull)) != 0);
     }
     if (guard && (sticky || (mant & 1ull))) ++mant;
     if (E == -127) {
@@ -150,32 +128,6 @@ KBIT_HD inline uint32_t wide_mean_bits(const uint64_t (&x)[kWideLimbs + 2], bool
     }
     if (E > 127) return sign | 0x7F800000u;
     return sign | (static_cast<uint32_t>(E + 127) << 23) | (static_cast<uint32_t>(mant) & 0x7FFFFFu);
-}
-
-// Rounded mean from the limb accumulators of the positive and the negative
-// values (carries not yet resolved) and the count nb.
-KBIT_HD inline uint32_t mean_from_limbs(uint64_t (&pos)[kWideLimbs + 2], uint64_t (&neg)[kWideLimbs + 2],
-                                        uint64_t nb) {
-    wide_normalize(pos);
-    wide_normalize(neg);
-    if (wide_cmp(pos, neg) >= 0) {
-        wide_sub(pos, neg);
-        return wide_mean_bits(pos, false, nb);
-    }
-    wide_sub(neg, pos);
-    return wide_mean_bits(neg, true, nb);
-}
-
-// The same from per-(sign, exponent) significand sums S[2][256] (sign 0
-// positive, 1 negative; exponent 255 unused).
-KBIT_HD inline uint32_t mean_from_sums(const uint64_t (&S)[2][256], uint64_t nb) {
-    uint64_t pos[kWideLimbs + 2] = {}, neg[kWideLimbs + 2] = {};
-    for (int e = 0; e < 255; ++e) {
-        const int shift = (e > 0 ? e : 1) - 1;
-        if (S[0][e]) wide_add_shifted(pos, S[0][e], shift);
-        if (S[1][e]) wide_add_shifted(neg, S[1][e], shift);
-    }
-    return mean_from_limbs(pos, neg, nb);
 }
 
 }  // namespace kbit

@@ -12,18 +12,25 @@
 //   code_b      = smallest i minimising |RN(RN(r_b / max(absmax2_g, 1e-8f))
 //                 - qmap2_i)|
 //
-// How: three launches on one stream.
-//   1. Each workgroup adds the integer significands of its values into
-//      per-wave LDS bins by (sign, exponent) with 64-bit LDS atomics, folds
-//      the bins into 32-bit-limb accumulators of the positive and negative
-//      sums (exact_mean.h), and writes them and its NaN/infinity flags to
-//      the workspace: 25 words per workgroup.
-//   2. One workgroup adds the records (32 threads per word), resolves the
-//      carries of the 320-bit sums and rounds the mean once.
-//   3. One wave per group: four blocks per lane, IEEE division, and the
-//      nearest code by binary search over the sorted map plus a walk to the
-//      lowest index with the same rounded distance (a full scan if the map
-//      is not sorted).
+// How: two launches on one stream.
+//   1. Each workgroup sums its values exactly into 32-bit-limb
+//      accumulators of the positive and the negative values (exact_mean.h):
+//      per round of 16 values per lane, each wave adds the integer
+//      significands of the values within 24 binades of its largest one into
+//      64-bit register sums (shifted to the window's bottom), sums those
+//      across the wave and adds them to the limbs; values further down go to
+//      per-wave LDS bins by (sign, exponent), folded into the limbs at the
+//      end.  The limbs and the NaN/infinity flags go to the workspace: 25
+//      words per workgroup.
+//   2. Every workgroup (1024 threads, at most 512 workgroups) first adds
+//      the records (a half wave per word) and rounds the mean itself (the
+//      records are complete: they come from the previous launch); workgroup
+//      0 stores it.  Then one wave per group of 256 blocks: four blocks per
+//      lane, IEEE division, and the nearest code: a count over 15 map
+//      entries held in registers, a binary search in LDS inside the block
+//      of 16 it picks, and a walk to the lowest index with the same rounded
+//      distance (a full scan if the map is not sorted).
+// The workspace holds only the records (scratch, no initialisation).
 #include "device.h"
 #include "exact_mean.h"
 #include "kbit_internal.h"
@@ -36,7 +43,12 @@ constexpr int kBinWaves = kBinThreads / kWave;
 constexpr int kMaxBinGroups = 256;  // workgroups of launch 1 (the workspace holds one record each)
 constexpr int kLimbWords = kWideLimbs + 2;
 constexpr int kRecordWords = 2 * kLimbWords + 1;  // uint64: limbs[sign][i], then the flags
-constexpr int kOffsetParts = 32;                  // threads per record word in launch 2
+constexpr int kEncThreads = 1024;                       // launch 2: one group of 256 blocks per wave
+constexpr int kEncWaves = kEncThreads / kWave;
+constexpr int kEncMaxGrid = 512;                        // each workgroup of launch 2 re-reads the records
+constexpr int kOffsetParts = 32;                        // lanes per record word in the mean (a half wave)
+constexpr int kOffsetLoads = kMaxBinGroups / kOffsetParts;  // records per such lane
+static_assert(kRecordWords * kOffsetParts <= kEncThreads, "a half wave per record word");
 constexpr int kGroup2 = 256;
 constexpr float kEps2 = 1e-8f;
 constexpr uint32_t kFlagNan = 1, kFlagPosInf = 2, kFlagNegInf = 4;
@@ -46,37 +58,151 @@ int bin_groups(int64_t nb) {
     return static_cast<int>(g < 1 ? 1 : (g > kMaxBinGroups ? kMaxBinGroups : g));
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    return (static_cast<uint64_t>(dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
+           dpp_u32<CTRL>(static_cast<uint32_t>(v));
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+
+// Sum over the wave (every lane active), returned uniform: DPP within each
+// row of 16 lanes, then the four row totals read out.
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+    v += dpp_u64<kDppXor1>(v);
+    v += dpp_u64<kDppXor2>(v);
+    v += dpp_u64<kDppHalfMirror>(v);
+    v += dpp_u64<kDppMirror>(v);
+    uint64_t t = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        t += (static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(v >> 32), 16 * r)) << 32) |
+             readlane_u32(static_cast<uint32_t>(v), 16 * r);
+    }
+    return t;
+}
+
+// Maximum over the wave (every lane active), returned uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppXor1>(v));
+    v = max(v, dpp_u32<kDppXor2>(v));
+    v = max(v, dpp_u32<kDppHalfMirror>(v));
+    v = max(v, dpp_u32<kDppMirror>(v));
+    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
+}
+
+constexpr int kBinVecs = 4;     // 16-byte loads per lane per round (16 values)
+constexpr int kWindowBits = 24;  // binades below the wave's top one that the register sums take
+
+// Launch 1.  Per round a wave holds 16 values per lane.  A finite nonzero
+// value with biased exponent e and integer significand m is m * 2^(e' - 1)
+// in units of 2^-149, e' = max(e, 1).  With E the wave's largest e' and
+// e0 = max(E - 24, 1), every value with e' >= e0 adds m << (e' - e0) (below
+// 2^48) to the register sum of its sign, in units of 2^(e0 - 1); the wave's
+// two sums (below 2^58) go into the workgroup's limb accumulators once per
+// round.  Values further down (more than 24 binades below the wave's top)
+// add m to a per-wave LDS bin of their sign and e.  NaN and infinities only
+// set flags.
 __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* __restrict__ a, int64_t nb,
                                                                   uint64_t* __restrict__ ws) {
     __shared__ unsigned long long bins[kBinWaves][2][256];
+    __shared__ unsigned long long limbs[2][kLimbWords];
     __shared__ uint32_t flags;
     const int wave = threadIdx.x / kWave;
+    const int lane = __lane_id();
+    uint32_t my_flags = 0;
+    // Values past nb (and a tail not in whole vectors) read as 0, which adds
+    // nothing; the round loop is uniform over the wave (the sums use every
+    // lane).
+    const int64_t nvec = nb / 4, nvec_all = (nb + 3) / 4;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBinThreads;
+    const u32x4* av = reinterpret_cast<const u32x4*>(a);
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(a) & 15u) == 0;
+    const auto load_round = [&](int64_t wb, u32x4 (&u)[kBinVecs]) {
+#pragma unroll
+        for (int k = 0; k < kBinVecs; ++k) {
+            const int64_t vi = wb + lane + k * stride;
+            if (aligned16 && vi < nvec) {
+                u[k] = av[vi];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) u[k][c] = 4 * vi + c < nb ? __float_as_uint(a[4 * vi + c]) : 0u;
+            }
+        }
+    };
+    // the first round's loads are in flight while the LDS is cleared
+    int64_t wb = static_cast<int64_t>(blockIdx.x) * kBinThreads + wave * kWave;
+    u32x4 u[kBinVecs];
+    load_round(wb, u);
     for (int i = threadIdx.x; i < kBinWaves * 2 * 256; i += kBinThreads) (&bins[0][0][0])[i] = 0;
+    if (threadIdx.x < 2 * kLimbWords) (&limbs[0][0])[threadIdx.x] = 0;
     if (threadIdx.x == 0) flags = 0;
     __syncthreads();
-    uint32_t my_flags = 0;
-    // four independent loads in flight per thread
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kBinThreads;
-    for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * kBinThreads + threadIdx.x; i0 < nb; i0 += 4 * stride) {
-        uint32_t u[4];
+    for (; wb < nvec_all; wb += kBinVecs * stride) {
+        if (wb != static_cast<int64_t>(blockIdx.x) * kBinThreads + wave * kWave) load_round(wb, u);
+        uint32_t top = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) u[k] = i0 + k * stride < nb ? __float_as_uint(a[i0 + k * stride]) : 0u;
+        for (int k = 0; k < kBinVecs; ++k) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t e = (u[k] >> 23) & 0xFFu, f = u[k] & 0x7FFFFFu, sg = u[k] >> 31;
-            if (e == 0xFFu) {
-                my_flags |= f ? kFlagNan : (sg ? kFlagNegInf : kFlagPosInf);
-            } else if (e | f) {
-                atomicAdd(&bins[wave][sg][e], static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t e = (u[k][c] >> 23) & 0xFFu;
+                if (e != 0xFFu && (u[k][c] & 0x7FFFFFFFu) != 0) top = max(top, max(e, 1u));
+            }
+        }
+        top = wave_max_u32(top);
+        const uint32_t e0 = top > kWindowBits + 1 ? top - kWindowBits : 1u;
+        // branch-free for the values in the window; the rest (rare) after
+        uint64_t sum_pos = 0, sum_neg = 0;
+        uint32_t slow = 0;
+#pragma unroll
+        for (int k = 0; k < kBinVecs; ++k) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t x = u[k][c];
+                const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
+                const bool neg = (x >> 31) != 0, special = e == 0xFFu;
+                my_flags |= special ? (f ? kFlagNan : (neg ? kFlagNegInf : kFlagPosInf)) : 0u;
+                const uint32_t ee = max(e, 1u), m = e ? (f | 0x800000u) : f;  // m = 0 for zeros
+                const bool fast = !special && ee >= e0;
+                const uint64_t t = static_cast<uint64_t>(fast ? m : 0u) << (fast ? ee - e0 : 0u);
+                sum_neg += neg ? t : 0ull;
+                sum_pos += neg ? 0ull : t;
+                slow |= (!special && !fast && m != 0) ? (1u << (4 * k + c)) : 0u;
+            }
+        }
+        if (slow != 0) {
+#pragma unroll
+            for (int k = 0; k < kBinVecs; ++k) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (slow & (1u << (4 * k + c))) {
+                        const uint32_t x = u[k][c];
+                        const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
+                        atomicAdd(&bins[wave][x >> 31][e], static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
+                    }
+                }
+            }
+        }
+        sum_pos = wave_sum_u64(sum_pos);
+        sum_neg = wave_sum_u64(sum_neg);
+        if (lane == 0) {
+#pragma unroll
+            for (int sg = 0; sg < 2; ++sg) {
+                const uint64_t v = sg ? sum_neg : sum_pos;
+                if (v != 0) {
+                    const WidePieces q = wide_pieces(v, static_cast<int>(e0) - 1);
+                    atomicAdd(&limbs[sg][q.w], static_cast<unsigned long long>(q.p0));
+                    atomicAdd(&limbs[sg][q.w + 1], static_cast<unsigned long long>(q.p1));
+                    atomicAdd(&limbs[sg][q.w + 2], static_cast<unsigned long long>(q.p2));
+                }
             }
         }
     }
     if (my_flags) atomicOr(&flags, my_flags);
     __syncthreads();
-    // bins -> limb accumulators (each limb below 2^44 per workgroup)
-    __shared__ unsigned long long limbs[2][kLimbWords];
-    if (threadIdx.x < 2 * kLimbWords) (&limbs[0][0])[threadIdx.x] = 0;
-    __syncthreads();
+    // bins -> limb accumulators
     for (int i = threadIdx.x; i < 2 * 256; i += kBinThreads) {
         uint64_t sum = 0;
 #pragma unroll
@@ -95,33 +221,69 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
     if (threadIdx.x == 0) rec[2 * kLimbWords] = flags;
 }
 
-// One workgroup: word k of the records (a limb of one sign, or the flags)
-// is summed (ORed) over the records by kOffsetParts threads; thread 0 then
-// rounds the mean from the limbs.  Limb totals stay below 2^52.
-__global__ __launch_bounds__(kRecordWords * kOffsetParts) void nested_offset_kernel(
-    const uint64_t* __restrict__ ws, int groups, int64_t nb, float* __restrict__ offset) {
-    __shared__ unsigned long long total[kRecordWords];
-    if (threadIdx.x < kRecordWords) total[threadIdx.x] = 0;
-    __syncthreads();
-    const int k = threadIdx.x % kRecordWords, part = threadIdx.x / kRecordWords;
-    uint64_t acc = 0;
-    for (int g = part; g < groups; g += kOffsetParts) {
-        const uint64_t v = ws[static_cast<int64_t>(g) * kRecordWords + k];
-        acc = k == 2 * kLimbWords ? (acc | v) : acc + v;
+// The records of launch 1 for the mean: half wave h of the workgroup
+// (kOffsetParts = 32 lanes) takes record word h (a limb of one sign, or
+// the flags) of every record, eight per lane; halves past the last word
+// load nothing.
+__device__ __forceinline__ void load_records(const uint64_t* __restrict__ ws, int groups,
+                                             uint64_t (&v)[kOffsetLoads]) {
+    const int k = threadIdx.x / kOffsetParts, part = threadIdx.x % kOffsetParts;
+#pragma unroll
+    for (int j = 0; j < kOffsetLoads; ++j) {
+        const int g = part + j * kOffsetParts;
+        v[j] = (k < kRecordWords && g < groups) ? ws[g * kRecordWords + k] : 0;
     }
-    if (acc != 0) {
-        if (k == 2 * kLimbWords) atomicOr(&total[k], static_cast<unsigned long long>(acc));
-        else atomicAdd(&total[k], static_cast<unsigned long long>(acc));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_or_u64(uint64_t v) {
+    return v | dpp_u64<CTRL>(v);
+}
+
+// The mean offset from the loaded records: each half wave sums (ORs, for
+// the flags) its word; thread 0 rounds the mean from the limb totals (each
+// below 2^60).  Every thread gets the offset (through LDS).  All threads of
+// the workgroup call it.
+__device__ inline float mean_offset(const uint64_t (&v)[kOffsetLoads], int64_t nb) {
+    __shared__ unsigned long long total[kRecordWords];
+    __shared__ float off;
+    uint64_t sum = 0, any = 0;
+#pragma unroll
+    for (int j = 0; j < kOffsetLoads; ++j) {
+        sum += v[j];
+        any |= v[j];
+    }
+    sum += dpp_u64<kDppXor1>(sum);
+    sum += dpp_u64<kDppXor2>(sum);
+    sum += dpp_u64<kDppHalfMirror>(sum);
+    sum += dpp_u64<kDppMirror>(sum);
+    any = dpp_or_u64<kDppXor1>(any);
+    any = dpp_or_u64<kDppXor2>(any);
+    any = dpp_or_u64<kDppHalfMirror>(any);
+    any = dpp_or_u64<kDppMirror>(any);
+    const auto row = [](uint64_t x, int lane) {
+        return (static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(x >> 32), lane)) << 32) |
+               readlane_u32(static_cast<uint32_t>(x), lane);
+    };
+    // The read-outs stay in uniform control flow (a cross-lane read inside
+    // a lane-0 branch lets the compiler move the sums' last step into that
+    // branch, where the other lanes do not run it).
+    const int k0 = 2 * (threadIdx.x / kWave);  // word of the wave's first half; k0 + 1 is odd: never the flags
+    const uint64_t t0 = k0 == 2 * kLimbWords ? (row(any, 0) | row(any, 16)) : row(sum, 0) + row(sum, 16);
+    const uint64_t t1 = row(sum, 32) + row(sum, 48);
+    if (__lane_id() == 0) {
+        if (k0 < kRecordWords) total[k0] = t0;
+        if (k0 + 1 < kRecordWords) total[k0 + 1] = t1;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t flags = static_cast<uint32_t>(total[2 * kLimbWords]);
+        const uint32_t fl = static_cast<uint32_t>(total[2 * kLimbWords]);
         uint32_t bits;
-        if ((flags & kFlagNan) || ((flags & kFlagPosInf) && (flags & kFlagNegInf))) {
+        if ((fl & kFlagNan) || ((fl & kFlagPosInf) && (fl & kFlagNegInf))) {
             bits = 0x7FC00000u;
-        } else if (flags & kFlagPosInf) {
+        } else if (fl & kFlagPosInf) {
             bits = 0x7F800000u;
-        } else if (flags & kFlagNegInf) {
+        } else if (fl & kFlagNegInf) {
             bits = 0xFF800000u;
         } else {
             uint64_t pos[kLimbWords], neg[kLimbWords];
@@ -132,28 +294,60 @@ __global__ __launch_bounds__(kRecordWords * kOffsetParts) void nested_offset_ker
             }
             bits = mean_from_limbs(pos, neg, static_cast<uint64_t>(nb));
         }
-        *offset = __uint_as_float(bits);
+        off = __uint_as_float(bits);
     }
+    __syncthreads();
+    return off;
 }
 
-// Lowest index with the smallest |RN(v - c_i)|: binary search for the
-// number j of codes <= v in a non-decreasing map, then the two neighbours;
-// rounded distances only grow away from v on either side, so the winner is
-// the upper neighbour if it is strictly closer, else the lowest index left
-// of v with the lower neighbour's rounded distance.  NaN gives 0.
-__device__ __forceinline__ uint32_t nearest_sorted(const float* c, float v) {
-    int j = 0;
+// Lowest index with the smallest |RN(v - c_i)| for four values at once, in
+// a non-decreasing map c (LDS) whose entries 16t + 15 (t < 15) are also in
+// sep[t] (uniform registers).  The number j of entries <= v among the
+// first 255 (the binary search's result) is 16 times the count of
+// separators <= v plus a binary search inside that block of 16 (the four
+// values step together, so each step's LDS reads share one wait).  Then the
+// neighbours: rounded distances only grow away from v on either side, so
+// the winner is entry j if it is strictly closer than entry j - 1, else the
+// lowest index left of v with entry j - 1's rounded distance.  NaN gives 0.
+__device__ __forceinline__ void nearest_sorted4(const float* c, const float (&sep)[15], const float (&v)[4],
+                                                uint32_t (&q)[4]) {
+    int j[4];
 #pragma unroll
-    for (int step = 128; step >= 1; step >>= 1) {
-        if (c[j + step - 1] <= v) j += step;
+    for (int k = 0; k < 4; ++k) {
+        int t = 0;
+#pragma unroll
+        for (int u = 0; u < 15; ++u) t += sep[u] <= v[k] ? 1 : 0;
+        j[k] = 16 * t;
     }
-    if (j == 0) return 0;
-    int i = j - 1;
-    const float dlo = fabsf(v - c[i]);
-    if (j < 256 && fabsf(v - c[j]) < dlo) return static_cast<uint32_t>(j);
+#pragma unroll
+    for (int step = 8; step >= 1; step >>= 1) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (c[j[k] + step - 1] <= v[k]) j[k] += step;
+        }
+    }
+    float dlo[4], dup[4], dleft[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // one batch of reads: entries j - 2, j - 1, j (clamped)
+        const int i = j[k] > 0 ? j[k] - 1 : 0;
+        dlo[k] = fabsf(v[k] - c[i]);
+        dup[k] = fabsf(v[k] - c[j[k]]);  // j <= 255
+        dleft[k] = fabsf(v[k] - c[i > 0 ? i - 1 : 0]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        int i = j[k] - 1;
+        if (j[k] == 0) {
+            i = 0;
+        } else if (dup[k] < dlo[k]) {
+            i = j[k];
+        } else if (i > 0 && dleft[k] == dlo[k]) {  // equal rounded distances further left (rare)
+            --i;
 #pragma unroll 1
-    while (i > 0 && fabsf(v - c[i - 1]) == dlo) --i;
-    return static_cast<uint32_t>(i);
+            while (i > 0 && fabsf(v[k] - c[i - 1]) == dlo[k]) --i;
+        }
+        q[k] = static_cast<uint32_t>(i);
+    }
 }
 
 // The definition's scan (strict <, from index 0): any map.
@@ -171,55 +365,91 @@ __device__ __forceinline__ uint32_t nearest_scan256(const float* c, float v) {
     return best;
 }
 
-constexpr int kEncThreads = 256;
-constexpr int kEncWaves = kEncThreads / kWave;
+// Four blocks per lane of group g (zeros past nb).
+__device__ __forceinline__ void load_group(const float* __restrict__ a, int64_t nb, int64_t g, bool aligned16,
+                                           float (&x)[4]) {
+    const int64_t b0 = g * kGroup2 + __lane_id() * 4;
+    if (aligned16 && b0 + 3 < nb) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(a + b0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = __uint_as_float(u[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = b0 + k < nb ? a[b0 + k] : 0.0f;
+    }
+}
 
 __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float* __restrict__ a, int64_t nb,
                                                                     const float* __restrict__ qmap2,
-                                                                    const float* __restrict__ offset_p,
+                                                                    const uint64_t* __restrict__ ws, int groups,
+                                                                    float* __restrict__ offset_out,
                                                                     uint8_t* __restrict__ code,
                                                                     float* __restrict__ absmax2) {
     __shared__ float c[256];
     __shared__ int unsorted;
+    uint64_t rec[kOffsetLoads];
+    load_records(ws, groups, rec);  // first: the mean waits on these
     if (threadIdx.x == 0) unsorted = 0;
     __syncthreads();
-    c[threadIdx.x] = qmap2[threadIdx.x];
-    // non-decreasing and NaN-free, else the full scan
-    if (threadIdx.x > 0 && !(qmap2[threadIdx.x - 1] <= qmap2[threadIdx.x])) unsorted = 1;
-    if (threadIdx.x == 0 && qmap2[0] != qmap2[0]) unsorted = 1;
-    __syncthreads();
-    const bool sorted = unsorted == 0;
-    const float offset = *offset_p;
+    if (threadIdx.x < 256) {
+        c[threadIdx.x] = qmap2[threadIdx.x];
+        // non-decreasing and NaN-free, else the full scan
+        if (threadIdx.x > 0 && !(qmap2[threadIdx.x - 1] <= qmap2[threadIdx.x])) unsorted = 1;
+        if (threadIdx.x == 0 && qmap2[0] != qmap2[0]) unsorted = 1;
+    }
+    // One group per wave per pass, groups g, g + step, ...; the first
+    // group's values are loaded before the mean so that both loads overlap,
+    // and each pass loads the next group before working on this one.
     const int lane = __lane_id();
     const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
-    const int64_t g = static_cast<int64_t>(blockIdx.x) * kEncWaves + threadIdx.x / kWave;  // wave-uniform
-    if (g >= ngroups) return;
-    const int64_t b0 = g * kGroup2 + lane * 4;
-    float r[4];
-    float m = 0.0f;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * kEncWaves;
+    int64_t g = static_cast<int64_t>(blockIdx.x) * kEncWaves + threadIdx.x / kWave;  // wave-uniform
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(a) & 15u) == 0;
+    const bool code4 = (reinterpret_cast<uintptr_t>(code) & 3u) == 0;
+    float x[4];
+    load_group(a, nb, g, aligned16, x);
+    float sep[15];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        r[k] = b0 + k < nb ? a[b0 + k] - offset : 0.0f;
-        m = __builtin_elementwise_maximum(m, fabsf(r[k]));
-    }
-    // group max: the bits of non-negative floats (and NaN above them) order
-    // as their values
-    uint32_t mb = __float_as_uint(m);
-    mb = max(mb, dpp_u32<kDppXor1>(mb));
-    mb = max(mb, dpp_u32<kDppXor2>(mb));
-    mb = max(mb, dpp_u32<kDppHalfMirror>(mb));
-    mb = max(mb, dpp_u32<kDppMirror>(mb));
-    mb = max(mb, shfl_xor_u32(mb, 16));
-    mb = max(mb, shfl_xor_u32(mb, 32));
-    const float amax2 = __uint_as_float(mb);
-    if (lane == 0) absmax2[g] = amax2;
-    const float s = __builtin_elementwise_maximum(amax2, kEps2);
+    for (int t = 0; t < 15; ++t) sep[t] = qmap2[16 * t + 15];
+    const float offset = mean_offset(rec, nb);  // has barriers: c[] and unsorted are set
+    const bool sorted = unsorted == 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *offset_out = offset;
+    for (; g < ngroups; g += step) {
+        float y[4];
+        load_group(a, nb, g + step, aligned16, y);  // zeros past the end: no load
+        const int64_t b0 = g * kGroup2 + lane * 4;
+        float r[4];
+        float m = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        if (b0 + k < nb) {
-            const float v = r[k] / s;
-            code[b0 + k] = static_cast<uint8_t>(sorted ? nearest_sorted(c, v) : nearest_scan256(c, v));
+        for (int k = 0; k < 4; ++k) {
+            r[k] = x[k] - offset;
+            if (b0 + k < nb) m = __builtin_elementwise_maximum(m, fabsf(r[k]));
         }
+        // group max: the bits of non-negative floats (and NaN above them)
+        // order as their values
+        const float amax2 = __uint_as_float(wave_max_u32(__float_as_uint(m)));
+        if (lane == 0) absmax2[g] = amax2;
+        const float s = __builtin_elementwise_maximum(amax2, kEps2);
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = r[k] / s;
+        uint32_t q[4];
+        if (sorted) {
+            nearest_sorted4(c, sep, v, q);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) q[k] = nearest_scan256(c, v[k]);
+        }
+        if (code4 && b0 + 3 < nb) {
+            *reinterpret_cast<uint32_t*>(code + b0) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (b0 + k < nb) code[b0 + k] = static_cast<uint8_t>(q[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = y[k];
     }
 }
 
@@ -235,12 +465,11 @@ int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, ui
     const int groups = bin_groups(nb);
     uint64_t* ws = static_cast<uint64_t*>(workspace);
     hipLaunchKernelGGL(nested_bins_kernel, dim3(groups), dim3(kBinThreads), 0, st, absmax, nb, ws);
-    hipLaunchKernelGGL(nested_offset_kernel, dim3(1), dim3(kRecordWords * kOffsetParts), 0, st, ws, groups, nb,
-                       offset);
     const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
-    const int64_t grid = (ngroups + kEncWaves - 1) / kEncWaves;
+    const int64_t want = (ngroups + kEncWaves - 1) / kEncWaves;
+    const int64_t grid = want < kEncMaxGrid ? want : kEncMaxGrid;
     hipLaunchKernelGGL(nested_encode_kernel, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st, absmax, nb,
-                       qmap2, offset, code, absmax2);
+                       qmap2, ws, groups, offset, code, absmax2);
     return static_cast<int>(hipGetLastError());
 }
 

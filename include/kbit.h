@@ -254,8 +254,9 @@ int linear_4bit_nested_bf16(const uint16_t* X, int64_t M, int32_t K, const uint3
  * offset      : device, 1 float32 (output; not written when nb == 0).
  * workspace   : device, >= kbit_nested_workspace_bytes(nb) bytes, 8-byte
  *               aligned, owned by the caller; its contents are scratch (no
- *               initialisation needed, overwritten by every call).
- * nb <= 2^36.  Three kernels run in order on the stream.
+ *               initialisation needed, overwritten by every call).  Calls
+ *               that share a workspace must not overlap.
+ * nb <= 2^36.  Two kernels run in order on the stream.
  * --------------------------------------------------------------------- */
 int64_t kbit_nested_workspace_bytes(int64_t nb);  /* -1 for nb outside [0, 2^36] */
 int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2,

@@ -59,6 +59,20 @@ def test_special_values():
     check(np.float32([3.0, 3 * 2.0 ** -24, 3 * 2.0 ** -60]), q, "single rounding")
 
 
+def test_wide_exponent_spread():
+    # magnitudes from the subnormals up to 2^100 with mixed signs: every wave
+    # of the significand sums has values inside and far below its top 24
+    # binades, and the positive and negative totals nearly cancel
+    rng = np.random.default_rng(31)
+    nb = 70001
+    e = rng.integers(-149, 100, nb)
+    sign = np.where(rng.random(nb) < 0.5, -1.0, 1.0)
+    a = (sign * np.ldexp(1.0 + rng.random(nb), e)).astype(np.float32)
+    check(a, codebooks.dynamic_map8(), "wide spread")
+    a[np.argmax(np.abs(a))] = 0.0
+    check(a, codebooks.dynamic_map8(), "wide spread, top removed")
+
+
 def test_other_maps():
     a = np.abs(synth.normal(3000, seed=4, dtype="fp32", sigma=0.05)).astype(np.float32)
     q = codebooks.dynamic_map8()
