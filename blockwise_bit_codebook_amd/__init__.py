@@ -20,7 +20,8 @@ import numpy as np
 
 __all__ = [
     "KbitError", "lib", "codebook_nf", "codebook_fp4", "codebook_lloyd_max_normal",
-    "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax", "linear_4bit",
+    "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax",
+    "quantize_nested_absmax_noalloc", "linear_4bit",
     "quantize_act_fwht_k4_bf16", "quantize_act_rpbh_k4_bf16", "n_words", "n_blocks",
 ]
 
@@ -193,6 +194,17 @@ def quantize_nested_absmax(absmax, qmap2, absmax_code=None, absmax2=None, offset
     name = "quantize_nested_absmax"
     _check(name, lib().quantize_nested_absmax(_ptr(absmax), nb, _ptr(qmap2), _ptr(absmax_code), _ptr(absmax2),
                                               _ptr(offset), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return absmax_code, absmax2, offset
+
+
+def quantize_nested_absmax_noalloc(absmax, qmap2, absmax_code, absmax2, offset):
+    """quantize_nested_absmax into caller-given outputs, with the library's
+    static per-GPU workspace: no allocation.  Calls on one GPU must not
+    overlap."""
+    nb = absmax.numel()
+    name = "quantize_nested_absmax_noalloc"
+    _check(name, lib().quantize_nested_absmax_noalloc(_ptr(absmax), nb, _ptr(qmap2), _ptr(absmax_code),
+                                                      _ptr(absmax2), _ptr(offset), _stream(absmax.device)))
     return absmax_code, absmax2, offset
 
 

@@ -34,6 +34,8 @@ def _signatures():
         ("linear_kbit_bf16_k4", [_p, _i64, _i32, _p, _p, _p, _i32, _i32, _p, _p]),
         ("linear_4bit_nested_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p, _f32, _i32, _i32, _p, _p]),
         ("quantize_nested_absmax", [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]),
+        ("kbit_nested_noalloc_scratch_bytes", []),
+        ("quantize_nested_absmax_noalloc", [_p, _i64, _p, _p, _p, _p, _p]),
     ]
     for t in DTYPES:
         for k in KS:
@@ -57,7 +59,8 @@ def load(path=LIB_PATH):
     for name, args in SIGNATURES:
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = {"kbit_strerror": ct.c_char_p, "kbit_nested_workspace_bytes": ct.c_int64}.get(name, ct.c_int)
+        fn.restype = {"kbit_strerror": ct.c_char_p, "kbit_nested_workspace_bytes": ct.c_int64,
+                      "kbit_nested_noalloc_scratch_bytes": ct.c_int64}.get(name, ct.c_int)
     return lib
 
 

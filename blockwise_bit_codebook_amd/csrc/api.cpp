@@ -230,6 +230,24 @@ int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2, 
         kbit::launch_nested_encode(absmax, nb, qmap2, absmax_code, absmax2, offset, workspace, stream));
 }
 
+int64_t kbit_nested_noalloc_scratch_bytes(void) { return kbit::nested_scratch_bytes(); }
+
+int quantize_nested_absmax_noalloc(const float* absmax, int64_t nb, const float* qmap2, uint8_t* absmax_code,
+                                   float* absmax2, float* offset, void* stream) {
+    if (nb < 0 || nb > kbit::kMaxNestedBlocks) return KBIT_EINVAL;
+    if (nb == 0) return KBIT_OK;
+    if (!absmax || !qmap2 || !absmax_code || !absmax2 || !offset) return KBIT_EINVAL;
+    if (kbit::nested_workspace_bytes(nb) > kbit::nested_scratch_bytes()) return KBIT_EINVAL;
+    if (!kbit::aligned(absmax, 4) || !kbit::aligned(qmap2, 4) || !kbit::aligned(absmax2, 4) ||
+        !kbit::aligned(offset, 4))
+        return KBIT_EALIGN;
+    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
+    void* scratch = kbit::nested_scratch_ptr();  // looked up once per device
+    if (scratch == nullptr) return KBIT_ELAUNCH;
+    return kbit::map_launch(
+        kbit::launch_nested_encode(absmax, nb, qmap2, absmax_code, absmax2, offset, scratch, stream));
+}
+
 int linear_kbit_bf16_k4(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed, const float* codebook16,
                         const float* absmax, int32_t N, int32_t blocksize, uint16_t* out, void* stream) {
     int l2b = 0;

@@ -29,6 +29,11 @@ int64_t nested_workspace_bytes(int64_t nb);
 int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
                          float* offset, void* workspace, void* stream);
 
+// The encoder's static device workspace: its size, and its device address
+// on the current device (null if it cannot be looked up).
+int64_t nested_scratch_bytes();
+void* nested_scratch_ptr();
+
 int launch_linear4_plain(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* codebook16,
                          const float* absmax, int N, int log2B, uint16_t* out, void* stream);
 

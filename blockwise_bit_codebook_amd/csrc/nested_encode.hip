@@ -30,10 +30,14 @@
 //      entries held in registers, a binary search in LDS inside the block
 //      of 16 it picks, and a walk to the lowest index with the same rounded
 //      distance (a full scan if the map is not sorted).
-// The workspace holds only the records (scratch, no initialisation).
+// The workspace holds only the records (scratch, no initialisation).  A
+// variant keeps it in a static device array instead (one per GPU, for
+// callers that cannot allocate).
 #include "device.h"
 #include "exact_mean.h"
 #include "kbit_internal.h"
+
+#include <atomic>
 
 namespace kbit {
 namespace {
@@ -471,6 +475,34 @@ int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, ui
     hipLaunchKernelGGL(nested_encode_kernel, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st, absmax, nb,
                        qmap2, ws, groups, offset, code, absmax2);
     return static_cast<int>(hipGetLastError());
+}
+
+// The encoder's workspace in device memory of this library, for callers
+// that cannot allocate: one copy per GPU, kept until the process ends.  Its
+// contents are scratch, so nothing needs clearing between calls.  Host code
+// must not pass the array's name to a kernel (it is a host-side stand-in);
+// it uses the device address from hipGetSymbolAddress, looked up once per
+// device.
+constexpr int64_t kScratchBytes = static_cast<int64_t>(kMaxBinGroups) * kRecordWords * 8;
+static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+
+namespace {
+std::atomic<void*> g_scratch[kMaxDevices];
+}  // namespace
+
+int64_t nested_scratch_bytes() { return kScratchBytes; }
+
+void* nested_scratch_ptr() {
+    const int dev = current_device_index();
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+        g_scratch[dev].store(q, std::memory_order_release);
+        p = q;
+    }
+    return p;
 }
 
 }  // namespace kbit

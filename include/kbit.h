@@ -22,7 +22,8 @@
  *     Nothing aborts the process.
  *   - Device pointers are plain device addresses (e.g. torch data_ptr()).
  *     The caller owns and allocates every buffer with exact sizes; the
- *     library allocates, frees and keeps no device memory and never
+ *     library allocates and frees no device memory, keeps none except the
+ *     static workspace of quantize_nested_absmax_noalloc, and never
  *     synchronises.  Inputs are read-only and left unmodified.
  *   - stream: a hipStream_t cast to void*; NULL means the null stream.  Work
  *     is enqueued asynchronously on that stream.
@@ -45,7 +46,8 @@
  *     nearest even.  Every result is the one the definitions above fix,
  *     bit for bit (no tolerance).
  *   - Limits: n <= 2^40 elements (KBIT_EINVAL beyond).
- *   - Calls on different streams may run concurrently (no shared state).
+ *   - Calls on different streams may run concurrently (no shared state),
+ *     except calls of quantize_nested_absmax_noalloc on one GPU.
  */
 #ifndef KBIT_H
 #define KBIT_H
@@ -262,6 +264,23 @@ int64_t kbit_nested_workspace_bytes(int64_t nb);  /* -1 for nb outside [0, 2^36]
 int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2,
                            uint8_t* absmax_code, float* absmax2, float* offset,
                            void* workspace, int64_t workspace_bytes, void* stream);
+
+/* quantize_nested_absmax without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it).  The
+ * workspace is a static array in this library's device memory, one per
+ * GPU, of kbit_nested_noalloc_scratch_bytes() bytes (51,200), held until
+ * the process ends; its contents are scratch (nothing to clear between
+ * calls).  It covers every nb up to 2^36 (KBIT_EINVAL beyond).
+ * All calls on one GPU share that array: calls that overlap on one GPU
+ * (different streams or host threads at the same time) race and give
+ * wrong results; serialise them.  Results are identical to
+ * quantize_nested_absmax's.  Other arguments as quantize_nested_absmax.
+ * KBIT_ELAUNCH also when the array's device address cannot be looked up. */
+int64_t kbit_nested_noalloc_scratch_bytes(void);
+int quantize_nested_absmax_noalloc(const float* absmax, int64_t nb, const float* qmap2,
+                                   uint8_t* absmax_code, float* absmax2, float* offset,
+                                   void* stream);
 
 /* ------------------------------------------------------------------------
  * W4A4-style activation assignment ([ORBIT] README W4A4 fast path and

@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 2 + 2, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 2 + 2 + 2, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -124,6 +124,14 @@ def test_validation_codes_before_any_device_access():
     assert ne(_A16, 1000, _A16, _A16, _A16, _A16, ct.c_void_p(0x40004), wsb, None) == -3
     assert ne(_A16, 1000, _A16, None, _A16, _A16, _W8, wsb, None) == -1
     assert ne(_A16, 1000, ct.c_void_p(0x20002), _A16, _A16, _A16, _W8, wsb, None) == -3
+    na = lib.quantize_nested_absmax_noalloc
+    assert lib.kbit_nested_noalloc_scratch_bytes() >= lib.kbit_nested_workspace_bytes(1 << 36)
+    assert na(None, 0, None, None, None, None, None) == 0                           # empty: no-op
+    assert na(_A16, -1, _A16, _A16, _A16, _A16, None) == -1
+    assert na(_A16, (1 << 36) + 1, _A16, _A16, _A16, _A16, None) == -1               # beyond the static workspace
+    assert na(None, 1000, _A16, _A16, _A16, _A16, None) == -1
+    assert na(_A16, 1000, _A16, _A16, _A16, None, None) == -1                        # no offset output
+    assert na(_A16, 1000, ct.c_void_p(0x20002), _A16, _A16, _A16, None) == -3        # qmap2 misaligned
     li = lib.linear_kbit_bf16_k4
     assert li(_A16, 4, 48, _A16, _A16, _A16, 64, 64, _A16, None) == -1            # K not a multiple of 32
     assert li(_A16, 4, 64, _A16, _A16, _A16, 0, 64, _A16, None) == -1             # N = 0
