@@ -15,6 +15,7 @@ block (uint8 tensor).
 """
 
 import ctypes as ct
+import operator
 
 import numpy as np
 
@@ -106,6 +107,38 @@ def _ptr(t):
     return ct.c_void_p(t.data_ptr())
 
 
+def _buf(t, what, dtype, count):
+    """Checks a buffer before its address goes to the library, which cannot
+    check sizes or element types: the dtype, and at least ``count``
+    elements.  Placement and contiguity are checked by ``_ptr``."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: element type {t.dtype}, expected {dtype}")
+    if t.numel() < count:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {count} needed")
+    return t
+
+
+def _same_device(ref, **tensors):
+    for what, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{what} is on {t.device}, the input on {ref.device}")
+
+
+def _blocks(n, blocksize):
+    try:
+        n, b = operator.index(n), operator.index(blocksize)
+    except TypeError:
+        raise TypeError(f"n and blocksize must be integers, got {n!r}, {blocksize!r}") from None
+    if b <= 0:
+        raise ValueError(f"blocksize must be positive, got {b}")
+    if n < 0:
+        raise ValueError(f"n must be >= 0, got {n}")
+    return n_blocks(n, b)
+
+
 def _stream(device):
     torch = _torch()
     return ct.c_void_p(torch.cuda.current_stream(device).cuda_stream)
@@ -127,11 +160,18 @@ def quantize_kbit(A, codebook, k, blocksize, absmax=None, packed=None, absmax_fo
     t = _dtype_name(A.dtype)
     n = A.numel()
     infix = _scale_infix(absmax_format)
+    if k not in (2, 3, 4, 5):
+        raise ValueError(f"k must be 2..5, got {k!r}")
+    nb = _blocks(n, blocksize)
+    sdt = torch.uint8 if infix else torch.float32
     if absmax is None:
-        absmax = torch.empty(n_blocks(n, blocksize), dtype=torch.uint8 if infix else torch.float32,
-                             device=A.device)
+        absmax = torch.empty(nb, dtype=sdt, device=A.device)
     if packed is None:
         packed = torch.empty(n_words(n, k), dtype=torch.int32, device=A.device)
+    _buf(codebook, "codebook", torch.float32, 1 << k)
+    _buf(absmax, "absmax (E4M4 bytes)" if infix else "absmax", sdt, nb)
+    _buf(packed, "packed", torch.int32, n_words(n, k))
+    _same_device(A, codebook=codebook, absmax=absmax, packed=packed)
     name = f"quantize_kbit_{infix}{t}_k{k}"
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(codebook), _ptr(A), _ptr(absmax), _ptr(packed), n, blocksize, _stream(A.device)))
@@ -144,18 +184,37 @@ def dequantize_kbit(packed, codebook, absmax, k, n, dtype, blocksize, out=None):
     absmax: fp32 scales, or uint8 E4M4 codes (selects the E4M4 entry point)."""
     torch = _torch()
     t = _dtype_name(dtype)
+    if k not in (2, 3, 4, 5):
+        raise ValueError(f"k must be 2..5, got {k!r}")
+    nb = _blocks(n, blocksize)
     if absmax.dtype == torch.uint8:
         infix = "e4m4_"
     elif absmax.dtype == torch.float32:
         infix = ""
     else:
-        raise TypeError(f"absmax must be float32 or uint8 (E4M4), got {absmax.dtype}")
+        raise TypeError(f"dequantize_kbit: the block scales are a float32 tensor, or a uint8 tensor of "
+                        f"E4M4 bytes; this one holds {absmax.dtype}")
     if out is None:
         out = torch.empty(n, dtype=dtype, device=packed.device)
+    _buf(packed, "packed", torch.int32, n_words(n, k))
+    _buf(codebook, "codebook", torch.float32, 1 << k)
+    _buf(absmax, "absmax", absmax.dtype, nb)
+    _buf(out, "out", dtype, n)
+    _same_device(packed, codebook=codebook, absmax=absmax, out=out)
     name = f"dequantize_kbit_{infix}{t}_k{k}"
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(packed), _ptr(codebook), _ptr(absmax), _ptr(out), n, blocksize, _stream(packed.device)))
     return out
+
+
+def _nested_state(packed, codebook16, absmax_code, qmap2, absmax2, n, nb):
+    torch = _torch()
+    _buf(packed, "packed", torch.int32, n_words(n, 4))
+    _buf(codebook16, "codebook16", torch.float32, 16)
+    _buf(absmax_code, "absmax_code", torch.uint8, nb)
+    _buf(qmap2, "qmap2", torch.float32, 256)
+    _buf(absmax2, "absmax2", torch.float32, -(-nb // 256))
+    _same_device(packed, codebook16=codebook16, absmax_code=absmax_code, qmap2=qmap2, absmax2=absmax2)
 
 
 def dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offset, n, dtype, blocksize,
@@ -163,13 +222,28 @@ def dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offs
     """Nested 4-bit dequantize with the scale rebuild fused into the decode."""
     torch = _torch()
     t = _dtype_name(dtype)
+    nb = _blocks(n, blocksize)
     if out is None:
         out = torch.empty(n, dtype=dtype, device=packed.device)
+    _nested_state(packed, codebook16, absmax_code, qmap2, absmax2, n, nb)
+    _buf(out, "out", dtype, n)
+    _same_device(packed, out=out)
     name = f"dequantize_4bit_nested_{t}"
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(packed), _ptr(codebook16), _ptr(absmax_code), _ptr(qmap2), _ptr(absmax2),
                     ct.c_float(float(offset)), _ptr(out), n, blocksize, _stream(packed.device)))
     return out
+
+
+def _encode_args(absmax, qmap2, absmax_code, absmax2, offset):
+    torch = _torch()
+    nb = absmax.numel()
+    _buf(absmax, "absmax", torch.float32, 0)
+    _buf(qmap2, "qmap2", torch.float32, 256)
+    _buf(absmax_code, "absmax_code", torch.uint8, nb)
+    _buf(absmax2, "absmax2", torch.float32, -(-nb // 256))
+    _buf(offset, "offset", torch.float32, 1)
+    _same_device(absmax, qmap2=qmap2, absmax_code=absmax_code, absmax2=absmax2, offset=offset)
 
 
 def quantize_nested_absmax(absmax, qmap2, absmax_code=None, absmax2=None, offset=None, workspace=None):
@@ -191,6 +265,9 @@ def quantize_nested_absmax(absmax, qmap2, absmax_code=None, absmax2=None, offset
         raise KbitError("kbit_nested_workspace_bytes", -1, "nb out of range")
     if workspace is None:
         workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    _encode_args(absmax, qmap2, absmax_code, absmax2, offset)
+    _buf(workspace, "workspace", torch.uint8, need)
+    _same_device(absmax, workspace=workspace)
     name = "quantize_nested_absmax"
     _check(name, lib().quantize_nested_absmax(_ptr(absmax), nb, _ptr(qmap2), _ptr(absmax_code), _ptr(absmax2),
                                               _ptr(offset), _ptr(workspace), workspace.numel(), _stream(dev)))
@@ -202,6 +279,7 @@ def quantize_nested_absmax_noalloc(absmax, qmap2, absmax_code, absmax2, offset):
     static per-GPU workspace: no allocation.  Calls on one GPU must not
     overlap."""
     nb = absmax.numel()
+    _encode_args(absmax, qmap2, absmax_code, absmax2, offset)
     name = "quantize_nested_absmax_noalloc"
     _check(name, lib().quantize_nested_absmax_noalloc(_ptr(absmax), nb, _ptr(qmap2), _ptr(absmax_code),
                                                       _ptr(absmax2), _ptr(offset), _stream(absmax.device)))
@@ -217,8 +295,19 @@ def linear_4bit(X, packed, codebook16, N, blocksize, absmax=None, absmax_code=No
     if X.dtype != torch.bfloat16 or X.dim() != 2:
         raise TypeError("X must be a 2-D bfloat16 tensor")
     M, K = X.shape
+    nb = _blocks(N * K, blocksize)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _buf(out, "out", torch.bfloat16, M * N)
+    _same_device(X, out=out)
+    if absmax_code is not None:
+        _nested_state(packed, codebook16, absmax_code, qmap2, absmax2, N * K, nb)
+        _same_device(X, packed=packed)
+    else:
+        _buf(packed, "packed", torch.int32, n_words(N * K, 4))
+        _buf(codebook16, "codebook16", torch.float32, 16)
+        _buf(absmax, "absmax", torch.float32, nb)
+        _same_device(X, packed=packed, codebook16=codebook16, absmax=absmax)
     if absmax_code is not None:
         name = "linear_4bit_nested_bf16"
         status = lib().linear_4bit_nested_bf16(_ptr(X), M, K, _ptr(packed), _ptr(codebook16), _ptr(absmax_code),
@@ -244,6 +333,12 @@ def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=No
         row_norm = torch.empty(rows, dtype=torch.float32, device=X.device)
     if packed is None:
         packed = torch.empty(n_words(rows * d, 4), dtype=torch.int32, device=X.device)
+    _buf(sign_bits, "sign_bits", sign_bits.dtype if sign_bits.dtype in (torch.int32, torch.uint32) else torch.int32,
+         -(-d // 32))
+    _buf(codebook16, "codebook16", torch.float32, 16)
+    _buf(row_norm, "row_norm", torch.float32, rows)
+    _buf(packed, "packed", torch.int32, n_words(rows * d, 4))
+    _same_device(X, sign_bits=sign_bits, codebook16=codebook16, row_norm=row_norm, packed=packed, perm=perm)
     if perm is None:
         name = "quantize_act_fwht_k4_bf16"
         status = lib().quantize_act_fwht_k4_bf16(_ptr(X), rows, d, _ptr(sign_bits), _ptr(codebook16),
