@@ -137,7 +137,7 @@ def test_dequantize_block_sizes(dtype, B):
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_round_trip_weight_matrix(dtype):
     # 8192 x 8192 weight-like tensor, B = 64: quantize with E4M4 scales,
-    # dequantize its own output; codes and words in full, outputs sampled
+    # dequantize its own output; codes, words and outputs in full
     import torch
     rows = cols = 8192
     B, K = 64, 4
@@ -148,15 +148,10 @@ def test_round_trip_weight_matrix(dtype):
     out = kb.dequantize_kbit(packed, to_dev(cb), code, K, x.size, _tdt(dtype), B)
     torch.cuda.synchronize()
     n = x.size
-    rng = np.random.default_rng(9)
-    sample_rows = np.concatenate([[0, rows - 1], rng.integers(0, rows, 30)])
     got_code, got_words, got_out = bits(code), bits(packed), bits(out)
-    for r in sample_rows:
-        lo, hi = int(r) * cols, (int(r) + 1) * cols
-        xr = numerics.widen(x[lo:hi], dtype)
-        w, c = e4m4.quantize_packed(xr, cb, K, B)
-        assert_bits_equal(got_code[lo // B:hi // B], c, f"codes row {r}")
-        assert_bits_equal(got_words[lo // 32 * K:hi // 32 * K], w, f"words row {r}")
-        want = e4m4.dequantize(kbit.unpack(w, K, cols), c, cb, B, dtype)
-        assert_bits_equal(got_out[lo:hi], np_bits(want), f"out row {r}")
+    w, c = e4m4.quantize_packed(numerics.widen(x, dtype), cb, K, B)
+    assert_bits_equal(got_code, c, "codes")
+    assert_bits_equal(got_words, w, "words")
+    want = e4m4.dequantize(kbit.unpack(w, K, n), c, cb, B, dtype)
+    assert_bits_equal(got_out, np_bits(want), "out")
     assert got_code.size == kb.n_blocks(n, B) and got_words.size == kb.n_words(n, K)

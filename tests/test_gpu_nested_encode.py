@@ -83,34 +83,30 @@ def test_other_maps():
     check(a, np.linspace(-1, 1, 256).astype(np.float32), "linear map")
 
 
-def test_chain_quantize_encode_nested_dequantize():
-    # 8192 x 8192 bf16 weight, B = 64: quantize, encode the absmax on the GPU,
-    # nested-dequantize; state in full, outputs sampled
+@pytest.mark.parametrize("shape", ["wide11008", "tall11008", "square8192"])
+def test_chain_quantize_encode_nested_dequantize(shape):
+    # bf16 weight of each shape plus a 192-element tail, B = 64: quantize,
+    # encode the absmax and nested-dequantize on the GPU; the oracle runs the
+    # same chain from the input alone, and every stage is compared in full
     import torch
-    rows = cols = 8192
+    rows, cols = synth.WEIGHT_SHAPES[shape]
     B = 64
-    x = synth.weight(rows, cols, "bf16", seed=synth.SEED_WEIGHT_SHAPES)
+    x = synth.weight(rows, cols, "bf16", seed=synth.SEED_WEIGHT_SHAPES, extra=synth.TAIL_EXTRA)
+    n = x.size
     cb = codebooks.nf(4)
     q = codebooks.dynamic_map8()
-    case("nested chain 8192x8192 bf16")
-    A = to_dev(x, "bf16")
-    packed, absmax = kb.quantize_kbit(A, to_dev(cb), 4, B)
+    case(f"nested chain {shape}+{synth.TAIL_EXTRA} bf16")
+    packed, absmax = kb.quantize_kbit(to_dev(x, "bf16"), to_dev(cb), 4, B)
     code, a2, off = kb.quantize_nested_absmax(absmax, to_dev(q))
+    out = kb.dequantize_4bit_nested(packed, to_dev(cb), code, to_dev(q), a2, float(off.item()), n,
+                                    torch.bfloat16, B)
     torch.cuda.synchronize()
-    wc, wa2, woff = nested.encode(bits(absmax).view(np.float32), q)
+    ww, wa = kbit.quantize_packed(numerics.widen(x, "bf16"), cb, 4, B)
+    assert_bits_equal(bits(absmax), np_bits(wa), "absmax")
+    assert_bits_equal(bits(packed), ww, "words")
+    wc, wa2, woff = nested.encode(wa, q)
     assert bits(off)[0] == np.float32(woff).view(np.uint32)
     assert_bits_equal(bits(a2), np_bits(wa2), "absmax2")
     assert_bits_equal(bits(code), wc, "codes")
-    out = kb.dequantize_4bit_nested(packed, to_dev(cb), code, to_dev(q), a2, float(off.item()), x.size,
-                                    torch.bfloat16, B)
-    torch.cuda.synchronize()
-    got = bits(out)
-    words = bits(packed)
-    rng = np.random.default_rng(1)
-    for r in np.concatenate([[0, rows - 1], rng.integers(0, rows, 20)]):
-        lo, hi = int(r) * cols, (int(r) + 1) * cols
-        blo, bhi = lo // B, hi // B
-        idx = kbit.unpack(words[lo // 32 * 4:hi // 32 * 4], 4, cols)
-        s = nested.scales(wc, wa2, woff, q)[blo:bhi]
-        want = numerics.narrow(kbit.dequantize_values(idx, s, cb, B), "bf16")
-        assert_bits_equal(got[lo:hi], want, f"out row {r}")
+    want = nested.dequantize_packed(ww, wc, wa2, woff, q, cb, n, B, "bf16")
+    assert_bits_equal(bits(out), np_bits(want), "out")

@@ -228,21 +228,18 @@ def test_determinism_and_input_immutability():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
-def test_full_size_8192_square_sampled(dtype):
+def test_full_size_8192_square(dtype):
     # the measured workload: 8192 x 8192, N(0, 0.02), blocksize 64, NF4;
-    # sampled blocks are recomputed by the oracle one by one
-    import torch
-    n, B, K = 8192 * 8192, 64, 4
+    # every word and every absmax compared with the oracle
     x = synth.weight(8192, 8192, dtype, seed=synth.SEED_WEIGHT_SHAPES)
-    cb = codebooks.nf(K)
-    case(f"quantize full 8192^2 {dtype}")
-    words, absmax = run_quantize(x, dtype, cb, K, B)
-    rng = np.random.default_rng(0)
-    blocks = np.unique(np.concatenate([rng.integers(0, n // B, 3000), [0, n // B - 1]]))
-    x32 = numerics.widen(x, dtype)
-    for b in blocks:
-        seg = x32[b * B:(b + 1) * B]
-        wi, wa = kbit.quantize_packed(seg, cb, K, B)
-        assert np_bits(wa)[0] == absmax[b], b
-        g0 = b * B // 32
-        assert np.array_equal(words[g0 * K:(g0 + B // 32) * K], wi), b
+    check_quantize(x, dtype, codebooks.nf(4), 4, 64, "8192^2")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("shape", ["wide11008", "tall11008", "square8192"])
+def test_weight_shapes_with_tail(shape, dtype):
+    # 11008 x 4096, 4096 x 11008 and 8192 x 8192 weights plus a 192-element
+    # tail (three more blocks of 64), NF4, blocksize 64; in full
+    rows, cols = synth.WEIGHT_SHAPES[shape]
+    x = synth.weight(rows, cols, dtype, seed=synth.SEED_WEIGHT_SHAPES, extra=synth.TAIL_EXTRA)
+    check_quantize(x, dtype, codebooks.nf(4), 4, 64, f"{shape}+{synth.TAIL_EXTRA}")
