@@ -1,8 +1,9 @@
 """GPU parity: linear layer over 4-bit weights, decode fused into the MFMA
 product, against the float64 reference on the oracle's decoded weights.
 
-Bar: within the fp32-accumulation bound of ``oracle.linear.tolerance`` plus
-half a bf16 ulp; bit-exact where every partial sum is exact.  Weight states
+Bar: within the fp32-accumulation bound of ``oracle.linear.tolerance`` (the
+classic summation bound with one fp32 ulp per addition) plus the bf16
+output rounding; bit-exact where every partial sum is exact.  Weight states
 are seeded host-side (oracle quantize for small shapes, random bit planes and
 scales for the large ones).
 """
@@ -94,6 +95,35 @@ def test_exact_sums_bit_exact():
     wb = linear.weights_bf16(words, cb, N, K, B, absmax=absmax)
     ref, _ = linear.reference(xb, wb)
     assert_bits_equal(got.ravel(), numerics.to_bf16_bits(ref.astype(np.float32)).ravel(), "exact sums")
+
+
+def test_adversarial_partial_sums():
+    # every weight is 1 (NF4's top entry, unit scales), so each output is the
+    # fp32 sum of an X row, and the rows are built so that partial sums
+    # round: huge values that cancel around many small ones, magnitudes
+    # walking over 2^-20 .. 2^20 with alternating signs, and runs of equal
+    # values below a large one.  The outputs must stay inside the bound,
+    # which assumes only a faithful rounding of each addition in the matrix
+    # cores.
+    M, N, K, B = 4, 32, 4096, 64
+    rng = np.random.default_rng(12)
+    cb = codebooks.nf(4)
+    assert cb[15] == 1.0
+    words = kbit.pack(np.full(N * K, 15, np.uint8), 4)
+    absmax = np.ones(N * K // B, np.float32)
+    x = np.ones((M, K), np.float32)
+    x[0, 0], x[0, -1] = 2.0 ** 24, -(2.0 ** 24)
+    x[1, 1::2] *= -1
+    x[1] *= np.exp2(np.cumsum(rng.choice([-1, 1], K)).clip(-20, 20))
+    x[2] = 1.0 + 2.0 ** -7
+    x[2, ::512] = 2.0 ** 23
+    x[3] = rng.choice([-1.0, 1.0], K) * np.exp2(rng.integers(-20, 21, K))
+    xb = numerics.to_bf16_bits(x)
+    case("linear adversarial partial sums")
+    got = run_plain(xb, words, cb, absmax, N, K, B)
+    wb = linear.weights_bf16(words, cb, N, K, B, absmax=absmax)
+    ref, absum = linear.reference(xb, wb)
+    _check(got, ref, absum, K, "adversarial")
 
 
 def test_matches_dequantize_then_matmul():

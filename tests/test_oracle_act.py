@@ -51,6 +51,30 @@ def test_tree_sum_pairs_contiguous_halves():
     assert float(act.tree_sum_rows(q2)[0]) == 2.0 ** 24 + 2.0
 
 
+@pytest.mark.parametrize("h", [4, 256])
+def test_fwht_stage_order_ascending(h):
+    # Stages run s = 1, 2, 4, ... (pairs at distance 1 first).  With
+    # u = [2^24, 1, 0, 1] (zeros after, which later stages only copy), by
+    # hand in fp32 with ties to even:
+    #   s = 1: [RN(2^24 + 1), 2^24 - 1, 1, -1] = [2^24, 2^24 - 1, 1, -1]
+    #   s = 2: [RN(2^24 + 1), 2^24 - 2, 2^24 - 1, 2^24] = [2^24, 2^24 - 2, 2^24 - 1, 2^24]
+    # The descending order (s = 2 first) gives [2^24 + 2, 2^24 - 2, 2^24, 2^24]
+    # instead (its first stage loses nothing here).  Every later stage pairs
+    # the block with zeros, so the four values repeat along the row.
+    u = np.zeros((1, h), np.float32)
+    u[0, :4] = [2.0 ** 24, 1.0, 0.0, 1.0]
+    got = act.fwht_rows(u, h)[0]
+    want = np.tile(np.array([2.0 ** 24, 2.0 ** 24 - 2, 2.0 ** 24 - 1, 2.0 ** 24], np.float32), h // 4)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # the case tells the orders apart: the descending stages, run here on
+    # the first four values, give the other vector
+    v = u[0, :4].copy()
+    b = np.float32([v[0] + v[2], v[1] + v[3], v[0] - v[2], v[1] - v[3]])
+    desc = np.float32([b[0] + b[1], b[0] - b[1], b[2] + b[3], b[2] - b[3]])
+    assert np.array_equal(desc, np.float32([2.0 ** 24 + 2, 2.0 ** 24 - 2, 2.0 ** 24, 2.0 ** 24]))
+    assert not np.array_equal(desc, want[:4])
+
+
 def test_assign_small_brute_force():
     rows, d = 3, 64
     x, signs = synth.activations_bf16(tokens=rows, d=d, seed=11)

@@ -47,6 +47,27 @@ def test_bound_holds_for_worst_order_fp32_sums():
     assert abs(float(Fraction(float(s)) - exact_sum)) <= bound
 
 
+def test_bound_holds_for_truncating_sums():
+    # the bound's unit is one fp32 ulp per addition: sums that truncate
+    # (round toward zero) at every step, the worst faithful rounding, of
+    # same-sign terms (whose errors all add up) stay inside it in three
+    # orders
+    rng = np.random.default_rng(8)
+    K = 4096
+    p = np.abs(rng.normal(1, 0.01, K)).astype(np.float32)   # same-sign terms: errors add up
+    exact_sum = sum(exact.frac(v) for v in p)
+    bound = linear.tolerance(float(np.sum(p.astype(np.float64))), K)
+    for order in (np.argsort(p), np.argsort(-p), np.arange(K)):
+        s = Fraction(0)
+        for v in p[order]:
+            t = s + exact.frac(v)
+            r = Fraction(float(np.float32(float(t))))
+            if r > t:                       # step down to the fp32 value below
+                r = Fraction(float(np.nextafter(np.float32(float(r)), np.float32(0))))
+            s = r
+        assert 0 < float(exact_sum - s) <= bound
+
+
 def test_weights_are_the_dequantized_state():
     N, K, B = 8, 128, 64
     w = synth.weight(N, K, "fp32", seed=2)
