@@ -126,6 +126,14 @@ __host__ __device__ __forceinline__ int pair_index(int b, int s0) {
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// A raw buffer resource over `bytes` bytes at p.  Loads through it beyond
+// `bytes` return 0 and stores beyond it are dropped, so a lane with nothing
+// to do can issue the same instruction with an offset past the end instead
+// of branching around it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+
 // 16-byte global load, optionally marked non-temporal (streamed once).
 template <bool NT>
 __device__ __forceinline__ u32x4 load16(const void* p) {

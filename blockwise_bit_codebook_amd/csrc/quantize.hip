@@ -12,53 +12,60 @@
 // How (this kernel's own design, not the pages' warp-per-32 layout):
 //   * Each lane owns 8 consecutive elements (one 16-byte load for 16-bit
 //     types; for fp32 two 16-byte loads, each covering 1 KiB of the wave
-//     row, put in place with v_permlane32_swap), so a wave covers 512
+//     row, put in place with v_permlane32_swap), so a wave row is 512
 //     elements = 16 groups of 32 and a lane produces one byte of each plane
-//     word of its group.  The four lanes of
-//     a quad exchange bytes (DPP + v_perm) and store their group's K words
-//     as consecutive dwords: one coalesced store per wave.
-//   * Block absmax as an integer max of the magnitude bits (16-bit types two
-//     at a time with v_pk_max_u16), then a DPP max over the block's B/8
-//     lanes.  Blocks of 1024..4096 span 2..8 wave tiles: the wave reduces
-//     over them first and re-reads them (from L2) to classify.
+//     word of its group.  The four lanes of a quad exchange bytes (DPP +
+//     v_perm) and store their group's K words as consecutive dwords: one
+//     coalesced store per wave row.
+//   * Block absmax: v_maximum3_f32 over the lane's 8 magnitudes (IEEE
+//     maximum, so NaN propagates), then an integer max of the float bits
+//     over the block's B/8 lanes (DPP; the bits of non-negative floats order
+//     as their values).  Blocks of 1024..4096 span 2..8 wave rows: the wave
+//     reduces over them first and re-reads them (from L2) to classify.
 //   * Nearest code without a division per element.  For a sorted codebook
 //     whose distinct neighbours are at least 2^-16 apart, the first-index
 //     argmin rule picks, between two neighbouring codes c_lo < c_hi, the
 //     upper one exactly when x_n >= u for one fp32 value u (the rule is
-//     monotone in x_n).  The prologue finds each u by bisecting the fp32
-//     values between the two codes with the rule itself, and turns it
-//     into a test on x and s: RN(x/s) >= u  <=>  x - M*s > 0, with M the
-//     midpoint of u and its fp32 predecessor, nudged by a few fp64 ulps to
-//     encode the round-to-even direction of an exact tie.  M*s has at most
-//     49 significant bits, so one fp64 fma gives the sign of x - M*s
-//     exactly, and the nudge is far below the smallest nonzero |x - M*s|.
-//     For 16-bit inputs (values and block maxima of at most 11 significant
-//     bits) M is held as an fp32 pair and two fp32 fmas give that sign
-//     (threshold.h, pair_bits).
+//     monotone in x_n).  The prologue finds each u by searching the fp32
+//     values between the two codes with the rule itself, and turns it into
+//     a sign test on x and s in the cheapest exact form for the input type
+//     (threshold.h): fp32 inputs test x - M*s with M the fp64 midpoint of u
+//     and its predecessor (one fp64 fma); fp16 inputs hold M as an fp32 pair
+//     (two fp32 fmas); bf16 inputs, whose values and block maxima have 8
+//     significant bits, need one fp32 fma against a single T in {p, u}
+//     chosen so that every achievable quotient falls on the right side.
 //     To know which threshold to test, each element computes
 //     q = fma(x, 0.99*rcp(s), 2.99 + 2^-10), an approximation of an affine
 //     image of x_n inside (2, 4); bits 16..22 of q pick one of 128 buckets.
-//     A bucket's entry holds the M of the one threshold whose window
+//     A bucket's entry holds the one threshold whose window
 //     [t - 2^-18, t + 2^-18] (in q) meets the bucket (q's error is below
 //     2^-21) and the plane bytes of the indices on either side (K = 5:
 //     plane 4 in bit 1 of byte 0, gathered by two accumulation chains of
-//     even and odd elements).  Codebooks
-//     that are unsorted, leave [-1, 1], have close distinct neighbours, or
-//     put two windows into one bucket, and blocks whose scale is not finite
-//     or above 2^125, take the exact path: IEEE division and the full
-//     first-index scan.
+//     even and odd elements); the sign bit of the test selects between them.
+//     Codebooks that are unsorted, leave [-1, 1], have close distinct
+//     neighbours, or put two windows into one bucket, and blocks whose scale
+//     is not finite or above 2^125, take the exact path: IEEE division and
+//     the full first-index scan.
 //   * The table sits in LDS with each bucket row replicated 16 times (16
 //     bytes per copy), and lane l reads copy l mod 16: the 16 lanes served
 //     in one LDS cycle hit 16 different 16-byte bank groups whatever their
 //     buckets, so a ds_read_b128 per element runs without bank conflicts.
-//     One v_perm_b32 forms the address (bucket byte of q, lane byte).
+//     One v_perm_b32 forms the address (bucket byte of q, lane byte).  All
+//     threads of the workgroup build it: the searches one wave (or half
+//     wave) per threshold, then 4..8 threads per bucket.
 //   * The block scale is stored as the fp32 absmax or, for the E4M4
 //     entry points ([QLORA-2] PATCH 005), as its one-byte E4M4 code; the
 //     indices come from the fp32 absmax either way.
 //   * Persistent grid of 1024-thread workgroups (16 waves, at most 64 VGPRs
-//     so two groups share a CU; 512 threads for K = 5); each wave walks its
-//     steps (two wave rows for 16-bit inputs, one for fp32) with the next
-//     step's loads in flight while the current one is classified.
+//     so two groups share a CU; 512 threads for K = 5).  Wave v takes wave
+//     rows v, v + nwaves, ..., so the grid streams through one narrow
+//     window of memory, and keeps a ring of 4 rows (16-bit types) or 2
+//     (fp32) in flight: 4 KB of input per wave, which with 32 waves per CU
+//     is one XCD's L2.  Loads (non-temporal) and stores go through buffer
+//     resources over the row, of 0 bytes for rows past the end, so every
+//     pass of the ring is the same straight-line code and the compiler
+//     waits for each row's own loads only.  The first ring loads go out
+//     before the table build.
 #include "device.h"
 #include "e4m4.h"
 #include "kbit_internal.h"
@@ -304,12 +311,6 @@ struct E4m4Scale {
     static constexpr bool kEncoded = true;
     __device__ static uint8_t encode(float m) { return static_cast<uint8_t>(e4m4_encode(m)); }
 };
-
-// Raw buffer resource over `bytes` bytes at p: loads past it read 0 and
-// stores past it are dropped, without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
-}
 
 // Wave rows kept in flight per wave: 4 KB of input per wave, i.e. 4 rows of
 // 16-bit values or 2 rows of fp32.  With 32 waves per CU and 32 CUs per XCD

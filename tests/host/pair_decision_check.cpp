@@ -1,11 +1,20 @@
-// Exhaustive host check of the quantize kernel's fp32 threshold decision
-// for 16-bit inputs (threshold.h, pair_bits / decide32): with u the
-// switching point between two neighbouring codes and p its fp32 predecessor,
-// Mh = p, Ml = (u - p) / 2 and Ml' = Ml nudged by one ulp, the sign of
-// fma(-Ml', s, fma(-Mh, s, x)) must equal [RN(x / s) >= u] for every bf16
-// (fp16) x in [-s, s] and every bf16 (fp16) significand of s.  Scaling x and
-// s by a power of two changes nothing, so s runs over [1, 2) plus a few
-// binades near the ends of the range.  Exit status 0 when no case differs.
+// Exhaustive host check of the quantize kernel's fp32 threshold decisions
+// for 16-bit inputs (threshold.h).  With u the switching point between two
+// neighbouring codes, p its fp32 predecessor and M = (u + p) / 2:
+//   * pair form (fp16 inputs): Mh = p, Ml = (u - p) / 2, Ml' = Ml nudged by
+//     one ulp; the sign of fma(-Ml', s, fma(-Mh, s, x)) must equal
+//     [RN(x / s) >= u] for every fp16 (and bf16) x in [-s, s] and every
+//     fp16 (bf16) significand of s;
+//   * T form (bf16 inputs): one value T in {p, u}, "upper" when
+//     fma(-T, s, x) is not negative.  Here T is derived by brute force: the
+//     quotients of two 8-bit significands times a power of two that fall in
+//     [p, u] (at most one value) are found exactly, and T = p when that
+//     value lies above M, or on M with the tie rounding to u; T = u
+//     otherwise.  Every bf16 x in [-s, s] against every bf16 significand of
+//     s must then decide as [RN(x / s) >= u].
+// Scaling x and s by a power of two changes nothing, so s runs over [1, 2)
+// plus a few binades near the ends of the range.  Exit status 0 when no case
+// differs.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -42,6 +51,56 @@ static Thr make_thr(float lo, float hi) {
     const uint32_t b = fb(Ml);
     t.Ml2 = bf(tie_up ? b - 1 : b + 1);  // M nudged down (ties up) or up (ties down)
     return t;
+}
+// T of the T form for bf16 inputs (see the header), or NAN if two distinct
+// quotients fell into [p, u] (the form would not apply).
+static float make_T(float u, float p) {
+    const double M = ((double)u + (double)p) * 0.5;
+    const bool tie_up = (float)M == u;
+    const double ref = std::fabs(p) > 0.0 ? std::fabs((double)p) : std::fabs((double)u);
+    bool found = false, above = false, conflict = false;
+    double n_seen = 0.0;
+    int ms_seen = 1;
+    for (int sign = -1; sign <= 1; sign += 2) {
+        for (int ms = 128; ms <= 255; ++ms) {
+            for (int mx = 1; mx <= 255; ++mx) {
+                int e;
+                std::frexp(ref * (double)ms / (double)mx, &e);  // (mx / ms) 2^e lands next to |p|
+                for (int de = -2; de <= 2; ++de) {
+                    const double num = sign * std::ldexp((double)mx, e + de);  // exact
+                    // q = num / ms in [p, u]  <=>  p * ms <= num <= u * ms (exact products)
+                    if (!((double)p * ms <= num && num <= (double)u * ms)) continue;
+                    if (found && num * ms_seen != n_seen * ms) conflict = true;  // a second value
+                    found = true;
+                    n_seen = num;
+                    ms_seen = ms;
+                    const double mms = M * ms;  // exact: M has 25 significant bits, ms 8
+                    above = num > mms || (num == mms && tie_up);
+                }
+            }
+        }
+    }
+    if (conflict) return NAN;
+#ifdef PLANT_T_FLIP
+    if (found) above = !above;  // the other choice: must be caught
+#endif
+    return found && above ? p : u;
+}
+static long long check_T(float T, float u, const std::vector<float>& svals) {
+    long long bad = 0;
+    for (float s : svals) {
+        for (uint32_t h = 0; h < 65536; ++h) {
+            const float x = bf(h << 16);
+            if (!(std::fabs(x) <= s)) continue;
+            const bool dec = !std::signbit(std::fmaf(-T, s, x));
+            const bool ref = key(x / s) >= key(u);
+            if (dec != ref) {
+                if (bad < 5) std::printf("  T mismatch x=%a s=%a u=%a T=%a dec=%d ref=%d\n", x, s, u, T, dec, ref);
+                ++bad;
+            }
+        }
+    }
+    return bad;
 }
 static long long check(const Thr& t, bool half, const std::vector<float>& svals) {
     long long bad = 0, n = 0;
@@ -102,7 +161,16 @@ int main(int argc, char** argv) {
     const unsigned nt = std::max(1u, std::min(8u, std::thread::hardware_concurrency()));
     for (unsigned w = 0; w < nt; ++w)
         pool.emplace_back([&] {
-            for (size_t i = next++; i < thr.size(); i = next++) bad += check(thr[i], false, sb) + check(thr[i], true, sh);
+            for (size_t i = next++; i < thr.size(); i = next++) {
+                bad += check(thr[i], false, sb) + check(thr[i], true, sh);
+                const float T = make_T(thr[i].u, thr[i].p);
+                if (T != T) {
+                    std::printf("  T form not applicable at u=%a\n", thr[i].u);
+                    ++bad;
+                } else {
+                    bad += check_T(T, thr[i].u, sb);
+                }
+            }
         });
     for (auto& th : pool) th.join();
     const int nthr = static_cast<int>(thr.size());
