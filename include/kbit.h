@@ -218,9 +218,11 @@ KBIT_DECLARE_NESTED(bf16, uint16_t)
  *               fp32 absmax) or dequantize_4bit_nested_bf16 (nested state)
  *               on the same state, element n*K + k;
  *   out[m][n] = RN_bf16( sum over k of X[m][k] * W[n][k] ): exact products,
- *               fp32 sums in an unspecified order, so the result is within
- *               (K + 16) * 2^-24 * sum |X[m][k] * W[n][k]| of the exact sum
- *               before the final rounding.
+ *               fp32 sums in an unspecified but fixed order (the same
+ *               inputs give the same bits), so the result is within
+ *               gamma(K - 1) * sum |X[m][k] * W[n][k]| of the exact sum
+ *               before the final rounding, gamma(j) = j*u/(1 - j*u), u =
+ *               2^-23 (one fp32 ulp per addition).
  * X      : device, M x K bf16 (row-major, 16-byte aligned).
  * packed : device, N*K/32*4 uint32 (16-byte aligned).
  * out    : device, M x N bf16 (row-major, output).
