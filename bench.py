@@ -306,6 +306,18 @@ def _cpu_worker(arg):
     return _cpu_chunks(list(range(w, ROWS // 128, P)) or [w % (ROWS // 128)], seconds)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(seconds_target):
     """Time the CPU oracle on a bounded sample of the same workload: one
     thread, then chunk-parallel over the host's cores (forked workers; call
@@ -316,7 +328,10 @@ def cpu_baseline(seconds_target):
 
     _CPU_X = synth.weight(ROWS, COLS, "bf16", seed=synth.SEED_WEIGHT_SHAPES)
     n1, t1 = _cpu_chunks(list(range(ROWS // 128)), seconds_target)
-    P = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    # at most 16 workers: the job's CPU share on a one-GPU host is 16 cores,
+    # whatever the affinity mask shows
+    P = max(1, min(16, affinity))
     with mp.get_context("fork").Pool(P) as pool:
         res = pool.map(_cpu_worker, [(w, P, seconds_target) for w in range(P)])
     nP = sum(r[0] for r in res)
@@ -336,6 +351,10 @@ def cpu_baseline(seconds_target):
                   f"over {P} forked processes for {tP:.1f} s; each chunk quantize + pack + nested encode + nested "
                   f"dequantize, numpy float32",
         "elements_per_s": round(nP / tP, 1),
+        "cpu_model": _cpu_model(),
+        "host_cores": os.cpu_count(),
+        "affinity_cores": affinity,
+        "cores_note": "workers capped at 16, the CPU share of one GPU's job on this host",
         "single_thread": {"value": gbs(n1, t1), "elements_per_s": round(n1 / t1, 1),
                           "sample": f"{n1} elements, chunks in order, one process, {t1:.1f} s"},
     }
@@ -399,6 +418,74 @@ def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, s
             "algorithmic_flops": flops, "TFLOP/s": round(tflops, 3),
             "frac_of_fp32_valu_peak": round(tflops / VALU_FP32_PEAK_TFLOPS, 4),
             "rows_per_s": round(rows / (avg * 1e-3), 1)}
+
+
+NESTED_CELL_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008), (8192, 8192))
+
+
+def bench_nested_cells(torch, kb, dev, reps, sets=4):
+    """Nested 4-bit dequantize for NF4 and FP4 x fp16/bf16/fp32 x the four
+    weight shapes (24 cells): N(0, 0.02) weight, blocksize 64, state from
+    the library's own quantize and nested encode; each cell timed in rounds
+    over rotated buffer sets."""
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}
+    esz = {"fp16": 2, "bf16": 2, "fp32": 4}
+    qmap = torch.from_numpy(kb.dynamic_map8()).to(dev)
+    cells = []
+    for cbname, cbv in (("nf4", kb.codebook_nf(4)), ("fp4", kb.codebook_fp4())):
+        cbt = torch.from_numpy(cbv).to(dev)
+        for name, dt in tdt.items():
+            for rows, cols in NESTED_CELL_SHAPES:
+                n = rows * cols
+                nb = n // BLOCK
+                g = torch.Generator(device=dev).manual_seed(rows * 7 + cols)
+                states = []
+                for i in range(sets):
+                    A = (torch.randn(n, generator=g, device=dev) * 0.02).to(dt)
+                    packed, absmax = kb.quantize_kbit(A, cbt, 4, BLOCK)
+                    code, a2, off = kb.quantize_nested_absmax(absmax, qmap)
+                    states.append((packed, code, a2, float(off.item()), torch.empty(n, dtype=dt, device=dev)))
+                    del A, absmax
+
+                # checked once through the binding, then timed through the
+                # C entry point with prepared arguments (a small cell's
+                # kernel is shorter than the binding's per-call checks)
+                for i in range(sets):
+                    p_, c_, a2_, o_, out_ = states[i]
+                    kb.dequantize_4bit_nested(p_, cbt, c_, qmap, a2_, o_, n, dt, BLOCK, out=out_)
+                fn = getattr(kb.lib(), f"dequantize_4bit_nested_{name}")
+                sp = torch.cuda.current_stream(dev).cuda_stream
+                dargs = [(p_.data_ptr(), cbt.data_ptr(), c_.data_ptr(), qmap.data_ptr(), a2_.data_ptr(), o_,
+                          out_.data_ptr(), n, BLOCK, sp) for p_, c_, a2_, o_, out_ in states]
+
+                def d(i):
+                    if fn(*dargs[i]):
+                        raise RuntimeError("nested dequantize launch failed")
+
+                for _ in range(3):
+                    for i in range(sets):
+                        d(i)
+                torch.cuda.synchronize()
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+                ev[0].record()
+                for r in range(reps):
+                    for i in range(sets):
+                        d(i)
+                    ev[r + 1].record()
+                torch.cuda.synchronize()
+                ts = np.array([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]) / sets * 1e3
+                nbytes = n // 2 + nb + 4 * (-(-nb // 256)) + esz[name] * n + 4 * 256 + 4 * 16
+                us = float(ts.mean())
+                cells.append({"codebook": cbname, "dtype": name, "shape": [rows, cols], "avg_us": round(us, 3),
+                              "median_us": round(float(np.median(ts)), 3), "bytes": nbytes,
+                              "GB/s": round(nbytes / (us * 1e-6) / 1e9, 2),
+                              "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+                del states
+                torch.cuda.empty_cache()
+    return {"workload": "nested 4-bit dequantize, N(0,0.02) weights, blocksize 64, groups of 256, dynamic map; "
+                        "NF4/FP4 x fp16/bf16/fp32 x 4096^2, 11008x4096, 4096x11008, 8192^2; 4 rotated buffer sets, "
+                        "state from the library's quantize + nested encode",
+            "cells": cells}
 
 
 def bench_sweep(torch, kb, dev, reps, sets=4):
@@ -800,7 +887,7 @@ def main(argv=None):
 
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
-    fp4 = warm = act = act_block = lin = sweep = None
+    fp4 = warm = act = act_block = lin = sweep = cells = None
     if not args.headline_only:
         pair = {"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only}
         cb_nf = cb
@@ -819,6 +906,7 @@ def main(argv=None):
                          for r, dd, pp in ACT_BLOCK_CASES]
         lin = bench_linear(torch, kb, synth, dev)
         sweep = bench_sweep(torch, kb, dev, reps)
+        cells = bench_nested_cells(torch, kb, dev, max(4, reps // 2))
 
     # The timed region (after the side measurements, which also bring the
     # GPU to its working clocks): args.steps steps, launched eagerly (Python issues a
@@ -917,12 +1005,17 @@ def main(argv=None):
         "act_block_hadamard": act_block,
         "linear_4bit": lin,
         "dtype_k_sweep": sweep,
+        "nested_dequant_cells": cells,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(dev),
         "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
         "hip": torch.version.hip,
+        "environment": {"torch": torch.__version__, "rocm_hip": torch.version.hip, "python": sys.version.split()[0],
+                        "cpu_model": _cpu_model(), "host_cores": os.cpu_count(),
+                        "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+                        "hbm_bytes": torch.cuda.get_device_properties(dev).total_memory},
     }
     print(json.dumps(line), flush=True)
     return 0
