@@ -219,7 +219,10 @@ def _nested_state(packed, codebook16, absmax_code, qmap2, absmax2, n, nb):
 
 def dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offset, n, dtype, blocksize,
                            out=None):
-    """Nested 4-bit dequantize with the scale rebuild fused into the decode."""
+    """Nested 4-bit dequantize with the scale rebuild fused into the decode.
+
+    offset: a float, or a one-element float32 tensor on the device (such as
+    quantize_nested_absmax's offset output), which the kernel reads itself."""
     torch = _torch()
     t = _dtype_name(dtype)
     nb = _blocks(n, blocksize)
@@ -228,10 +231,18 @@ def dequantize_4bit_nested(packed, codebook16, absmax_code, qmap2, absmax2, offs
     _nested_state(packed, codebook16, absmax_code, qmap2, absmax2, n, nb)
     _buf(out, "out", dtype, n)
     _same_device(packed, out=out)
-    name = f"dequantize_4bit_nested_{t}"
+    if isinstance(offset, torch.Tensor):
+        # read on the device when the kernel starts: no host round trip
+        _buf(offset, "offset", torch.float32, 1)
+        _same_device(packed, offset=offset)
+        name = f"dequantize_4bit_nested_{t}_offptr"
+        off_arg = _ptr(offset)
+    else:
+        name = f"dequantize_4bit_nested_{t}"
+        off_arg = ct.c_float(float(offset))
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(packed), _ptr(codebook16), _ptr(absmax_code), _ptr(qmap2), _ptr(absmax2),
-                    ct.c_float(float(offset)), _ptr(out), n, blocksize, _stream(packed.device)))
+                    off_arg, _ptr(out), n, blocksize, _stream(packed.device)))
     return out
 
 
@@ -290,7 +301,8 @@ def linear_4bit(X, packed, codebook16, N, blocksize, absmax=None, absmax_code=No
                 offset=None, out=None):
     """out[M, N] = X[M, K] @ W[N, K]^T with W decoded from its 4-bit planes inside
     the kernel (bf16 in and out).  Scales: fp32 ``absmax``, or the nested state
-    (``absmax_code``, ``qmap2``, ``absmax2``, ``offset``)."""
+    (``absmax_code``, ``qmap2``, ``absmax2``, ``offset`` as a float or a
+    one-element float32 device tensor read by the kernel)."""
     torch = _torch()
     if X.dtype != torch.bfloat16 or X.dim() != 2:
         raise TypeError("X must be a 2-D bfloat16 tensor")
@@ -308,7 +320,14 @@ def linear_4bit(X, packed, codebook16, N, blocksize, absmax=None, absmax_code=No
         _buf(codebook16, "codebook16", torch.float32, 16)
         _buf(absmax, "absmax", torch.float32, nb)
         _same_device(X, packed=packed, codebook16=codebook16, absmax=absmax)
-    if absmax_code is not None:
+    if absmax_code is not None and isinstance(offset, torch.Tensor):
+        _buf(offset, "offset", torch.float32, 1)
+        _same_device(X, offset=offset)
+        name = "linear_4bit_nested_bf16_offptr"
+        status = lib().linear_4bit_nested_bf16_offptr(_ptr(X), M, K, _ptr(packed), _ptr(codebook16),
+                                                      _ptr(absmax_code), _ptr(qmap2), _ptr(absmax2), _ptr(offset),
+                                                      N, blocksize, _ptr(out), _stream(X.device))
+    elif absmax_code is not None:
         name = "linear_4bit_nested_bf16"
         status = lib().linear_4bit_nested_bf16(_ptr(X), M, K, _ptr(packed), _ptr(codebook16), _ptr(absmax_code),
                                                _ptr(qmap2), _ptr(absmax2), ct.c_float(float(offset)), N,

@@ -33,6 +33,7 @@ def _signatures():
         ("kbit_nested_workspace_bytes", [_i64]),
         ("linear_kbit_bf16_k4", [_p, _i64, _i32, _p, _p, _p, _i32, _i32, _p, _p]),
         ("linear_4bit_nested_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p, _f32, _i32, _i32, _p, _p]),
+        ("linear_4bit_nested_bf16_offptr", [_p, _i64, _i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _p, _p]),
         ("quantize_nested_absmax", [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]),
         ("kbit_nested_noalloc_scratch_bytes", []),
         ("quantize_nested_absmax_noalloc", [_p, _i64, _p, _p, _p, _p, _p]),
@@ -44,6 +45,7 @@ def _signatures():
             sig.append((f"quantize_kbit_e4m4_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
             sig.append((f"dequantize_kbit_e4m4_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
         sig.append((f"dequantize_4bit_nested_{t}", [_p, _p, _p, _p, _p, _f32, _p, _i64, _i32, _p]))
+        sig.append((f"dequantize_4bit_nested_{t}_offptr", [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _p]))
     return sig
 
 

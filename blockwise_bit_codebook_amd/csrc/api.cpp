@@ -78,19 +78,19 @@ int do_dequantize(Dtype t, ScaleFmt f, int K, const uint32_t* packed, const floa
 }
 
 int do_nested(Dtype t, const uint32_t* packed, const float* codebook16, const uint8_t* code,
-              const float* qmap2, const float* absmax2, float offset, void* out, int64_t n,
-              int32_t blocksize, void* stream) {
+              const float* qmap2, const float* absmax2, float offset, const float* offset_ptr, void* out,
+              int64_t n, int32_t blocksize, void* stream) {
     const int l2b = log2_block(blocksize);
     if (l2b < 0) return KBIT_EBLOCK;
     if (n < 0 || n > kMaxElems) return KBIT_EINVAL;
     if (n == 0) return KBIT_OK;
     if (!packed || !codebook16 || !code || !qmap2 || !absmax2 || !out) return KBIT_EINVAL;
     if (!aligned(out, 16) || !aligned(codebook16, 4) || !aligned(qmap2, 4) || !aligned(absmax2, 4) ||
-        !aligned(packed, 4))
+        !aligned(packed, 4) || !aligned(offset_ptr, 4))
         return KBIT_EALIGN;
     if (current_device_cus() <= 0) return KBIT_EDEVICE;
-    return map_launch(
-        launch_dequantize_nested(t, packed, codebook16, code, qmap2, absmax2, offset, out, n, l2b, stream));
+    return map_launch(launch_dequantize_nested(t, packed, codebook16, code, qmap2, absmax2, offset, offset_ptr, out,
+                                               n, l2b, stream));
 }
 
 // Shared checks of the linear entry points (K % 32 == 0; packed 16-byte
@@ -203,8 +203,16 @@ KBIT_DEFINE_ALL_K(bf16, uint16_t, Dtype::bf16)
                                        const uint8_t* absmax_code, const float* qmap2,                \
                                        const float* absmax2, float offset, CTYPE* out, int64_t n,     \
                                        int32_t blocksize, void* stream) {                             \
-        return kbit::do_nested(DT, packed, codebook16, absmax_code, qmap2, absmax2, offset, out, n,   \
-                               blocksize, stream);                                                    \
+        return kbit::do_nested(DT, packed, codebook16, absmax_code, qmap2, absmax2, offset, nullptr,  \
+                               out, n, blocksize, stream);                                            \
+    }                                                                                                 \
+    int dequantize_4bit_nested_##TNAME##_offptr(const uint32_t* packed, const float* codebook16,      \
+                                                const uint8_t* absmax_code, const float* qmap2,       \
+                                                const float* absmax2, const float* offset, CTYPE* out, \
+                                                int64_t n, int32_t blocksize, void* stream) {         \
+        if (n > 0 && offset == nullptr) return KBIT_EINVAL;                                           \
+        return kbit::do_nested(DT, packed, codebook16, absmax_code, qmap2, absmax2, 0.0f, offset, out, \
+                               n, blocksize, stream);                                                 \
     }
 KBIT_DEFINE_NESTED(fp32, float, Dtype::fp32)
 KBIT_DEFINE_NESTED(fp16, uint16_t, Dtype::fp16)
@@ -259,18 +267,38 @@ int linear_kbit_bf16_k4(const uint16_t* X, int64_t M, int32_t K, const uint32_t*
     return kbit::map_launch(kbit::launch_linear4_plain(X, M, K, packed, codebook16, absmax, N, l2b, out, stream));
 }
 
+namespace kbit {
+namespace {
+int do_linear_nested(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed, const float* codebook16,
+                     const uint8_t* absmax_code, const float* qmap2, const float* absmax2, float offset,
+                     const float* offset_ptr, int32_t N, int32_t blocksize, uint16_t* out, void* stream) {
+    int l2b = 0;
+    const int c = check_linear(X, M, K, packed, codebook16, N, blocksize, out, l2b);
+    if (c != 1) return c;
+    if (!absmax_code || !qmap2 || !absmax2) return KBIT_EINVAL;
+    if (!aligned(qmap2, 4) || !aligned(absmax2, 4) || !aligned(offset_ptr, 4)) return KBIT_EALIGN;
+    if (current_device_cus() <= 0) return KBIT_EDEVICE;
+    return map_launch(launch_linear4_nested(X, M, K, packed, codebook16, absmax_code, qmap2, absmax2, offset,
+                                            offset_ptr, N, l2b, out, stream));
+}
+}  // namespace
+}  // namespace kbit
+
 int linear_4bit_nested_bf16(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed,
                             const float* codebook16, const uint8_t* absmax_code, const float* qmap2,
                             const float* absmax2, float offset, int32_t N, int32_t blocksize, uint16_t* out,
                             void* stream) {
-    int l2b = 0;
-    const int c = kbit::check_linear(X, M, K, packed, codebook16, N, blocksize, out, l2b);
-    if (c != 1) return c;
-    if (!absmax_code || !qmap2 || !absmax2) return KBIT_EINVAL;
-    if (!kbit::aligned(qmap2, 4) || !kbit::aligned(absmax2, 4)) return KBIT_EALIGN;
-    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
-    return kbit::map_launch(kbit::launch_linear4_nested(X, M, K, packed, codebook16, absmax_code, qmap2, absmax2,
-                                                        offset, N, l2b, out, stream));
+    return kbit::do_linear_nested(X, M, K, packed, codebook16, absmax_code, qmap2, absmax2, offset, nullptr, N,
+                                  blocksize, out, stream);
+}
+
+int linear_4bit_nested_bf16_offptr(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed,
+                                   const float* codebook16, const uint8_t* absmax_code, const float* qmap2,
+                                   const float* absmax2, const float* offset, int32_t N, int32_t blocksize,
+                                   uint16_t* out, void* stream) {
+    if (M > 0 && offset == nullptr) return KBIT_EINVAL;
+    return kbit::do_linear_nested(X, M, K, packed, codebook16, absmax_code, qmap2, absmax2, 0.0f, offset, N,
+                                  blocksize, out, stream);
 }
 
 int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const uint32_t* sign_bits,

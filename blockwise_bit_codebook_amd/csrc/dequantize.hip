@@ -226,10 +226,13 @@ template <class E, int U = kSteps, bool NTS = kNtStore>
 __global__ __launch_bounds__(kThreads) void dequantize_nested_kernel(
     const uint32_t* __restrict__ packed, const float* __restrict__ cb, const uint8_t* __restrict__ code,
     const float* __restrict__ qmap2, const float* __restrict__ absmax2, float offset,
-    typename E::storage* __restrict__ out, int64_t n, int log2B) {
+    const float* __restrict__ offset_ptr, typename E::storage* __restrict__ out, int64_t n, int log2B) {
     __shared__ float cb_lds[32];
     __shared__ float2 pair_lds[256];
     __shared__ float qmap_lds[256];
+    // the offset from device memory when given (a uniform load, in flight
+    // with the table staging), else the argument
+    if (offset_ptr != nullptr) offset = *offset_ptr;
     stage_codebook<4>(cb, cb_lds, pair_lds);
     qmap_lds[threadIdx.x] = qmap2[threadIdx.x];
     __syncthreads();
@@ -256,12 +259,13 @@ int launch_plain(const uint32_t* packed, const float* cb, Scale scale, void* out
 
 template <class E, int U = kSteps, bool NTS = kNtStore>
 int launch_nested(const uint32_t* packed, const float* cb, const uint8_t* code, const float* qmap2,
-                  const float* absmax2, float offset, void* out, int64_t n, int log2B, void* stream) {
+                  const float* absmax2, float offset, const float* offset_ptr, void* out, int64_t n, int log2B,
+                  void* stream) {
     auto kern = dequantize_nested_kernel<E, U, NTS>;
     static std::atomic<int> occupancy[kMaxDevices];
     const int64_t grid = persistent_grid(kern, occupancy, (n + kWaveTile * U - 1) / (kWaveTile * U));
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), packed, cb, code, qmap2, absmax2, offset,
+                       static_cast<hipStream_t>(stream), packed, cb, code, qmap2, absmax2, offset, offset_ptr,
                        static_cast<typename E::storage*>(out), n, log2B);
     return static_cast<int>(hipGetLastError());
 }
@@ -300,14 +304,18 @@ int launch_dequantize(Dtype t, ScaleFmt f, int K, const uint32_t* packed, const 
 
 int launch_dequantize_nested(Dtype t, const uint32_t* packed, const float* codebook16,
                              const uint8_t* code, const float* qmap2, const float* absmax2,
-                             float offset, void* out, int64_t n, int log2B, void* stream) {
+                             float offset, const float* offset_ptr, void* out, int64_t n, int log2B,
+                             void* stream) {
     switch (t) {
         case Dtype::fp32:
-            return launch_nested<Fp32>(packed, codebook16, code, qmap2, absmax2, offset, out, n, log2B, stream);
+            return launch_nested<Fp32>(packed, codebook16, code, qmap2, absmax2, offset, offset_ptr, out, n, log2B,
+                                       stream);
         case Dtype::fp16:
-            return launch_nested<Fp16>(packed, codebook16, code, qmap2, absmax2, offset, out, n, log2B, stream);
+            return launch_nested<Fp16>(packed, codebook16, code, qmap2, absmax2, offset, offset_ptr, out, n, log2B,
+                                       stream);
         default:
-            return launch_nested<Bf16>(packed, codebook16, code, qmap2, absmax2, offset, out, n, log2B, stream);
+            return launch_nested<Bf16>(packed, codebook16, code, qmap2, absmax2, offset, offset_ptr, out, n, log2B,
+                                       stream);
     }
 }
 

@@ -21,7 +21,8 @@ int launch_dequantize(Dtype t, ScaleFmt f, int K, const uint32_t* packed, const 
 
 int launch_dequantize_nested(Dtype t, const uint32_t* packed, const float* codebook16,
                              const uint8_t* code, const float* qmap2, const float* absmax2,
-                             float offset, void* out, int64_t n, int log2B, void* stream);
+                             float offset, const float* offset_ptr, void* out, int64_t n, int log2B,
+                             void* stream);
 
 // Workspace bytes the nested-state encoder needs for nb blocks.
 int64_t nested_workspace_bytes(int64_t nb);
@@ -38,8 +39,8 @@ int launch_linear4_plain(const uint16_t* X, int64_t M, int K, const uint32_t* pa
                          const float* absmax, int N, int log2B, uint16_t* out, void* stream);
 
 int launch_linear4_nested(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* codebook16,
-                          const uint8_t* code, const float* qmap2, const float* absmax2, float offset, int N,
-                          int log2B, uint16_t* out, void* stream);
+                          const uint8_t* code, const float* qmap2, const float* absmax2, float offset,
+                          const float* offset_ptr, int N, int log2B, uint16_t* out, void* stream);
 
 int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream);

@@ -32,6 +32,8 @@
 #include "kbit_internal.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace kbit {
 namespace {
 
@@ -57,6 +59,7 @@ struct LinNested {
     const uint8_t* code;
     const float* absmax2;
     float offset;
+    const float* offset_ptr;  // when not null, the offset is read from here at kernel start
     struct Raw {
         uint32_t code;
         float a2;
@@ -114,6 +117,9 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
                                                               uint16_t* __restrict__ out) {
     constexpr bool kXAhead = MT == 1;
     using C = Chunk<Scale, kXAhead>;
+    if constexpr (std::is_same<Scale, LinNested>::value) {
+        if (sc.offset_ptr != nullptr) sc.offset = *sc.offset_ptr;
+    }
     __shared__ float2 pair_lds[256];
     __shared__ float qmap_lds[256];
     __shared__ float red[kLinWaves][MT][16][17];
@@ -253,10 +259,10 @@ int launch_linear4_plain(const uint16_t* X, int64_t M, int K, const uint32_t* pa
 }
 
 int launch_linear4_nested(const uint16_t* X, int64_t M, int K, const uint32_t* packed, const float* codebook16,
-                          const uint8_t* code, const float* qmap2, const float* absmax2, float offset, int N,
-                          int log2B, uint16_t* out, void* stream) {
-    return launch_linear4(X, M, K, packed, codebook16, LinNested{code, absmax2, offset}, qmap2, N, log2B, out,
-                          stream);
+                          const uint8_t* code, const float* qmap2, const float* absmax2, float offset,
+                          const float* offset_ptr, int N, int log2B, uint16_t* out, void* stream) {
+    return launch_linear4(X, M, K, packed, codebook16, LinNested{code, absmax2, offset, offset_ptr}, qmap2, N, log2B,
+                          out, stream);
 }
 
 }  // namespace kbit

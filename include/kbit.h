@@ -198,12 +198,24 @@ KBIT_DECLARE_E4M4_ALL_K(bf16, uint16_t)
  * absmax2     : device, ceil(ceil(n/B)/256) float32.
  * offset      : the fp32 mean offset (by value).
  * out         : device, n elements of the named type (output).
+ * The _offptr variants read the offset from device memory instead (one
+ * float32, 4-byte aligned, e.g. the offset output of
+ * quantize_nested_absmax), when the kernel starts: quantize, nested
+ * encode and nested dequantize then run as one stream-ordered chain (or
+ * one captured graph) with no read-back to the host.  Results are
+ * identical to the by-value entry point's with that offset.  A null
+ * offset is KBIT_EINVAL (unless n == 0).
  * --------------------------------------------------------------------- */
-#define KBIT_DECLARE_NESTED(TNAME, CTYPE)                                               \
-    int dequantize_4bit_nested_##TNAME(const uint32_t* packed, const float* codebook16, \
-                                       const uint8_t* absmax_code, const float* qmap2,  \
-                                       const float* absmax2, float offset, CTYPE* out,  \
-                                       int64_t n, int32_t blocksize, void* stream);
+#define KBIT_DECLARE_NESTED(TNAME, CTYPE)                                                        \
+    int dequantize_4bit_nested_##TNAME(const uint32_t* packed, const float* codebook16,          \
+                                       const uint8_t* absmax_code, const float* qmap2,           \
+                                       const float* absmax2, float offset, CTYPE* out,           \
+                                       int64_t n, int32_t blocksize, void* stream);              \
+    int dequantize_4bit_nested_##TNAME##_offptr(const uint32_t* packed, const float* codebook16, \
+                                                const uint8_t* absmax_code, const float* qmap2,  \
+                                                const float* absmax2, const float* offset,       \
+                                                CTYPE* out, int64_t n, int32_t blocksize,        \
+                                                void* stream);
 KBIT_DECLARE_NESTED(fp32, float)
 KBIT_DECLARE_NESTED(fp16, uint16_t)
 KBIT_DECLARE_NESTED(bf16, uint16_t)
@@ -236,6 +248,13 @@ int linear_4bit_nested_bf16(const uint16_t* X, int64_t M, int32_t K, const uint3
                             const float* codebook16, const uint8_t* absmax_code, const float* qmap2,
                             const float* absmax2, float offset, int32_t N, int32_t blocksize,
                             uint16_t* out, void* stream);
+/* The same with the offset read from device memory (one float32, 4-byte
+ * aligned; null is KBIT_EINVAL unless M == 0), as the _offptr nested
+ * dequantize entry points. */
+int linear_4bit_nested_bf16_offptr(const uint16_t* X, int64_t M, int32_t K, const uint32_t* packed,
+                                   const float* codebook16, const uint8_t* absmax_code,
+                                   const float* qmap2, const float* absmax2, const float* offset,
+                                   int32_t N, int32_t blocksize, uint16_t* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * Nested-state encoder: the input of dequantize_4bit_nested from the fp32

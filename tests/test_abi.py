@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 24 + 3 + 2 + 2 + 2 + 2, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 3 + 2 + 2 + 2 + 2 + 1, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -101,6 +101,10 @@ def test_validation_codes_before_any_device_access():
     nd = lib.dequantize_4bit_nested_fp16
     assert nd(_A16, _A16, None, _A16, _A16, ct.c_float(0.0), _A16, 10, 64, None) == -1
     assert nd(_A16, _A16, _A16, _A16, _A16, ct.c_float(0.0), _A16, 10, 96, None) == -2
+    ndp = lib.dequantize_4bit_nested_fp16_offptr
+    assert ndp(_A16, _A16, _A16, _A16, _A16, None, _A16, 10, 64, None) == -1      # no offset
+    assert ndp(_A16, _A16, _A16, _A16, _A16, ct.c_void_p(0x20002), _A16, 10, 64, None) == -3  # offset misaligned
+    assert ndp(None, None, None, None, None, None, None, 0, 64, None) == 0        # empty: no-op
     qe = lib.quantize_kbit_e4m4_fp16_k2
     _B1 = ct.c_void_p(0x30001)                                     # byte-aligned only
     assert qe(_A16, _A16, _B1, _A16, 10, 48, None) == -2
@@ -141,6 +145,9 @@ def test_validation_codes_before_any_device_access():
     assert li(_A16, 4, 64, _A16, _A16, None, 64, 64, _A16, None) == -1            # no absmax
     ln = lib.linear_4bit_nested_bf16
     assert ln(_A16, 4, 64, _A16, _A16, None, _A16, _A16, ct.c_float(0), 64, 64, _A16, None) == -1
+    lnp = lib.linear_4bit_nested_bf16_offptr
+    assert lnp(_A16, 4, 64, _A16, _A16, _A16, _A16, _A16, None, 64, 64, _A16, None) == -1       # no offset
+    assert lnp(_A16, 4, 64, _A16, _A16, _A16, _A16, _A16, ct.c_void_p(0x20002), 64, 64, _A16, None) == -3
     assert ln(_A4, 4, 64, _A16, _A16, _A16, _A16, _A16, ct.c_float(0), 64, 64, _A16, None) == -3
     act = lib.quantize_act_fwht_k4_bf16
     assert act(_A16, 4, 2000, _A16, _A16, _A16, _A16, None) == -1  # d not a multiple of 256

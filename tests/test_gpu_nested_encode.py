@@ -86,8 +86,9 @@ def test_other_maps():
 @pytest.mark.parametrize("shape", ["wide11008", "tall11008", "square8192"])
 def test_chain_quantize_encode_nested_dequantize(shape):
     # bf16 weight of each shape plus a 192-element tail, B = 64: quantize,
-    # encode the absmax and nested-dequantize on the GPU; the oracle runs the
-    # same chain from the input alone, and every stage is compared in full
+    # encode the absmax and nested-dequantize on the GPU as one stream-ordered
+    # chain; the oracle runs the same chain from the input alone, and every
+    # stage is compared in full
     import torch
     rows, cols = synth.WEIGHT_SHAPES[shape]
     B = 64
@@ -98,8 +99,8 @@ def test_chain_quantize_encode_nested_dequantize(shape):
     case(f"nested chain {shape}+{synth.TAIL_EXTRA} bf16")
     packed, absmax = kb.quantize_kbit(to_dev(x, "bf16"), to_dev(cb), 4, B)
     code, a2, off = kb.quantize_nested_absmax(absmax, to_dev(q))
-    out = kb.dequantize_4bit_nested(packed, to_dev(cb), code, to_dev(q), a2, float(off.item()), n,
-                                    torch.bfloat16, B)
+    # the offset stays on the device: the kernel reads it (no host round trip)
+    out = kb.dequantize_4bit_nested(packed, to_dev(cb), code, to_dev(q), a2, off, n, torch.bfloat16, B)
     torch.cuda.synchronize()
     ww, wa = kbit.quantize_packed(numerics.widen(x, "bf16"), cb, 4, B)
     assert_bits_equal(bits(absmax), np_bits(wa), "absmax")
