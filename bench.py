@@ -253,7 +253,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     header = ["# rocprofv3 summary: k-bit quantize / dequantize kernels, 8192x8192 bf16, NF4, blocksize 64", "",
               "The bench step is quantize_kbit_bf16_k4 + dequantize_4bit_nested_bf16; the E4M4-scale pair, "
               "the plain fp32-scale dequantize and the nested-state encoder (quantize_nested_absmax: "
-              "nested_bins/offset/encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements."]
+              "nested_bins_kernel + nested_encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements."]
     return _summarize_into(table, trace_dir, fetch_dir, write_dir, header, PROFILE_COMMANDS,
                            "kbit_kernels_8192sq_bf16_nf4_b64.md",
                            timed_last={"quantize_kbit_bf16_k4": PROFILE_STEPS,
@@ -362,7 +362,11 @@ def cpu_baseline(seconds_target):
 
 ACT_ROWS = ACT_D = 4096
 ACT_FLOPS_PER_ELEM = 15          # 12 butterfly add/sub + square + add (norm tree) + divide
-VALU_FP32_PEAK_TFLOPS = 157.3    # 256 CUs x 4 SIMDs x 32 fp32 lanes (packed) x 2 x 2.4 GHz
+# The activation path's arithmetic is single fp32 operations (adds, compares,
+# one multiply), not fused multiply-adds, and packed fp32 is not used: its
+# roof is the non-packed VALU issue rate, one lane operation per lane per
+# clock: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9   # 39.3e12 lane operations / s
 
 
 def act_bytes(rows=ACT_ROWS, d=ACT_D):
@@ -416,7 +420,9 @@ def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, s
             "avg_us": round(avg * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
             "bytes": nbytes, "GB/s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
             "algorithmic_flops": flops, "TFLOP/s": round(tflops, 3),
-            "frac_of_fp32_valu_peak": round(tflops / VALU_FP32_PEAK_TFLOPS, 4),
+            "alu": {"bound": "alu", "achieved": round(tflops * 1e12, 1), "peak": VALU_LANE_OPS_PEAK,
+                    "unit": "lane-ops/s", "frac": round(tflops * 1e12 / VALU_LANE_OPS_PEAK, 4),
+                    "note": "algorithmic operations (15 per element) against the non-packed VALU issue rate"},
             "rows_per_s": round(rows / (avg * 1e-3), 1)}
 
 
