@@ -57,7 +57,7 @@
 //     entry points ([QLORA-2] PATCH 005), as its one-byte E4M4 code; the
 //     indices come from the fp32 absmax either way.
 //   * Persistent grid of 1024-thread workgroups (16 waves, at most 64 VGPRs
-//     so two groups share a CU; 512 threads for K = 5).  Wave v takes wave
+//     so two groups share a CU; 512-thread groups for K = 5).  Wave v takes wave
 //     rows v, v + nwaves, ..., so the grid streams through one narrow
 //     window of memory, and keeps a ring of 4 rows (16-bit types) or 2
 //     (fp32) in flight: 4 KB of input per wave, which with 32 waves per CU
@@ -521,8 +521,8 @@ int launch_cfg(const float* cb, const void* A, void* absmax, uint32_t* packed, i
 template <class E, class S, int K>
 int launch_k(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
              void* stream) {
-    // K = 5 runs 512-thread groups: its kernels need up to 64 VGPRs only
-    // with the smaller group, whose waves fill the SIMDs' remaining slots.
+    // K = 5 runs 512-thread groups (52-54 VGPRs, 8 waves per SIMD either
+    // way); 1024-thread groups measured the same within noise.
     constexpr int TH = K == 5 ? 512 : kQThreads;
     switch (log2B) {
         case 5: return launch_cfg<E, S, K, 5, TH>(cb, A, absmax, packed, n, log2B, stream);
