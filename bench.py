@@ -6,8 +6,9 @@ bf16 (per-block scales rebuilt from 8-bit codes over groups of 256 plus a
 mean offset), on an 8192 x 8192 weight drawn from N(0, 0.02).  Inputs live in
 HBM before timing starts.  Several buffer sets are rotated so that the
 256 MB last-level cache cannot hold a step's working set.  The timed region
-is exactly --steps steps (after --warmup untimed ones), launched eagerly,
-with fence-free HIP events at its two ends on the kernels' stream.
+is exactly --steps steps (after --warmup untimed ones, which follow at least
+--settle-ms of back-to-back steps), launched eagerly, with fence-free HIP
+events at its two ends on the kernels' stream.
 
 Prints one JSON line.  ``value`` is the step's algorithmic bytes (read +
 written by both kernels) divided by the wall time per step, in GB/s.
@@ -46,6 +47,7 @@ ROWS = COLS = 8192
 BLOCK = 64
 K = 4
 GROUP2 = 256
+KERNEL_ROUNDS_MIN = 50  # rounds of back-to-back launches per step kernel for its launch duration
 
 
 def algorithmic_bytes(n):
@@ -80,6 +82,9 @@ def parse(argv=None):
     ap.add_argument("--warmup", type=int, default=300,
                     help="untimed steps right before the timed ones (about 18 ms at 8192^2; the GPU needs "
                          "some milliseconds of sustained load to reach its working clocks)")
+    ap.add_argument("--settle-ms", type=float, default=25.0,
+                    help="before each warmup, back-to-back steps for at least this long (the GPU reaches its "
+                         "sustained clocks only after some milliseconds of continuous load, whatever --warmup is)")
     ap.add_argument("--sets", type=int, default=4, help="rotated input/output buffer sets")
     ap.add_argument("--rr-reps", type=int, default=0,
                     help="rounds of the per-kernel timing (default: steps / sets, at least 5)")
@@ -133,6 +138,9 @@ KERNELS = {
 def _matches(pat, name):
     return all(p in name for p in pat)
 PROFILE_STEPS = 200  # --steps of the trace command below
+PROFILE_SETS = 4     # its --sets (the default)
+# launches of each step kernel in the rounds after its timed steps
+PROFILE_ROUND_LAUNCHES = max(KERNEL_ROUNDS_MIN, PROFILE_STEPS // PROFILE_SETS) * PROFILE_SETS
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o trace -- "
@@ -261,8 +269,8 @@ def summarize(trace_dir, fetch_dir, write_dir):
               "nested_bins_kernel + nested_encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements."]
     return _summarize_into(table, trace_dir, fetch_dir, write_dir, header, PROFILE_COMMANDS,
                            "kbit_kernels_8192sq_bf16_nf4_b64.md",
-                           timed_last={"quantize_kbit_bf16_k4": PROFILE_STEPS,
-                                       "dequantize_4bit_nested_bf16": PROFILE_STEPS})
+                           timed_last={"quantize_kbit_bf16_k4": PROFILE_ROUND_LAUNCHES,
+                                       "dequantize_4bit_nested_bf16": PROFILE_ROUND_LAUNCHES})
 
 
 def summarize_side(trace_dir, fetch_dir, write_dir):
@@ -837,6 +845,35 @@ def main(argv=None):
         step(s_)
     torch.cuda.synchronize()
 
+    # The two step kernels through their C entry points, with arguments
+    # prepared once per buffer set: the same calls quant_only and
+    # nested_only make, without the wrappers' per-call checks, so that
+    # Python stays well ahead of the GPU.
+    stream_ptr = torch.cuda.current_stream(dev).cuda_stream
+    qfn, dfn = kb.lib().quantize_kbit_bf16_k4, kb.lib().dequantize_4bit_nested_bf16
+    qargs = [(cb.data_ptr(), s_["A"].data_ptr(), s_["absmax"].data_ptr(), s_["packed"].data_ptr(), n, BLOCK,
+              stream_ptr) for s_ in sets]
+    dargs = [(s_["packed"].data_ptr(), cb.data_ptr(), s_["code"].data_ptr(), qmap.data_ptr(),
+              s_["absmax2"].data_ptr(), float(offset), s_["out"].data_ptr(), n, BLOCK, stream_ptr) for s_ in sets]
+
+    def settle():
+        # Steps back to back for at least --settle-ms (chunks of 16 with a
+        # sync after each), so that what follows starts at the GPU's
+        # sustained clocks however short --warmup is.
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        i = rc_ = 0
+        while True:
+            for _ in range(16):
+                j = i % args.sets
+                rc_ |= qfn(*qargs[j])
+                rc_ |= dfn(*dargs[j])
+                i += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() >= t_end:
+                break
+        if rc_:
+            raise RuntimeError(f"a settle launch failed: {kb.lib().kbit_strerror(rc_)}")
+
 
     # Side kernels: per-kernel launch time from events on the same stream, in
     # round robin: each round launches every kernel once per buffer set, with
@@ -862,6 +899,7 @@ def main(argv=None):
                        for r in range(reps)] for j, name in enumerate(fns)}
 
     # bring the GPU to its working clocks before the side measurements too
+    settle()
     for i in range(args.warmup):
         step(sets[i % args.sets])
     torch.cuda.synchronize()
@@ -926,19 +964,13 @@ def main(argv=None):
     # step by 1-2.5 us (measured), so the per-kernel launch durations of the
     # roofline come from the rounds right after the timed region: each step
     # kernel alone, back to back over the rotated buffer sets, with an event
-    # at each round's ends (args.steps launches of each kernel in all).
+    # at each round's ends (max(KERNEL_ROUNDS_MIN, steps / sets) rounds).
     # The events are created without the system-scope fence
     # (hipEventDisableSystemFence): default events add a cache flush per
-    # record.  All launches call the two C entry points directly with
-    # arguments prepared once per buffer set: the same calls quant_only and
-    # nested_only make, without the wrappers' per-call checks, so that
-    # Python stays well ahead of the GPU.
-    stream_ptr = torch.cuda.current_stream(dev).cuda_stream
-    qfn, dfn = kb.lib().quantize_kbit_bf16_k4, kb.lib().dequantize_4bit_nested_bf16
-    qargs = [(cb.data_ptr(), s_["A"].data_ptr(), s_["absmax"].data_ptr(), s_["packed"].data_ptr(), n, BLOCK,
-              stream_ptr) for s_ in sets]
-    dargs = [(s_["packed"].data_ptr(), cb.data_ptr(), s_["code"].data_ptr(), qmap.data_ptr(),
-              s_["absmax2"].data_ptr(), float(offset), s_["out"].data_ptr(), n, BLOCK, stream_ptr) for s_ in sets]
+    # record.  All launches call the two C entry points directly (qfn,
+    # dfn).  A settle period of back-to-back steps comes before the
+    # --warmup steps.
+    settle()
     for i in range(args.warmup):
         step(sets[i % args.sets])
     torch.cuda.synchronize()
@@ -963,7 +995,7 @@ def main(argv=None):
     value = (qbytes + nbytes) / (ms_step * 1e-3) / 1e9
 
     def launch_rounds(fn, argsets):
-        rounds = max(1, args.steps // len(argsets))
+        rounds = max(KERNEL_ROUNDS_MIN, args.steps // len(argsets))
         rm = hev.create(rounds + 1)
         code = 0
         hev.record(rm[0])
@@ -1015,6 +1047,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": round(ms_step, 5),
         "gpu_ms_per_step": round(gpu_ms / args.steps, 5),
         "higher_is_better": True,

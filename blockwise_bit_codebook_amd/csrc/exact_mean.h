@@ -39,13 +39,39 @@ KBIT_HD inline WidePieces wide_pieces(uint64_t v, int shift) {
 
 KBIT_HD inline int bit_length64(uint64_t v) { return v ? 64 - __builtin_clzll(v) : 0; }
 
-// fp32 bits of RN32((P - N) * 2^-149 / nb), 1 <= nb <= 2^36, from the limb
-// accumulators of P (positive values) and N (negative values): limb i
-// weighs 2^(32 i), each limb is below 2^61 (carries not yet resolved), and
-// |P - N| < 2^320.  Straight-line code for one thread: every array index is
-// a constant after unrolling.
+// Division by the block count nb (1 <= nb <= 2^36) of any n below 2^63,
+// without a divide instruction: with l = ceil(log2 nb) and
+// m = ceil(2^(63 + l) / nb), floor(n / nb) = floor(n * m / 2^(63 + l)).
+// (Division by an invariant integer through a multiply-high, after Granlund
+// and Montgomery, "Division by invariant integers using multiplication",
+// 1994.)  Why: n * m / 2^(63 + l) = n / nb + n * e / 2^(63 + l) with
+// m = 2^(63 + l) / nb + e, 0 <= e < 1, and the second term is below
+// 2^-l <= 1 / nb, while the fraction of n / nb is at most 1 - 1 / nb; so
+// the floor does not change.  m is below 2^64 (2^(l - 1) < nb unless nb is
+// 1, where m = 2^63).  The host builds it once per call.
+struct NbDivider {
+    uint64_t nb, m;
+    int l;
+};
+inline NbDivider make_nb_divider(uint64_t nb) {
+    int l = 0;
+    while ((1ull << l) < nb) ++l;
+    const unsigned __int128 num = (static_cast<unsigned __int128>(1) << (63 + l)) + (nb - 1);
+    return NbDivider{nb, static_cast<uint64_t>(num / nb), l};
+}
+KBIT_HD inline uint64_t div_nb(const NbDivider& d, uint64_t n) {  // n < 2^63
+    const unsigned __int128 p = static_cast<unsigned __int128>(n) * d.m;  // below 2^127
+    return static_cast<uint64_t>(p >> 63) >> d.l;
+}
+
+// fp32 bits of RN32((P - N) * 2^-149 / nb), 1 <= nb <= 2^36 (the divider
+// of nb), from the limb accumulators of P (positive values) and N (negative
+// values): limb i weighs 2^(32 i), each limb is below 2^61 (carries not yet
+// resolved), and |P - N| < 2^320.  Straight-line code for one thread: every
+// array index is a constant after unrolling.
 KBIT_HD inline uint32_t mean_from_limbs(const uint64_t (&pos)[kWideLimbs + 2], const uint64_t (&neg)[kWideLimbs + 2],
-                                        uint64_t nb) {
+                                        const NbDivider& div) {
+    const uint64_t nb = div.nb;
     constexpr int L = kWideLimbs + 2;
     // D = P - N as 32-bit digits plus a final carry (floor division by 2^32
     // at each limb keeps every intermediate within int64).
@@ -98,8 +124,9 @@ KBIT_HD inline uint32_t mean_from_limbs(const uint64_t (&pos)[kWideLimbs + 2], c
     const int s = 32 * (top - 2) + b + 1;
     bool sticky = low || (mid & ((1ull << (b + 1)) - 1ull)) != 0;
     // Q = Nq / nb has at least 27 bits; the value is (Q + fraction) * 2^s.
-    const uint64_t Q = Nq / nb;
-    sticky = sticky || (Nq % nb) != 0;
+    // Nq < 2^63 (its top bit is bit 62).
+    const uint64_t Q = div_nb(div, Nq);
+    sticky = sticky || Nq - Q * nb != 0;
     const int qb = bit_length64(Q);
     int E = qb - 1 + s - 149;  // exponent of the leading bit
     // drop dq low bits of Q: down to 24 significant bits, or to the 2^-149

@@ -13,23 +13,25 @@
 //                 - qmap2_i)|
 //
 // How: two launches on one stream.
-//   1. Each workgroup sums its values exactly into 32-bit-limb
-//      accumulators of the positive and the negative values (exact_mean.h):
-//      per round of 16 values per lane, each wave adds the integer
-//      significands of the values within 24 binades of its largest one into
-//      64-bit register sums (shifted to the window's bottom), sums those
-//      across the wave and adds them to the limbs; values further down go to
-//      per-wave LDS bins by (sign, exponent), folded into the limbs at the
-//      end.  The limbs and the NaN/infinity flags go to the workspace: 25
-//      words per workgroup.
+//   1. Each workgroup (1024 threads) sums its values exactly into
+//      32-bit-limb accumulators of the positive and the negative values
+//      (exact_mean.h): per round of 4 values per lane, each wave adds the
+//      integer significands of the values within 24 binades of its largest
+//      one into 64-bit register sums (shifted to the window's bottom), sums
+//      those across the wave and adds them to the limbs; values further down
+//      go to LDS bins by (sign, exponent), folded into the limbs at the end.
+//      The limbs, carried into 32-bit digits, and the NaN/infinity flags go
+//      to the workspace: 25 32-bit words per workgroup.
 //   2. Every workgroup (1024 threads, at most 512 workgroups) first adds
 //      the records (a half wave per word) and rounds the mean itself (the
-//      records are complete: they come from the previous launch); workgroup
-//      0 stores it.  Then one wave per group of 256 blocks: four blocks per
-//      lane, IEEE division, and the nearest code: a count over 15 map
-//      entries held in registers, a binary search in LDS inside the block
-//      of 16 it picks, and a walk to the lowest index with the same rounded
-//      distance (a full scan if the map is not sorted).
+//      records are complete: they come from the previous launch; the
+//      division by nb is a multiply-high by a constant the host computes);
+//      workgroup 0 stores it.  Then one wave per group of 256 blocks: four
+//      blocks per lane, the group max from the group's value range (taken
+//      while the mean is pending), IEEE division, and the nearest code: a
+//      count over 15 map entries held in registers, a binary search in LDS
+//      inside the block of 16 it picks, and a walk to the lowest index with
+//      the same rounded distance (a full scan if the map is not sorted).
 // The workspace holds only the records (scratch, no initialisation).  A
 // variant keeps it in a static device array instead (one per GPU, for
 // callers that cannot allocate).
@@ -42,11 +44,11 @@
 namespace kbit {
 namespace {
 
-constexpr int kBinThreads = 256;
+constexpr int kBinThreads = 1024;
 constexpr int kBinWaves = kBinThreads / kWave;
 constexpr int kMaxBinGroups = 256;  // workgroups of launch 1 (the workspace holds one record each)
 constexpr int kLimbWords = kWideLimbs + 2;
-constexpr int kRecordWords = 2 * kLimbWords + 1;  // uint64: limbs[sign][i], then the flags
+constexpr int kRecordWords = 2 * kLimbWords + 1;  // uint32: digits[sign][i], then the flags
 constexpr int kEncThreads = 1024;                       // launch 2: one group of 256 blocks per wave
 constexpr int kEncWaves = kEncThreads / kWave;
 constexpr int kEncMaxGrid = 512;                        // each workgroup of launch 2 re-reads the records
@@ -57,9 +59,18 @@ constexpr int kGroup2 = 256;
 constexpr float kEps2 = 1e-8f;
 constexpr uint32_t kFlagNan = 1, kFlagPosInf = 2, kFlagNegInf = 4;
 
+constexpr int kBinVecs = 1;      // 16-byte loads per lane per round (4 values)
+constexpr int kWindowBits = 24;  // binades below the wave's top one that the register sums take
+constexpr int64_t kRoundValues = static_cast<int64_t>(kBinThreads) * kBinVecs * 4;  // per workgroup
+
 int bin_groups(int64_t nb) {
-    const int64_t g = (nb + 4095) / 4096;
+    const int64_t g = (nb + kRoundValues - 1) / kRoundValues;
     return static_cast<int>(g < 1 ? 1 : (g > kMaxBinGroups ? kMaxBinGroups : g));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_i32(int32_t v) {
+    return static_cast<int32_t>(dpp_u32<CTRL>(static_cast<uint32_t>(v)));
 }
 
 template <int CTRL>
@@ -97,23 +108,34 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
-constexpr int kBinVecs = 4;     // 16-byte loads per lane per round (16 values)
-constexpr int kWindowBits = 24;  // binades below the wave's top one that the register sums take
-
-// Launch 1.  Per round a wave holds 16 values per lane.  A finite nonzero
+// Launch 1.  Per round a wave holds 4 values per lane.  A finite nonzero
 // value with biased exponent e and integer significand m is m * 2^(e' - 1)
 // in units of 2^-149, e' = max(e, 1).  With E the wave's largest e' and
 // e0 = max(E - 24, 1), every value with e' >= e0 adds m << (e' - e0) (below
 // 2^48) to the register sum of its sign, in units of 2^(e0 - 1); the wave's
-// two sums (below 2^58) go into the workgroup's limb accumulators once per
-// round.  Values further down (more than 24 binades below the wave's top)
-// add m to a per-wave LDS bin of their sign and e.  NaN and infinities only
-// set flags.
+// two sums (below 2^56) go into the wave's own limb accumulators in LDS
+// once per round, as three pieces below 2^33 (lane 0 alone writes them, so
+// no atomics).  Values further down (more than 24 binades below the wave's
+// top) add m to the workgroup's LDS bin of their sign and e, folded into
+// wave 0's limbs at the end (only if any exist).  NaN and infinities only
+// set flags.  Then wave 0 adds the waves' limbs (lane 12 s + i takes limb i
+// of sign s) and carries them into 32-bit digits.
+//
+// Bounds (nb <= 2^36, at most 2^28 values per workgroup): a wave's limb
+// takes at most one piece per round and sign, so all 16 waves' limbs of
+// one index add up to below 2^20 * 2^33 (2^20 wave rounds of 256 values),
+// plus at most 256 bin pieces; a bin stays below 2^28 * 2^24.  A
+// workgroup's sum is below 2^28 * 2^277, so its carried digits fit the 10
+// low limbs and each is below 2^32; launch 2 adds at most 256 of them per
+// limb.
+//
+// The record is word-major: word k of workgroup b at ws[k * groups + b],
+// so that launch 2 reads each word of all records with contiguous loads.
 __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* __restrict__ a, int64_t nb,
-                                                                  uint64_t* __restrict__ ws) {
-    __shared__ unsigned long long bins[kBinWaves][2][256];
-    __shared__ unsigned long long limbs[2][kLimbWords];
-    __shared__ uint32_t flags;
+                                                                  uint32_t* __restrict__ ws) {
+    __shared__ unsigned long long bins[2][256];
+    __shared__ unsigned long long wlimbs[kBinWaves][2][kLimbWords];
+    __shared__ uint32_t flags, any_slow;
     const int wave = threadIdx.x / kWave;
     const int lane = __lane_id();
     uint32_t my_flags = 0;
@@ -137,15 +159,17 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
         }
     };
     // the first round's loads are in flight while the LDS is cleared
-    int64_t wb = static_cast<int64_t>(blockIdx.x) * kBinThreads + wave * kWave;
+    const int64_t wb0 = static_cast<int64_t>(blockIdx.x) * kBinThreads + wave * kWave;
+    int64_t wb = wb0;
     u32x4 u[kBinVecs];
     load_round(wb, u);
-    for (int i = threadIdx.x; i < kBinWaves * 2 * 256; i += kBinThreads) (&bins[0][0][0])[i] = 0;
-    if (threadIdx.x < 2 * kLimbWords) (&limbs[0][0])[threadIdx.x] = 0;
-    if (threadIdx.x == 0) flags = 0;
+    for (int i = threadIdx.x; i < 2 * 256; i += kBinThreads) (&bins[0][0])[i] = 0;
+    for (int i = threadIdx.x; i < kBinWaves * 2 * kLimbWords; i += kBinThreads) (&wlimbs[0][0][0])[i] = 0;
+    if (threadIdx.x == 0) flags = any_slow = 0;
     __syncthreads();
+    unsigned long long* my_limbs = &wlimbs[wave][0][0];
     for (; wb < nvec_all; wb += kBinVecs * stride) {
-        if (wb != static_cast<int64_t>(blockIdx.x) * kBinThreads + wave * kWave) load_round(wb, u);
+        if (wb != wb0) load_round(wb, u);
         uint32_t top = 0;
 #pragma unroll
         for (int k = 0; k < kBinVecs; ++k) {
@@ -177,6 +201,7 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
             }
         }
         if (slow != 0) {
+            atomicOr(&any_slow, 1u);
 #pragma unroll
             for (int k = 0; k < kBinVecs; ++k) {
 #pragma unroll
@@ -184,7 +209,7 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
                     if (slow & (1u << (4 * k + c))) {
                         const uint32_t x = u[k][c];
                         const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
-                        atomicAdd(&bins[wave][x >> 31][e], static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
+                        atomicAdd(&bins[x >> 31][e], static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
                     }
                 }
             }
@@ -197,45 +222,68 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
                 const uint64_t v = sg ? sum_neg : sum_pos;
                 if (v != 0) {
                     const WidePieces q = wide_pieces(v, static_cast<int>(e0) - 1);
-                    atomicAdd(&limbs[sg][q.w], static_cast<unsigned long long>(q.p0));
-                    atomicAdd(&limbs[sg][q.w + 1], static_cast<unsigned long long>(q.p1));
-                    atomicAdd(&limbs[sg][q.w + 2], static_cast<unsigned long long>(q.p2));
+                    unsigned long long* l = my_limbs + sg * kLimbWords + q.w;
+                    l[0] += q.p0;
+                    l[1] += q.p1;
+                    l[2] += q.p2;
                 }
             }
         }
     }
     if (my_flags) atomicOr(&flags, my_flags);
     __syncthreads();
-    // bins -> limb accumulators
-    for (int i = threadIdx.x; i < 2 * 256; i += kBinThreads) {
-        uint64_t sum = 0;
-#pragma unroll
-        for (int w = 0; w < kBinWaves; ++w) sum += (&bins[w][0][0])[i];
-        const int sg = i >> 8, e = i & 255;
-        if (sum != 0) {
-            const WidePieces q = wide_pieces(sum, (e > 0 ? e : 1) - 1);
-            atomicAdd(&limbs[sg][q.w], static_cast<unsigned long long>(q.p0));
-            atomicAdd(&limbs[sg][q.w + 1], static_cast<unsigned long long>(q.p1));
-            atomicAdd(&limbs[sg][q.w + 2], static_cast<unsigned long long>(q.p2));
+    if (any_slow != 0) {  // workgroup-uniform: bins -> wave 0's limbs
+        for (int i = threadIdx.x; i < 2 * 256; i += kBinThreads) {
+            const uint64_t sum = (&bins[0][0])[i];
+            const int sg = i >> 8, e = i & 255;
+            if (sum != 0) {
+                const WidePieces q = wide_pieces(sum, (e > 0 ? e : 1) - 1);
+                atomicAdd(&wlimbs[0][sg][q.w], static_cast<unsigned long long>(q.p0));
+                atomicAdd(&wlimbs[0][sg][q.w + 1], static_cast<unsigned long long>(q.p1));
+                atomicAdd(&wlimbs[0][sg][q.w + 2], static_cast<unsigned long long>(q.p2));
+            }
         }
+        __syncthreads();
     }
-    __syncthreads();
-    uint64_t* rec = ws + static_cast<int64_t>(blockIdx.x) * kRecordWords;
-    if (threadIdx.x < 2 * kLimbWords) rec[threadIdx.x] = (&limbs[0][0])[threadIdx.x];
-    if (threadIdx.x == 0) rec[2 * kLimbWords] = flags;
+    if (wave == 0) {
+        // lane 12 s + i: limb i of sign s over all waves
+        uint64_t t = 0;
+        if (lane < 2 * kLimbWords) {
+#pragma unroll
+            for (int w = 0; w < kBinWaves; ++w) t += (&wlimbs[w][0][0])[lane];
+        }
+        // carries, in uniform control flow (every lane runs the cross-lane
+        // reads); lane 12 s + i keeps digit i of sign s
+        uint32_t digit = 0;
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            uint64_t c = 0;
+#pragma unroll
+            for (int i = 0; i < kLimbWords; ++i) {
+                const int src = sg * kLimbWords + i;
+                const uint64_t v = ((static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(t >> 32), src)) << 32) |
+                                    readlane_u32(static_cast<uint32_t>(t), src)) + c;
+                digit = lane == src ? static_cast<uint32_t>(v) : digit;
+                c = v >> 32;
+            }
+        }
+        const int64_t groups = gridDim.x;
+        if (lane < 2 * kLimbWords) ws[lane * groups + blockIdx.x] = digit;
+        if (lane == 0) ws[2 * kLimbWords * groups + blockIdx.x] = flags;
+    }
 }
 
 // The records of launch 1 for the mean: half wave h of the workgroup
-// (kOffsetParts = 32 lanes) takes record word h (a limb of one sign, or
-// the flags) of every record, eight per lane; halves past the last word
-// load nothing.
-__device__ __forceinline__ void load_records(const uint64_t* __restrict__ ws, int groups,
+// (kOffsetParts = 32 lanes) takes record word h (a digit of one sign, or
+// the flags) of every record, eight per lane, widened to 64 bits; halves
+// past the last word load nothing.
+__device__ __forceinline__ void load_records(const uint32_t* __restrict__ ws, int groups,
                                              uint64_t (&v)[kOffsetLoads]) {
     const int k = threadIdx.x / kOffsetParts, part = threadIdx.x % kOffsetParts;
 #pragma unroll
     for (int j = 0; j < kOffsetLoads; ++j) {
         const int g = part + j * kOffsetParts;
-        v[j] = (k < kRecordWords && g < groups) ? ws[g * kRecordWords + k] : 0;
+        v[j] = (k < kRecordWords && g < groups) ? ws[static_cast<int64_t>(k) * groups + g] : 0;
     }
 }
 
@@ -246,9 +294,9 @@ __device__ __forceinline__ uint64_t dpp_or_u64(uint64_t v) {
 
 // The mean offset from the loaded records: each half wave sums (ORs, for
 // the flags) its word; thread 0 rounds the mean from the limb totals (each
-// below 2^60).  Every thread gets the offset (through LDS).  All threads of
+// below 2^40).  Every thread gets the offset (through LDS).  All threads of
 // the workgroup call it.
-__device__ inline float mean_offset(const uint64_t (&v)[kOffsetLoads], int64_t nb) {
+__device__ inline float mean_offset(const uint64_t (&v)[kOffsetLoads], const NbDivider& div) {
     __shared__ unsigned long long total[kRecordWords];
     __shared__ float off;
     uint64_t sum = 0, any = 0;
@@ -296,7 +344,7 @@ __device__ inline float mean_offset(const uint64_t (&v)[kOffsetLoads], int64_t n
                 pos[i] = total[i];
                 neg[i] = total[kLimbWords + i];
             }
-            bits = mean_from_limbs(pos, neg, static_cast<uint64_t>(nb));
+            bits = mean_from_limbs(pos, neg, div);
         }
         off = __uint_as_float(bits);
     }
@@ -369,6 +417,44 @@ __device__ __forceinline__ uint32_t nearest_scan256(const float* c, float v) {
     return best;
 }
 
+// Order-preserving integer key of a float (larger value, larger key; -0
+// below +0): the float bits with the magnitude bits flipped for negatives.
+__device__ __forceinline__ int32_t order_key(float x) {
+    const int32_t b = static_cast<int32_t>(__float_as_uint(x));
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float from_order_key(int32_t k) {
+    return __uint_as_float(static_cast<uint32_t>(k ^ ((k >> 31) & 0x7FFFFFFF)));
+}
+
+// Largest and smallest key of a group's values over the wave (every lane
+// active), returned uniform.
+struct GroupRange {
+    int32_t hi, lo;
+};
+__device__ __forceinline__ GroupRange group_range(const float (&x)[4], int64_t b0, int64_t nb) {
+    int32_t hi = INT32_MIN, lo = INT32_MAX;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (b0 + k < nb) {
+            const int32_t key = order_key(x[k]);
+            hi = max(hi, key);
+            lo = min(lo, key);
+        }
+    }
+    hi = max(hi, dpp_i32<kDppXor1>(hi));
+    lo = min(lo, dpp_i32<kDppXor1>(lo));
+    hi = max(hi, dpp_i32<kDppXor2>(hi));
+    lo = min(lo, dpp_i32<kDppXor2>(lo));
+    hi = max(hi, dpp_i32<kDppHalfMirror>(hi));
+    lo = min(lo, dpp_i32<kDppHalfMirror>(lo));
+    hi = max(hi, dpp_i32<kDppMirror>(hi));
+    lo = min(lo, dpp_i32<kDppMirror>(lo));
+    const auto rd = [](int32_t v, int l) { return static_cast<int32_t>(readlane_u32(static_cast<uint32_t>(v), l)); };
+    return GroupRange{max(max(rd(hi, 0), rd(hi, 16)), max(rd(hi, 32), rd(hi, 48))),
+                      min(min(rd(lo, 0), rd(lo, 16)), min(rd(lo, 32), rd(lo, 48)))};
+}
+
 // Four blocks per lane of group g (zeros past nb).
 __device__ __forceinline__ void load_group(const float* __restrict__ a, int64_t nb, int64_t g, bool aligned16,
                                            float (&x)[4]) {
@@ -385,10 +471,10 @@ __device__ __forceinline__ void load_group(const float* __restrict__ a, int64_t 
 
 __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float* __restrict__ a, int64_t nb,
                                                                     const float* __restrict__ qmap2,
-                                                                    const uint64_t* __restrict__ ws, int groups,
+                                                                    const uint32_t* __restrict__ ws, int groups,
                                                                     float* __restrict__ offset_out,
                                                                     uint8_t* __restrict__ code,
-                                                                    float* __restrict__ absmax2) {
+                                                                    float* __restrict__ absmax2, NbDivider div) {
     __shared__ float c[256];
     __shared__ int unsorted;
     uint64_t rec[kOffsetLoads];
@@ -402,8 +488,9 @@ __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float*
         if (threadIdx.x == 0 && qmap2[0] != qmap2[0]) unsorted = 1;
     }
     // One group per wave per pass, groups g, g + step, ...; the first
-    // group's values are loaded before the mean so that both loads overlap,
-    // and each pass loads the next group before working on this one.
+    // group's values are loaded, and their range taken, before the mean, so
+    // that this overlaps the wait for the records and the mean; each pass
+    // loads the next group before working on this one.
     const int lane = __lane_id();
     const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
     const int64_t step = static_cast<int64_t>(gridDim.x) * kEncWaves;
@@ -415,28 +502,26 @@ __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float*
     float sep[15];
 #pragma unroll
     for (int t = 0; t < 15; ++t) sep[t] = qmap2[16 * t + 15];
-    const float offset = mean_offset(rec, nb);  // has barriers: c[] and unsorted are set
+    GroupRange range = group_range(x, g * kGroup2 + lane * 4, nb);
+    const float offset = mean_offset(rec, div);  // has barriers: c[] and unsorted are set
     const bool sorted = unsorted == 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) *offset_out = offset;
     for (; g < ngroups; g += step) {
         float y[4];
         load_group(a, nb, g + step, aligned16, y);  // zeros past the end: no load
         const int64_t b0 = g * kGroup2 + lane * 4;
-        float r[4];
-        float m = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            r[k] = x[k] - offset;
-            if (b0 + k < nb) m = __builtin_elementwise_maximum(m, fabsf(r[k]));
-        }
-        // group max: the bits of non-negative floats (and NaN above them)
-        // order as their values
-        const float amax2 = __uint_as_float(wave_max_u32(__float_as_uint(m)));
+        // Group max of |RN(x - offset)|: RN(x - offset) does not decrease as
+        // x grows, so the max is at the group's largest or smallest value.
+        // A NaN anywhere makes the offset NaN, and then every |r| and this
+        // max are NaN; an infinite offset gives NaN exactly for the groups
+        // that hold the same infinity (inf - inf), as it does per value.
+        const float amax2 = __builtin_elementwise_maximum(fabsf(from_order_key(range.hi) - offset),
+                                                          fabsf(from_order_key(range.lo) - offset));
         if (lane == 0) absmax2[g] = amax2;
         const float s = __builtin_elementwise_maximum(amax2, kEps2);
         float v[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = r[k] / s;
+        for (int k = 0; k < 4; ++k) v[k] = (x[k] - offset) / s;
         uint32_t q[4];
         if (sorted) {
             nearest_sorted4(c, sep, v, q);
@@ -454,26 +539,27 @@ __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float*
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[k] = y[k];
+        range = group_range(x, (g + step) * kGroup2 + lane * 4, nb);
     }
 }
 
 }  // namespace
 
 int64_t nested_workspace_bytes(int64_t nb) {
-    return static_cast<int64_t>(bin_groups(nb)) * kRecordWords * 8;
+    return static_cast<int64_t>(bin_groups(nb)) * kRecordWords * 4;
 }
 
 int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
                          float* offset, void* workspace, void* stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const int groups = bin_groups(nb);
-    uint64_t* ws = static_cast<uint64_t*>(workspace);
+    uint32_t* ws = static_cast<uint32_t*>(workspace);
     hipLaunchKernelGGL(nested_bins_kernel, dim3(groups), dim3(kBinThreads), 0, st, absmax, nb, ws);
     const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
     const int64_t want = (ngroups + kEncWaves - 1) / kEncWaves;
     const int64_t grid = want < kEncMaxGrid ? want : kEncMaxGrid;
     hipLaunchKernelGGL(nested_encode_kernel, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st, absmax, nb,
-                       qmap2, ws, groups, offset, code, absmax2);
+                       qmap2, ws, groups, offset, code, absmax2, make_nb_divider(static_cast<uint64_t>(nb)));
     return static_cast<int>(hipGetLastError());
 }
 
@@ -483,8 +569,8 @@ int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, ui
 // must not pass the array's name to a kernel (it is a host-side stand-in);
 // it uses the device address from hipGetSymbolAddress, looked up once per
 // device.
-constexpr int64_t kScratchBytes = static_cast<int64_t>(kMaxBinGroups) * kRecordWords * 8;
-static __device__ __align__(256) uint64_t scratch[kScratchBytes / 8];
+constexpr int64_t kScratchBytes = static_cast<int64_t>(kMaxBinGroups) * kRecordWords * 4;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
 
 namespace {
 std::atomic<void*> g_scratch[kMaxDevices];

@@ -290,7 +290,7 @@ int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2,
  * allocation, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid it).  The
  * workspace is a static array in this library's device memory, one per
- * GPU, of kbit_nested_noalloc_scratch_bytes() bytes (51,200), held until
+ * GPU, of kbit_nested_noalloc_scratch_bytes() bytes (25,600), held until
  * the process ends; its contents are scratch (nothing to clear between
  * calls).  It covers every nb up to 2^36 (KBIT_EINVAL beyond).
  * All calls on one GPU share that array: calls that overlap on one GPU

@@ -118,7 +118,7 @@ def test_validation_codes_before_any_device_access():
     assert lib.kbit_nested_workspace_bytes(-1) == -1
     assert lib.kbit_nested_workspace_bytes((1 << 36) + 1) == -1
     wsb = lib.kbit_nested_workspace_bytes(1000)
-    assert wsb >= 8 * 25
+    assert wsb >= 4 * 25                                       # one record of 25 32-bit words
     ne = lib.quantize_nested_absmax
     _W8 = ct.c_void_p(0x40000)
     assert ne(None, 0, None, None, None, None, None, 0, None) == 0                   # empty: no-op
