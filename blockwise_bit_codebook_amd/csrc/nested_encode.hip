@@ -68,6 +68,13 @@ int bin_groups(int64_t nb) {
     return static_cast<int>(g < 1 ? 1 : (g > kMaxBinGroups ? kMaxBinGroups : g));
 }
 
+// Lane i of each row of 16 gets lane i - 1's value, lane 0 of a row gets 0
+// (DPP row_shr:1; with bound_ctrl set, a source lane outside the row reads
+// as zero).
+__device__ __forceinline__ uint32_t row_shr1_or_zero(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x111, 0xF, 0xF, true));
+}
+
 template <int CTRL>
 __device__ __forceinline__ int32_t dpp_i32(int32_t v) {
     return static_cast<int32_t>(dpp_u32<CTRL>(static_cast<uint32_t>(v)));
@@ -118,7 +125,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // no atomics).  Values further down (more than 24 binades below the wave's
 // top) add m to the workgroup's LDS bin of their sign and e, folded into
 // wave 0's limbs at the end (only if any exist).  NaN and infinities only
-// set flags.  Then wave 0 adds the waves' limbs (lane 12 s + i takes limb i
+// set flags.  Then wave 0 adds the waves' limbs (lane 16 s + i takes limb i
 // of sign s) and carries them into 32-bit digits.
 //
 // Bounds (nb <= 2^36, at most 2^28 values per workgroup): a wave's limb
@@ -246,29 +253,32 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
         __syncthreads();
     }
     if (wave == 0) {
-        // lane 12 s + i: limb i of sign s over all waves
+        // Lane 16 s + i (i < 12) adds limb i of sign s over all waves
+        // (t < 2^54), then the digits: each limb keeps its low 32 bits plus
+        // the high part of the limb below (one DPP row shift: each sign's
+        // limbs sit in one row of 16 lanes), which leaves sums below 2^33,
+        // i.e. carries of 0 or 1.  Those resolve as in a carry-lookahead
+        // adder: G marks the lanes whose sum reached 2^32, P those whose low
+        // 32 bits are all ones (they pass a carry on), and the carry into
+        // each lane is bit i of ((G | P) + G) ^ (G | P) ^ G.  Limbs 10 and 11
+        // never receive pieces (the top piece lands at limb 9), so no carry
+        // leaves a sign's row.
+        const int sg = lane >> 4, li = lane & 15;
+        const bool mine = lane < 32 && li < kLimbWords;
         uint64_t t = 0;
-        if (lane < 2 * kLimbWords) {
+        if (mine) {
 #pragma unroll
-            for (int w = 0; w < kBinWaves; ++w) t += (&wlimbs[w][0][0])[lane];
+            for (int w = 0; w < kBinWaves; ++w) t += wlimbs[w][sg][li];
         }
-        // carries, in uniform control flow (every lane runs the cross-lane
-        // reads); lane 12 s + i keeps digit i of sign s
-        uint32_t digit = 0;
-#pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-            uint64_t c = 0;
-#pragma unroll
-            for (int i = 0; i < kLimbWords; ++i) {
-                const int src = sg * kLimbWords + i;
-                const uint64_t v = ((static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(t >> 32), src)) << 32) |
-                                    readlane_u32(static_cast<uint32_t>(t), src)) + c;
-                digit = lane == src ? static_cast<uint32_t>(v) : digit;
-                c = v >> 32;
-            }
-        }
+        const uint32_t hi_below = row_shr1_or_zero(static_cast<uint32_t>(t >> 32));
+        const uint64_t sum = (t & 0xFFFFFFFFull) + hi_below;
+        const uint32_t low = static_cast<uint32_t>(sum);
+        const uint64_t G = __ballot(mine && (sum >> 32) != 0);
+        const uint64_t P = __ballot(mine && low == 0xFFFFFFFFu);
+        const uint64_t carries = ((G | P) + G) ^ (G | P) ^ G;
+        const uint32_t digit = low + static_cast<uint32_t>((carries >> lane) & 1ull);
         const int64_t groups = gridDim.x;
-        if (lane < 2 * kLimbWords) ws[lane * groups + blockIdx.x] = digit;
+        if (mine) ws[(sg * kLimbWords + li) * groups + blockIdx.x] = digit;
         if (lane == 0) ws[2 * kLimbWords * groups + blockIdx.x] = flags;
     }
 }
