@@ -389,10 +389,14 @@ def act_bytes(rows=ACT_ROWS, d=ACT_D):
     return 2 * n + d // 8 + 64 + (n // 32) * 4 * 4 + 4 * rows
 
 
-def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, sets=12):
+def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, sets=12, tables=False):
     """Timing of the W4A4 activation assignment on rows x d bf16 (rows
     N(0,1) x 10^U(-1,1), shared sign mask, Lloyd-Max-16 scaled by sqrt(h/d)
-    for d/h Hadamard blocks; with ``perm`` a random column permutation)."""
+    for d/h Hadamard blocks; with ``perm`` a random column permutation).
+    With ``tables`` the calls take the codebook's prepared tables
+    (act_tables_k4, built once before timing) instead of the codebook.
+    Launches go straight to the C entry point with arguments prepared per
+    buffer set, so that Python stays ahead of the GPU."""
     x, signs = synth.activations_bf16(rows, d)
     h = d & -d
     cb = (kb.codebook_lloyd_max_normal(16) * np.float32(np.sqrt(h / d))).astype(np.float32)
@@ -405,22 +409,36 @@ def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, s
     bufs = [(x0 if i == 0 else x0.clone(),
              torch.empty(rows, dtype=torch.float32, device=dev),
              torch.empty(kb.n_words(rows * d, 4), dtype=torch.int32, device=dev)) for i in range(sets)]
+    tab = kb.act_tables_k4(cbl) if tables else None
+    # one call through the wrapper per set (argument checks), then direct calls
+    for b in bufs:
+        kb.quantize_act_fwht_k4_bf16(b[0], sg, None if tables else cbl, row_norm=b[1], packed=b[2], perm=pm,
+                                     tables=tab)
     torch.cuda.synchronize()
-
-    def run(b):
-        kb.quantize_act_fwht_k4_bf16(b[0], sg, cbl, row_norm=b[1], packed=b[2], perm=pm)
-
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    cb_arg = (tab if tables else cbl).data_ptr()
+    name = ("quantize_act_rpbh_k4_bf16" if perm else "quantize_act_fwht_k4_bf16") + ("_tables" if tables else "")
+    fn = getattr(kb.lib(), name)
+    if perm:
+        args = [(b[0].data_ptr(), rows, d, pm.data_ptr(), sg.data_ptr(), cb_arg, b[1].data_ptr(), b[2].data_ptr(),
+                 stream) for b in bufs]
+    else:
+        args = [(b[0].data_ptr(), rows, d, sg.data_ptr(), cb_arg, b[1].data_ptr(), b[2].data_ptr(), stream)
+                for b in bufs]
+    rc = 0
     for _ in range(3):
-        for b in bufs:
-            run(b)
+        for a in args:
+            rc |= fn(*a)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record()
     for r in range(reps):
-        for b in bufs:
-            run(b)
+        for a in args:
+            rc |= fn(*a)
         ev[r + 1].record()
     torch.cuda.synchronize()
+    if rc:
+        raise RuntimeError(f"an activation launch failed: {kb.lib().kbit_strerror(rc)}")
     ts = np.array([ev[r].elapsed_time(ev[r + 1]) / sets for r in range(reps)])
     avg = float(ts.mean())
     nbytes = act_bytes(rows, d) + (4 * d if perm else 0)
@@ -429,7 +447,8 @@ def bench_act(torch, kb, synth, dev, reps, rows=ACT_ROWS, d=ACT_D, perm=False, s
     tflops = flops / (avg * 1e-3) / 1e12
     return {"workload": f"{rows} x {d} bf16 activations, Hadamard blocks of {h}"
                         f"{', column permutation' if perm else ''}, Lloyd-Max-16, K=4 planes, "
-                        f"{sets} rotated buffer sets",
+                        f"{sets} rotated buffer sets"
+                        f"{', prepared codebook tables' if tables else ', tables built per call'}",
             "avg_us": round(avg * 1e3, 3), "median_us": round(float(np.median(ts)) * 1e3, 3),
             "bytes": nbytes, "GB/s": round(gbps, 2), "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
             "algorithmic_flops": flops, "TFLOP/s": round(tflops, 3),
@@ -951,8 +970,12 @@ def main(argv=None):
                 "note": "same buffer set every launch (warm cache); not the headline number"}
         if not args.no_act:
             act = bench_act(torch, kb, synth, dev, reps)
-            act_block = [bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp)
-                         for r, dd, pp in ACT_BLOCK_CASES]
+            act["prepared_tables"] = bench_act(torch, kb, synth, dev, reps, tables=True)
+            act_block = []
+            for r, dd, pp in ACT_BLOCK_CASES:
+                one = bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp)
+                one["prepared_tables"] = bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp, tables=True)
+                act_block.append(one)
         lin = bench_linear(torch, kb, synth, dev)
         sweep = bench_sweep(torch, kb, dev, reps)
         cells = bench_nested_cells(torch, kb, dev, max(4, reps // 2))

@@ -23,7 +23,7 @@ __all__ = [
     "KbitError", "lib", "codebook_nf", "codebook_fp4", "codebook_lloyd_max_normal",
     "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax",
     "quantize_nested_absmax_noalloc", "linear_4bit",
-    "quantize_act_fwht_k4_bf16", "quantize_act_rpbh_k4_bf16", "n_words", "n_blocks",
+    "quantize_act_fwht_k4_bf16", "quantize_act_rpbh_k4_bf16", "act_tables_k4", "n_words", "n_blocks",
 ]
 
 _TORCH_NAME = {"fp32": "float32", "fp16": "float16", "bf16": "bfloat16"}
@@ -340,13 +340,31 @@ def linear_4bit(X, packed, codebook16, N, blocksize, absmax=None, absmax_code=No
     return out
 
 
-def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=None, perm=None):
+def act_tables_k4(codebook16, tables=None):
+    """Prepared assignment tables of a 16-entry codebook (uint8 tensor of
+    kbit_act_tables_bytes() bytes), for ``quantize_act_fwht_k4_bf16(...,
+    tables=...)``: built once instead of by every workgroup of every call."""
+    torch = _torch()
+    _buf(codebook16, "codebook16", torch.float32, 16)
+    nbytes = lib().kbit_act_tables_bytes()
+    if tables is None:
+        tables = torch.empty(nbytes, dtype=torch.uint8, device=codebook16.device)
+    _buf(tables, "tables", torch.uint8, nbytes)
+    _same_device(codebook16, tables=tables)
+    _check("act_tables_k4", lib().act_tables_k4(_ptr(codebook16), _ptr(tables), _stream(codebook16.device)))
+    return tables
+
+
+def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16=None, row_norm=None, packed=None, perm=None, tables=None):
     """Token norm + sign flip + block FWHT (h = largest power of two dividing
     d) + Lloyd-Max assignment of bf16 [rows, d]; with ``perm`` (int32 [d])
-    the columns are permuted first (quantize_act_rpbh_k4_bf16)."""
+    the columns are permuted first (quantize_act_rpbh_k4_bf16).  Give either
+    ``codebook16`` or ``tables`` (from act_tables_k4)."""
     torch = _torch()
     if X.dtype != torch.bfloat16 or X.dim() != 2:
         raise TypeError("X must be a 2-D bfloat16 tensor")
+    if (codebook16 is None) == (tables is None):
+        raise TypeError("give exactly one of codebook16 and tables")
     rows, d = X.shape
     if row_norm is None:
         row_norm = torch.empty(rows, dtype=torch.float32, device=X.device)
@@ -354,27 +372,33 @@ def quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=None, packed=No
         packed = torch.empty(n_words(rows * d, 4), dtype=torch.int32, device=X.device)
     _buf(sign_bits, "sign_bits", sign_bits.dtype if sign_bits.dtype in (torch.int32, torch.uint32) else torch.int32,
          -(-d // 32))
-    _buf(codebook16, "codebook16", torch.float32, 16)
+    if tables is None:
+        _buf(codebook16, "codebook16", torch.float32, 16)
+        cb, suffix = codebook16, ""
+    else:
+        _buf(tables, "tables", torch.uint8, lib().kbit_act_tables_bytes())
+        cb, suffix = tables, "_tables"
     _buf(row_norm, "row_norm", torch.float32, rows)
     _buf(packed, "packed", torch.int32, n_words(rows * d, 4))
-    _same_device(X, sign_bits=sign_bits, codebook16=codebook16, row_norm=row_norm, packed=packed, perm=perm)
+    _same_device(X, sign_bits=sign_bits, codebook16=cb, row_norm=row_norm, packed=packed, perm=perm)
     if perm is None:
-        name = "quantize_act_fwht_k4_bf16"
-        status = lib().quantize_act_fwht_k4_bf16(_ptr(X), rows, d, _ptr(sign_bits), _ptr(codebook16),
-                                                  _ptr(row_norm), _ptr(packed), _stream(X.device))
+        name = "quantize_act_fwht_k4_bf16" + suffix
+        status = getattr(lib(), name)(_ptr(X), rows, d, _ptr(sign_bits), _ptr(cb), _ptr(row_norm), _ptr(packed),
+                                      _stream(X.device))
     else:
         if perm.dtype != torch.int32 or perm.numel() != d:
             raise TypeError("perm must be an int32 tensor of d entries")
-        name = "quantize_act_rpbh_k4_bf16"
-        status = lib().quantize_act_rpbh_k4_bf16(_ptr(X), rows, d, _ptr(perm), _ptr(sign_bits), _ptr(codebook16),
-                                                  _ptr(row_norm), _ptr(packed), _stream(X.device))
+        name = "quantize_act_rpbh_k4_bf16" + suffix
+        status = getattr(lib(), name)(_ptr(X), rows, d, _ptr(perm), _ptr(sign_bits), _ptr(cb), _ptr(row_norm),
+                                      _ptr(packed), _stream(X.device))
     _check(name, status)
     return packed, row_norm
 
 
-def quantize_act_rpbh_k4_bf16(X, perm, sign_bits, codebook16, row_norm=None, packed=None):
+def quantize_act_rpbh_k4_bf16(X, perm, sign_bits, codebook16=None, row_norm=None, packed=None, tables=None):
     """Column permutation, then quantize_act_fwht_k4_bf16's path."""
-    return quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=row_norm, packed=packed, perm=perm)
+    return quantize_act_fwht_k4_bf16(X, sign_bits, codebook16, row_norm=row_norm, packed=packed, perm=perm,
+                                     tables=tables)
 
 
 def _make_named(fn_name, generic, **fixed):

@@ -30,6 +30,10 @@ def _signatures():
         ("kbit_dynamic_map8", [_p]),
         ("quantize_act_fwht_k4_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p]),
         ("quantize_act_rpbh_k4_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p, _p]),
+        ("kbit_act_tables_bytes", []),
+        ("act_tables_k4", [_p, _p, _p]),
+        ("quantize_act_fwht_k4_bf16_tables", [_p, _i64, _i32, _p, _p, _p, _p, _p]),
+        ("quantize_act_rpbh_k4_bf16_tables", [_p, _i64, _i32, _p, _p, _p, _p, _p, _p]),
         ("kbit_nested_workspace_bytes", [_i64]),
         ("linear_kbit_bf16_k4", [_p, _i64, _i32, _p, _p, _p, _i32, _i32, _p, _p]),
         ("linear_4bit_nested_bf16", [_p, _i64, _i32, _p, _p, _p, _p, _p, _f32, _i32, _i32, _p, _p]),
@@ -62,7 +66,8 @@ def load(path=LIB_PATH):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = {"kbit_strerror": ct.c_char_p, "kbit_nested_workspace_bytes": ct.c_int64,
-                      "kbit_nested_noalloc_scratch_bytes": ct.c_int64}.get(name, ct.c_int)
+                      "kbit_nested_noalloc_scratch_bytes": ct.c_int64,
+                      "kbit_act_tables_bytes": ct.c_int64}.get(name, ct.c_int)
     return lib
 
 

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
                                                                 const uint32_t* __restrict__ sign_bits,
                                                                 const int32_t* __restrict__ perm,
                                                                 const float* __restrict__ cb,
+                                                                const u32x4* __restrict__ prep,
                                                                 float* __restrict__ row_norm,
                                                                 uint32_t* __restrict__ packed, int slots) {
     constexpr int kH = 1 << L;
@@ -146,7 +147,14 @@ __global__ __launch_bounds__(kMaxThreads) void act_block_kernel(const uint16_t* 
     uint16_t* raw = reinterpret_cast<uint16_t*>(slot_lds + row_buffer_floats(d) * 4);  // permutation only
     float* cs = chunk_sum[slot];
 
-    const ActPlan plan = build_act_tables(T, cb, nthreads);
+    // the codebook's tables: built here, or copied from the prepared form
+    ActPlan plan;
+    if (prep != nullptr) {  // uniform
+        plan = load_act_tables(T, prep, nthreads);
+        __syncthreads();
+    } else {
+        plan = build_act_tables(T, cb, nthreads);
+    }
 
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * slots; base < rows;
          base += static_cast<int64_t>(gridDim.x) * slots) {
@@ -262,7 +270,7 @@ constexpr int kLdsBudget = 160 * 1024;
 
 template <int L, bool kPerm>
 int launch_block_t(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits, const int32_t* perm,
-                   const float* cb, float* row_norm, uint32_t* packed, void* stream) {
+                   const float* cb, const u32x4* prep, float* row_norm, uint32_t* packed, void* stream) {
     auto kern = act_block_kernel<L, kPerm>;
     // Allow the largest dynamic LDS any d needs (once per kernel; HIP on
     // gfx950 accepts it, and a refusal would show at the launch).
@@ -286,21 +294,21 @@ int launch_block_t(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(threads), dyn, static_cast<hipStream_t>(stream),
-                       X, rows, d, sign_bits, perm, cb, row_norm, packed, slots);
+                       X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, slots);
     return static_cast<int>(hipGetLastError());
 }
 
 template <bool kPerm>
 int launch_block(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits, const int32_t* perm,
-                 const float* cb, float* row_norm, uint32_t* packed, void* stream) {
+                 const float* cb, const u32x4* prep, float* row_norm, uint32_t* packed, void* stream) {
     switch (__builtin_ctz(static_cast<unsigned>(d))) {
-        case 8: return launch_block_t<8, kPerm>(X, rows, d, sign_bits, perm, cb, row_norm, packed, stream);
-        case 9: return launch_block_t<9, kPerm>(X, rows, d, sign_bits, perm, cb, row_norm, packed, stream);
-        case 10: return launch_block_t<10, kPerm>(X, rows, d, sign_bits, perm, cb, row_norm, packed, stream);
-        case 11: return launch_block_t<11, kPerm>(X, rows, d, sign_bits, perm, cb, row_norm, packed, stream);
-        case 12: return launch_block_t<12, kPerm>(X, rows, d, sign_bits, perm, cb, row_norm, packed, stream);
-        case 13: return launch_block_t<13, kPerm>(X, rows, d, sign_bits, perm, cb, row_norm, packed, stream);
-        case 14: return launch_block_t<14, kPerm>(X, rows, d, sign_bits, perm, cb, row_norm, packed, stream);
+        case 8: return launch_block_t<8, kPerm>(X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, stream);
+        case 9: return launch_block_t<9, kPerm>(X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, stream);
+        case 10: return launch_block_t<10, kPerm>(X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, stream);
+        case 11: return launch_block_t<11, kPerm>(X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, stream);
+        case 12: return launch_block_t<12, kPerm>(X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, stream);
+        case 13: return launch_block_t<13, kPerm>(X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, stream);
+        case 14: return launch_block_t<14, kPerm>(X, rows, d, sign_bits, perm, cb, prep, row_norm, packed, stream);
         default: return static_cast<int>(hipErrorInvalidValue);
     }
 }
@@ -310,10 +318,12 @@ int launch_block(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bi
 bool act_block_supported(int d) { return d >= 256 && d <= kMaxD && d % 256 == 0; }
 
 int launch_act_block(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits, const int32_t* perm,
-                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream) {
+                     const float* codebook16, const void* tables, float* row_norm, uint32_t* packed,
+                     void* stream) {
     if (!act_block_supported(d)) return static_cast<int>(hipErrorInvalidValue);
-    if (perm) return launch_block<true>(X, rows, d, sign_bits, perm, codebook16, row_norm, packed, stream);
-    return launch_block<false>(X, rows, d, sign_bits, nullptr, codebook16, row_norm, packed, stream);
+    const u32x4* prep = static_cast<const u32x4*>(tables);
+    if (perm) return launch_block<true>(X, rows, d, sign_bits, perm, codebook16, prep, row_norm, packed, stream);
+    return launch_block<false>(X, rows, d, sign_bits, nullptr, codebook16, prep, row_norm, packed, stream);
 }
 
 }  // namespace kbit

@@ -171,6 +171,34 @@ __device__ __forceinline__ ActPlan build_act_tables(ActTables& T, const float* _
     return plan;
 }
 
+// The tables in a form built once per codebook (act_tables_kernel) and
+// loaded by every workgroup instead of its own build: the 128 bucket
+// entries, then {fast, slope bits, 0, 0}, then the codebook as 4 vectors.
+constexpr int kActPrepEntries = kBuckets + 1 + 4;  // u32x4 each: 2,128 bytes
+
+// Writes the prepared form of T (built with plan) to out; threads of one
+// workgroup, after the build's last barrier.
+__device__ __forceinline__ void store_act_tables(const ActTables& T, const ActPlan& plan, u32x4* __restrict__ out,
+                                                 int nthreads) {
+    for (int i = threadIdx.x; i < kBuckets; i += nthreads) out[i] = T.master[i];
+    if (threadIdx.x == 0) out[kBuckets] = u32x4{plan.fast ? 1u : 0u, __float_as_uint(plan.slope), 0u, 0u};
+    if (threadIdx.x < 4) {
+        const int i = 4 * threadIdx.x;
+        out[kBuckets + 1 + threadIdx.x] = u32x4{__float_as_uint(T.code[i]), __float_as_uint(T.code[i + 1]),
+                                                __float_as_uint(T.code[i + 2]), __float_as_uint(T.code[i + 3])};
+    }
+}
+
+// Fills T's bank-spread rows and codebook from the prepared form and
+// returns the plan.  Every thread of the workgroup calls it; a workgroup
+// barrier must separate it from the first use of T.
+__device__ __forceinline__ ActPlan load_act_tables(ActTables& T, const u32x4* __restrict__ prep, int nthreads) {
+    for (int i = threadIdx.x; i < kBuckets * kCopies; i += nthreads) T.row[i] = prep[i / kCopies];
+    if (threadIdx.x < 16) T.code[threadIdx.x] = __uint_as_float(prep[kBuckets + 1 + threadIdx.x / 4][threadIdx.x % 4]);
+    const u32x4 pl = prep[kBuckets];
+    return ActPlan{pl[0] != 0u, __uint_as_float(pl[1])};
+}
+
 // Indices of the 16 transformed values v of a row with norm `norm`, as two
 // plane accumulators: bit k of byte j of acc[h] is plane j of element
 // 8h + k.  Every lane of the wave must work on the same row (the finite-norm

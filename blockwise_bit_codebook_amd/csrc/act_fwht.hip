@@ -55,7 +55,8 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
                                                                const uint32_t* __restrict__ sign_bits,
                                                                const float* __restrict__ cb,
                                                                float* __restrict__ row_norm,
-                                                               uint32_t* __restrict__ packed) {
+                                                               uint32_t* __restrict__ packed,
+                                                               const u32x4* __restrict__ prep) {
     constexpr int kActThreads = kRowThreads * kSlots;
     __shared__ ActTables T;
     __shared__ alignas(16) float buf[kSlots][kBufFloats];
@@ -85,10 +86,13 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     // The table build (once per workgroup) runs in the first iteration, its
     // three stages between the butterfly passes, so that it shares their
     // barriers and overlaps their work.  Every workgroup has at least one
-    // row (the grid is at most ceil(rows / kSlots)).
+    // row (the grid is at most ceil(rows / kSlots)).  With prepared tables
+    // (prep, built once per codebook) the workgroup copies them instead; the
+    // loop's barriers come before their first use.
     ActBuild tb;
     ActPlan plan{false, 0.0f};
-    bool first = true;  // uniform
+    bool first = prep == nullptr;  // uniform
+    if (prep != nullptr) plan = load_act_tables(T, prep, kActThreads);
 
     // Sign flips as XOR masks on the raw bf16 words: element 2i is the low
     // half of word i (sign bit 15), element 2i+1 the high half (bit 31).
@@ -193,9 +197,17 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
     }
 }
 
+// The prepared tables of a codebook: one workgroup builds them as the
+// activation kernels do and stores them (store_act_tables).
+__global__ __launch_bounds__(512) void act_tables_kernel(const float* __restrict__ cb, u32x4* __restrict__ out) {
+    __shared__ ActTables T;
+    const ActPlan plan = build_act_tables(T, cb, 512);
+    store_act_tables(T, plan, out, 512);
+}
+
 template <int kSlots>
 int launch_act_slots(const uint16_t* X, int64_t rows, const uint32_t* sign_bits, const float* codebook16,
-                     float* row_norm, uint32_t* packed, void* stream) {
+                     const u32x4* prep, float* row_norm, uint32_t* packed, void* stream) {
     constexpr int kActThreads = kRowThreads * kSlots;
     auto kern = act_fwht_kernel<kSlots>;
     static std::atomic<int> occupancy[kMaxDevices];
@@ -205,16 +217,25 @@ int launch_act_slots(const uint16_t* X, int64_t rows, const uint32_t* sign_bits,
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kActThreads), 0,
-                       static_cast<hipStream_t>(stream), X, rows, sign_bits, codebook16, row_norm, packed);
+                       static_cast<hipStream_t>(stream), X, rows, sign_bits, codebook16, row_norm, packed, prep);
     return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace
 
 int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
-                    const float* codebook16, float* row_norm, uint32_t* packed, void* stream) {
+                    const float* codebook16, const void* tables, float* row_norm, uint32_t* packed, void* stream) {
     (void)d;
-    return launch_act_slots<kSlotsDefault>(X, rows, sign_bits, codebook16, row_norm, packed, stream);
+    return launch_act_slots<kSlotsDefault>(X, rows, sign_bits, codebook16, static_cast<const u32x4*>(tables),
+                                           row_norm, packed, stream);
+}
+
+int64_t act_tables_bytes() { return static_cast<int64_t>(act::kActPrepEntries) * 16; }
+
+int launch_act_tables(const float* codebook16, void* tables, void* stream) {
+    hipLaunchKernelGGL(act_tables_kernel, dim3(1), dim3(512), 0, static_cast<hipStream_t>(stream), codebook16,
+                       static_cast<u32x4*>(tables));
+    return static_cast<int>(hipGetLastError());
 }
 
 }  // namespace kbit

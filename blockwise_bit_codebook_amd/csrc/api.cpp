@@ -306,9 +306,10 @@ int quantize_act_fwht_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const 
     const int c = kbit::check_act(X, rows, d, sign_bits, nullptr, codebook16, row_norm, packed);
     if (c != 1) return c;
     if (d == 4096)
-        return kbit::map_launch(kbit::launch_act_fwht(X, rows, d, sign_bits, codebook16, row_norm, packed, stream));
+        return kbit::map_launch(
+            kbit::launch_act_fwht(X, rows, d, sign_bits, codebook16, nullptr, row_norm, packed, stream));
     return kbit::map_launch(
-        kbit::launch_act_block(X, rows, d, sign_bits, nullptr, codebook16, row_norm, packed, stream));
+        kbit::launch_act_block(X, rows, d, sign_bits, nullptr, codebook16, nullptr, row_norm, packed, stream));
 }
 
 int quantize_act_rpbh_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const int32_t* perm,
@@ -318,7 +319,40 @@ int quantize_act_rpbh_k4_bf16(const uint16_t* X, int64_t rows, int32_t d, const 
     const int c = kbit::check_act(X, rows, d, sign_bits, perm, codebook16, row_norm, packed);
     if (c != 1) return c;
     return kbit::map_launch(
-        kbit::launch_act_block(X, rows, d, sign_bits, perm, codebook16, row_norm, packed, stream));
+        kbit::launch_act_block(X, rows, d, sign_bits, perm, codebook16, nullptr, row_norm, packed, stream));
+}
+
+int64_t kbit_act_tables_bytes(void) { return kbit::act_tables_bytes(); }
+
+int act_tables_k4(const float* codebook16, void* tables, void* stream) {
+    if (!codebook16 || !tables) return KBIT_EINVAL;
+    if (!kbit::aligned(codebook16, 4) || !kbit::aligned(tables, 16)) return KBIT_EALIGN;
+    if (kbit::current_device_cus() <= 0) return KBIT_EDEVICE;
+    return kbit::map_launch(kbit::launch_act_tables(codebook16, tables, stream));
+}
+
+int quantize_act_fwht_k4_bf16_tables(const uint16_t* X, int64_t rows, int32_t d, const uint32_t* sign_bits,
+                                     const void* tables, float* row_norm, uint32_t* packed, void* stream) {
+    if (rows > 0 && tables && !kbit::aligned(tables, 16)) return KBIT_EALIGN;
+    const float* t = static_cast<const float*>(tables);  // checked like a codebook (non-null)
+    const int c = kbit::check_act(X, rows, d, sign_bits, nullptr, t, row_norm, packed);
+    if (c != 1) return c;
+    if (d == 4096)
+        return kbit::map_launch(kbit::launch_act_fwht(X, rows, d, sign_bits, nullptr, tables, row_norm, packed, stream));
+    return kbit::map_launch(
+        kbit::launch_act_block(X, rows, d, sign_bits, nullptr, nullptr, tables, row_norm, packed, stream));
+}
+
+int quantize_act_rpbh_k4_bf16_tables(const uint16_t* X, int64_t rows, int32_t d, const int32_t* perm,
+                                     const uint32_t* sign_bits, const void* tables, float* row_norm,
+                                     uint32_t* packed, void* stream) {
+    if (!perm && rows > 0) return KBIT_EINVAL;
+    if (rows > 0 && tables && !kbit::aligned(tables, 16)) return KBIT_EALIGN;
+    const float* t = static_cast<const float*>(tables);
+    const int c = kbit::check_act(X, rows, d, sign_bits, perm, t, row_norm, packed);
+    if (c != 1) return c;
+    return kbit::map_launch(
+        kbit::launch_act_block(X, rows, d, sign_bits, perm, nullptr, tables, row_norm, packed, stream));
 }
 
 }  // extern "C"

@@ -42,12 +42,18 @@ int launch_linear4_nested(const uint16_t* X, int64_t M, int K, const uint32_t* p
                           const uint8_t* code, const float* qmap2, const float* absmax2, float offset,
                           const float* offset_ptr, int N, int log2B, uint16_t* out, void* stream);
 
+// tables: null (each workgroup builds the codebook's tables) or the
+// prepared tables of launch_act_tables (codebook16 is then unused).
 int launch_act_fwht(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits,
-                    const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
+                    const float* codebook16, const void* tables, float* row_norm, uint32_t* packed, void* stream);
 // Any d with act_block_supported(d); perm may be null (identity).
 bool act_block_supported(int d);
 int launch_act_block(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits, const int32_t* perm,
-                     const float* codebook16, float* row_norm, uint32_t* packed, void* stream);
+                     const float* codebook16, const void* tables, float* row_norm, uint32_t* packed,
+                     void* stream);
+// The prepared tables of a 16-entry codebook (act_tables_bytes() bytes).
+int64_t act_tables_bytes();
+int launch_act_tables(const float* codebook16, void* tables, void* stream);
 
 // CU count of the current device (at least 1).
 int device_cu_count();

@@ -350,6 +350,29 @@ int quantize_act_rpbh_k4_bf16(const uint16_t* X, int64_t rows, int32_t d,
                               const float* codebook16, float* row_norm,
                               uint32_t* packed, void* stream);
 
+/* Prepared tables of a codebook for the two calls above.  The assignment's
+ * switching-point tables depend only on codebook16; without them every
+ * workgroup of every call builds them again (about 2.6 us per call at
+ * 4096 x 4096).  act_tables_k4 builds them once, on the stream, into
+ * `tables` (device, kbit_act_tables_bytes() bytes, 16-byte aligned, owned
+ * by the caller; its contents are opaque and hold a copy of the codebook).
+ * The _tables variants then take them in place of codebook16 and give
+ * results identical to the plain calls with that codebook (the same
+ * definition, [ORBIT] README W4A4 fast path).  Tables must come from
+ * act_tables_k4 of this library; a buffer rebuilt for another codebook
+ * changes the results of later calls, not of calls already ordered
+ * before the rebuild on the stream.  Other arguments and errors as the
+ * plain calls (KBIT_EALIGN also for tables not 16-byte aligned). */
+int64_t kbit_act_tables_bytes(void);
+int act_tables_k4(const float* codebook16, void* tables, void* stream);
+int quantize_act_fwht_k4_bf16_tables(const uint16_t* X, int64_t rows, int32_t d,
+                                     const uint32_t* sign_bits, const void* tables,
+                                     float* row_norm, uint32_t* packed, void* stream);
+int quantize_act_rpbh_k4_bf16_tables(const uint16_t* X, int64_t rows, int32_t d,
+                                     const int32_t* perm, const uint32_t* sign_bits,
+                                     const void* tables, float* row_norm,
+                                     uint32_t* packed, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

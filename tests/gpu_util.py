@@ -59,6 +59,20 @@ def case(msg):
     print(f"[case] {msg}", file=sys.stderr, flush=True)
 
 
+def assert_f32_bits_equal_nan_as_nan(got, want, what):
+    """fp32 bit patterns equal, except that a NaN matches any NaN: IEEE
+    754 leaves the sign and payload of a NaN result open when NaN operands
+    meet, and the pages do not fix them; the NaN positions must match."""
+    got = np.asarray(got, np.uint32)
+    want = np.asarray(want, np.uint32)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    gnan = ((got & 0x7F800000) == 0x7F800000) & ((got & 0x7FFFFF) != 0)
+    wnan = ((want & 0x7F800000) == 0x7F800000) & ((want & 0x7FFFFF) != 0)
+    bad = np.flatnonzero(gnan != wnan)
+    assert bad.size == 0, f"{what}: NaN at {bad[:5].tolist()} on one side only"
+    assert_bits_equal(np.where(gnan, 0, got), np.where(wnan, 0, want), what)
+
+
 def assert_bits_equal(got, want, what):
     got = np.asarray(got)
     want = np.asarray(want)

@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 24 + 3 + 3 + 2 + 2 + 2 + 2 + 1, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 3 + 2 + 2 + 2 + 2 + 1 + 4, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -161,3 +161,17 @@ def test_validation_codes_before_any_device_access():
     assert rp(_A16, 4, 3900, _A16, _A16, _A16, _A16, _A16, None) == -1   # d
     assert rp(_A16, 4, 3840, _A4, _A16, _A16, _A16, _A16, None) == -3    # perm not 16-byte aligned
     assert rp(None, 0, 3840, None, None, None, None, None, None) == 0     # rows = 0: no-op
+    assert lib.kbit_act_tables_bytes() == 133 * 16
+    tb = lib.act_tables_k4
+    assert tb(None, _A16, None) == -1                                    # no codebook
+    assert tb(_A16, None, None) == -1                                    # no tables
+    assert tb(_A16, _A4, None) == -3                                     # tables not 16-byte aligned
+    at = lib.quantize_act_fwht_k4_bf16_tables
+    assert at(_A16, 4, 4096, _A16, None, _A16, _A16, None) == -1         # no tables
+    assert at(_A16, 4, 4096, _A16, _A4, _A16, _A16, None) == -3          # tables misaligned
+    assert at(_A16, 4, 2000, _A16, _A16, _A16, _A16, None) == -1         # d
+    assert at(None, 0, 4096, None, None, None, None, None) == 0
+    rt = lib.quantize_act_rpbh_k4_bf16_tables
+    assert rt(_A16, 4, 3840, None, _A16, _A16, _A16, _A16, None) == -1   # no permutation
+    assert rt(_A16, 4, 3840, _A16, _A16, _A4, _A16, _A16, None) == -3    # tables misaligned
+    assert rt(None, 0, 3840, None, None, None, None, None, None) == 0

@@ -116,3 +116,17 @@ def test_activation_path():
     bad(ValueError, "row_norm", kb.quantize_act_fwht_k4_bf16, X, z(d // 32, i32), z(16, f32), row_norm=z(3, f32))
     bad(ValueError, "packed", kb.quantize_act_fwht_k4_bf16, X, z(d // 32, i32), z(16, f32), packed=z(10, i32))
     bad(TypeError, "perm", kb.quantize_act_rpbh_k4_bf16, X, z(d, torch.int64), z(d // 32, i32), z(16, f32))
+
+
+def test_activation_prepared_tables():
+    rows, d = 4, 512
+    X = z(rows * d, bf16).view(rows, d)
+    tb = kb.lib().kbit_act_tables_bytes()
+    placement_only(kb.quantize_act_fwht_k4_bf16, X, z(d // 32, i32), tables=z(tb, u8))
+    placement_only(kb.act_tables_k4, z(16, f32))
+    bad(ValueError, "tables", kb.quantize_act_fwht_k4_bf16, X, z(d // 32, i32), tables=z(tb - 1, u8))
+    bad(TypeError, "tables", kb.quantize_act_fwht_k4_bf16, X, z(d // 32, i32), tables=z(tb, f32))
+    bad(TypeError, "exactly one", kb.quantize_act_fwht_k4_bf16, X, z(d // 32, i32))
+    bad(TypeError, "exactly one", kb.quantize_act_fwht_k4_bf16, X, z(d // 32, i32), z(16, f32), tables=z(tb, u8))
+    bad(ValueError, "codebook16", kb.act_tables_k4, z(15, f32))
+    bad(ValueError, "tables", kb.act_tables_k4, z(16, f32), tables=z(tb - 1, u8))
