@@ -529,7 +529,10 @@ def bench_nested_cells(torch, kb, dev, reps, sets=4):
 def bench_sweep(torch, kb, dev, reps, sets=4):
     """Quantize and plain dequantize of the 8192 x 8192 N(0, 0.02) weight for
     every input type and K = 2..5 (NF_K codebook, blocksize 64), each pair in
-    round robin over rotated buffer sets."""
+    round robin over rotated buffer sets.  After one call through each
+    wrapper (argument checks), the launches go straight to the C entry
+    points with arguments prepared per buffer set: a wrapper call costs
+    Python time of the order of a launch, which would starve the GPU."""
     n = ROWS * COLS
     nb = n // BLOCK
     tdt = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
@@ -544,11 +547,26 @@ def bench_sweep(torch, kb, dev, reps, sets=4):
             cbk = torch.from_numpy(kb.codebook_nf(Kk)).to(dev)
             packed = [torch.empty(kb.n_words(n, Kk), dtype=torch.int32, device=dev) for _ in range(sets)]
 
-            def q(i):
+            for i in range(sets):
                 kb.quantize_kbit(bufs[i][0], cbk, Kk, BLOCK, absmax=bufs[i][1], packed=packed[i])
+                kb.dequantize_kbit(packed[i], cbk, bufs[i][1], Kk, n, dt, BLOCK, out=bufs[i][2])
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream(dev).cuda_stream
+            qf = getattr(kb.lib(), f"quantize_kbit_{name}_k{Kk}")
+            df = getattr(kb.lib(), f"dequantize_kbit_{name}_k{Kk}")
+            qa = [(cbk.data_ptr(), bufs[i][0].data_ptr(), bufs[i][1].data_ptr(), packed[i].data_ptr(), n, BLOCK,
+                   stream) for i in range(sets)]
+            da = [(packed[i].data_ptr(), cbk.data_ptr(), bufs[i][1].data_ptr(), bufs[i][2].data_ptr(), n, BLOCK,
+                   stream) for i in range(sets)]
+            rc = 0
+
+            def q(i):
+                nonlocal rc
+                rc |= qf(*qa[i])
 
             def d(i):
-                kb.dequantize_kbit(packed[i], cbk, bufs[i][1], Kk, n, dt, BLOCK, out=bufs[i][2])
+                nonlocal rc
+                rc |= df(*da[i])
 
             for _ in range(3):
                 for i in range(sets):
@@ -566,6 +584,8 @@ def bench_sweep(torch, kb, dev, reps, sets=4):
                     d(i)
                 ev[r][2].record()
             torch.cuda.synchronize()
+            if rc:
+                raise RuntimeError(f"a sweep launch failed: {kb.lib().kbit_strerror(rc)}")
             tq = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / sets * 1e3
             td = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) / sets * 1e3
             bq = esz[name] * n + 4 * (n // 32) * Kk + 4 * nb + 4 * (1 << Kk)
@@ -840,6 +860,12 @@ def main(argv=None):
         kb.dequantize_4bit_nested(s["packed"], cb, s["code"], qmap, s["absmax2"], offset, n,
                                   torch.bfloat16, BLOCK, out=s["out"])
 
+    # The side kernels through their wrappers.  Their Python cost (a few
+    # microseconds) is far below every side kernel's duration, and the small
+    # gaps keep these measurements from the power limiting that long runs of
+    # gap-free launches of the VALU-heavy quantize show (measured: FP4
+    # quantize 31-44 us, average 36.4, with direct calls after the other
+    # side kernels, against 29.7-31.0 with the wrappers).
     def quant_only(s):
         kb.quantize_kbit(s["A"], cb, K, BLOCK, absmax=s["absmax"], packed=s["packed"])
 
@@ -863,36 +889,6 @@ def main(argv=None):
     for s_ in sets:                              # eager once per set: per-device setup happens here
         step(s_)
     torch.cuda.synchronize()
-
-    # The two step kernels through their C entry points, with arguments
-    # prepared once per buffer set: the same calls quant_only and
-    # nested_only make, without the wrappers' per-call checks, so that
-    # Python stays well ahead of the GPU.
-    stream_ptr = torch.cuda.current_stream(dev).cuda_stream
-    qfn, dfn = kb.lib().quantize_kbit_bf16_k4, kb.lib().dequantize_4bit_nested_bf16
-    qargs = [(cb.data_ptr(), s_["A"].data_ptr(), s_["absmax"].data_ptr(), s_["packed"].data_ptr(), n, BLOCK,
-              stream_ptr) for s_ in sets]
-    dargs = [(s_["packed"].data_ptr(), cb.data_ptr(), s_["code"].data_ptr(), qmap.data_ptr(),
-              s_["absmax2"].data_ptr(), float(offset), s_["out"].data_ptr(), n, BLOCK, stream_ptr) for s_ in sets]
-
-    def settle():
-        # Steps back to back for at least --settle-ms (chunks of 16 with a
-        # sync after each), so that what follows starts at the GPU's
-        # sustained clocks however short --warmup is.
-        t_end = time.perf_counter() + args.settle_ms * 1e-3
-        i = rc_ = 0
-        while True:
-            for _ in range(16):
-                j = i % args.sets
-                rc_ |= qfn(*qargs[j])
-                rc_ |= dfn(*dargs[j])
-                i += 1
-            torch.cuda.synchronize()
-            if time.perf_counter() >= t_end:
-                break
-        if rc_:
-            raise RuntimeError(f"a settle launch failed: {kb.lib().kbit_strerror(rc_)}")
-
 
     # Side kernels: per-kernel launch time from events on the same stream, in
     # round robin: each round launches every kernel once per buffer set, with
