@@ -83,6 +83,40 @@ def test_other_maps():
     check(a, np.linspace(-1, 1, 256).astype(np.float32), "linear map")
 
 
+def _bucket_edge_values():
+    # floats on and next to the starts of the code search's key buckets
+    # (keys of [-1, 1] in steps of 2^18 of the order key), both signs
+    k = np.arange(0, 0x3F800000, 1 << 18, dtype=np.int64)[::80]
+    bits = np.concatenate([k, k + 1, np.maximum(k - 1, 0)]).astype(np.uint32)
+    pos = bits.view(np.float32)
+    return np.concatenate([pos, -pos]).astype(np.float32)
+
+
+@pytest.mark.parametrize("name", ["dense", "wide", "signed zeros", "tiny", "edges"])
+def test_sorted_maps_for_the_bucket_table(name):
+    # sorted maps that stress the search's bucket table: many entries in one
+    # bucket (the walk), entries outside [-1, 1] (counted everywhere or
+    # nowhere), -0 before +0, subnormal entries, map entries on bucket edges
+    rng = np.random.default_rng(77)
+    q = codebooks.dynamic_map8()
+    if name == "dense":
+        q = np.sort(np.float32(0.3) + np.float32(2.0 ** -20) * np.arange(256, dtype=np.float32)).astype(np.float32)
+    elif name == "wide":
+        q = np.linspace(-4, 4, 256).astype(np.float32)
+    elif name == "signed zeros":
+        q = np.sort(rng.uniform(-1, 1, 256)).astype(np.float32)
+        q[127], q[128] = np.float32(-0.0), np.float32(0.0)
+    elif name == "tiny":
+        q = np.sort(np.concatenate([rng.uniform(-1, 1, 200), np.float32(1e-42) * np.arange(-28, 28)])).astype(np.float32)
+    else:
+        e = _bucket_edge_values()
+        q = np.sort(rng.choice(e, 256, replace=False)).astype(np.float32)
+    # signed values around a mean, so that r / absmax2 spans [-1, 1]
+    a = synth.normal(5000, seed=78, dtype="fp32", sigma=0.05).astype(np.float32)
+    a[:64] = np.float32(a.mean())
+    check(a, q, f"bucket table, {name} map")
+
+
 @pytest.mark.parametrize("shape", ["wide11008", "tall11008", "square8192"])
 def test_chain_quantize_encode_nested_dequantize(shape):
     # bf16 weight of each shape plus a 192-element tail, B = 64: quantize,
