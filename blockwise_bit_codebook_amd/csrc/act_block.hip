@@ -42,6 +42,8 @@
 #include "kbit_internal.h"
 #include "launch.h"
 
+#include <atomic>
+
 namespace kbit {
 namespace {
 
@@ -272,12 +274,16 @@ template <int L, bool kPerm>
 int launch_block_t(const uint16_t* X, int64_t rows, int d, const uint32_t* sign_bits, const int32_t* perm,
                    const float* cb, const u32x4* prep, float* row_norm, uint32_t* packed, void* stream) {
     auto kern = act_block_kernel<L, kPerm>;
-    // Allow the largest dynamic LDS any d needs (once per kernel; HIP on
-    // gfx950 accepts it, and a refusal would show at the launch).
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       kLdsBudget - kStaticLds);
-    (void)attr;
+    // Allow the largest dynamic LDS any d needs, once per kernel and device
+    // (HIP on gfx950 accepts it, and a refusal would show at the launch).
+    // Concurrent first calls may both set it; the call is idempotent.
+    static std::atomic<int> lds_set[kMaxDevices];
+    const int dev = current_device_index();
+    if (dev >= 0 && dev < kMaxDevices && lds_set[dev].load(std::memory_order_acquire) == 0) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kLdsBudget - kStaticLds);
+        lds_set[dev].store(1, std::memory_order_release);
+    }
     const int row_bytes = row_lds_bytes(d, kPerm);
     int slots = (kLdsBudget - kStaticLds - 1024) / row_bytes;
     if (slots > kMaxSlots) slots = kMaxSlots;
