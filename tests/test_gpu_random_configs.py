@@ -124,6 +124,20 @@ def test_random_config_activation(seed):
     check_act(x, s, cb, f"random seed={seed} scale={scale:.3g}", perm=perm)
 
 
+@pytest.mark.parametrize("seed", range(3100, 3116))
+def test_random_config_activation_prepared_tables(seed):
+    # the same draw, through the codebook's prepared tables
+    from tests.test_gpu_act_tables import check
+    rng = np.random.default_rng(seed)
+    d = 256 * int(rng.integers(1, 65))
+    rows = int(rng.integers(1, 48))
+    scale = float(2.0 ** rng.uniform(-6, 3))
+    cb = (codebooks.lloyd_max_normal(16) * np.float32(scale)).astype(np.float32)
+    x, s = synth.activations_bf16(tokens=rows, d=d, seed=seed)
+    perm = rng.permutation(d) if rng.integers(2) else None
+    check(x, s, cb, f"random seed={seed} scale={scale:.3g}", perm=perm)
+
+
 @pytest.mark.parametrize("seed", range(4000, 4024))
 def test_random_config_linear(seed):
     # random M, N, K (a multiple of 32) and blocksize; the fp32-sum bound of
