@@ -861,11 +861,11 @@ def main(argv=None):
                                   torch.bfloat16, BLOCK, out=s["out"])
 
     # The side kernels through their wrappers.  Their Python cost (a few
-    # microseconds) is far below every side kernel's duration, and the small
-    # gaps keep these measurements from the power limiting that long runs of
-    # gap-free launches of the VALU-heavy quantize show (measured: FP4
-    # quantize 31-44 us, average 36.4, with direct calls after the other
-    # side kernels, against 29.7-31.0 with the wrappers).
+    # microseconds) is far below every side kernel's duration.  With direct
+    # calls the whole side round robin queued up at once, and the FP4
+    # quantize that follows it measured 31-44 us (average 36.4) against
+    # 29.7-31.0 us with the wrappers; alone, back to back or alternating
+    # with the nested dequantize, FP4 quantize runs 29.9-30.3 us, as NF4.
     def quant_only(s):
         kb.quantize_kbit(s["A"], cb, K, BLOCK, absmax=s["absmax"], packed=s["packed"])
 
