@@ -235,6 +235,13 @@ def test_full_size_8192_square(dtype):
     check_quantize(x, dtype, codebooks.nf(4), 4, 64, "8192^2")
 
 
+def test_full_size_8192_square_fp4_bf16():
+    # the FP4 side measurement's workload: 8192 x 8192 bf16, blocksize 64,
+    # FP4 (whose simple midpoints many bf16 values hit exactly); in full
+    x = synth.weight(8192, 8192, "bf16", seed=synth.SEED_WEIGHT_SHAPES)
+    check_quantize(x, "bf16", codebooks.fp4(), 4, 64, "8192^2 fp4")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("shape", ["wide11008", "tall11008", "square8192"])
 def test_weight_shapes_with_tail(shape, dtype):
