@@ -116,22 +116,23 @@ def parse(argv=None):
 CAL_BYTES = 192 << 20
 CAL_COPIES = 3
 _Q_SRC = ["blockwise_bit_codebook_amd/csrc/quantize.hip", "blockwise_bit_codebook_amd/csrc/device.h",
-          "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/e4m4.h"]
+          "blockwise_bit_codebook_amd/csrc/threshold.h", "blockwise_bit_codebook_amd/csrc/e4m4.h",
+          "blockwise_bit_codebook_amd/csrc/nested_sums.h"]
 _D_SRC = ["blockwise_bit_codebook_amd/csrc/dequantize.hip", "blockwise_bit_codebook_amd/csrc/device.h",
           "blockwise_bit_codebook_amd/csrc/e4m4.h"]
 _E_SRC = ["blockwise_bit_codebook_amd/csrc/nested_encode.hip", "blockwise_bit_codebook_amd/csrc/exact_mean.h",
-          "blockwise_bit_codebook_amd/csrc/device.h"]
+          "blockwise_bit_codebook_amd/csrc/device.h", "blockwise_bit_codebook_amd/csrc/nested_sums.h"]
 KERNELS = {
     # name used in the JSON line: (substrings that all appear in the HIP kernel's demangled name,
     # sources that define it)
-    "quantize_kbit_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "F32Scale, 4,"), _Q_SRC),
+    "quantize_kbit_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "F32Scale, 4,", ", false>"), _Q_SRC),
     "dequantize_4bit_nested_bf16": (("::dequantize_nested_kernel<kbit::Bf16",), _D_SRC),
-    "quantize_kbit_e4m4_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "E4m4Scale, 4,"), _Q_SRC),
+    "quantize_kbit_e4m4_bf16_k4": (("::quantize_kernel<kbit::Bf16,", "E4m4Scale, 4,", ", false>"), _Q_SRC),
     "dequantize_kbit_e4m4_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "E4m4Scale>"), _D_SRC),
     "dequantize_kbit_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "PlainScale>"), _D_SRC),
     # the nested-state encoder's two launches
     "nested_bins_kernel": (("::nested_bins_kernel",), _E_SRC),
-    "nested_encode_kernel": (("::nested_encode_kernel",), _E_SRC),
+    "nested_encode_kernel": (("::nested_encode_kernel<8>",), _E_SRC),
 }
 
 
@@ -661,6 +662,33 @@ def linear_bytes(M, N, K):
     return N * K // 2 + nb + 4 * (-(-nb // GROUP2)) + 4 * 256 + 64 + 2 * M * K + 2 * M * N
 
 
+def bench_quantize_nested(torch, kb, sets, cb, qmap, n, reps, round_robin, kstats):
+    """Per-call time of quantize_4bit_nested_bf16 (two kernels) and of
+    quantize_kbit_bf16_k4 followed by quantize_nested_absmax (three), in one
+    round robin over the buffer sets."""
+    nb = -(-n // BLOCK)
+
+    def fused(s):
+        kb.quantize_4bit_nested(s["A"], cb, qmap, BLOCK, absmax=s["absmax"], packed=s["packed"],
+                                absmax_code=s["enc_code"], absmax2=s["enc_a2"], offset=s["enc_off"],
+                                workspace=s["qws"])
+
+    def chain(s):
+        kb.quantize_kbit(s["A"], cb, K, BLOCK, absmax=s["absmax"], packed=s["packed"])
+        kb.quantize_nested_absmax(s["absmax"], qmap, absmax_code=s["enc_code"], absmax2=s["enc_a2"],
+                                  offset=s["enc_off"], workspace=s["ws"])
+
+    r = round_robin({"quantize_4bit_nested_bf16": fused, "quantize_kbit_bf16_k4+quantize_nested_absmax": chain},
+                    reps, bufs=sets)
+    kbytes = kernel_bytes(n)
+    enc_once = kbytes["quantize_nested_absmax"] - 4 * nb   # the absmax read once
+    return {"quantize_4bit_nested_bf16": kstats(r["quantize_4bit_nested_bf16"],
+                                                kbytes["quantize_kbit_bf16_k4"] + enc_once, elems=n),
+            "quantize_kbit_bf16_k4+quantize_nested_absmax": kstats(
+                r["quantize_kbit_bf16_k4+quantize_nested_absmax"],
+                kbytes["quantize_kbit_bf16_k4"] + kbytes["quantize_nested_absmax"], elems=n)}
+
+
 def bench_linear(torch, kb, synth, dev, reps=20, shapes=None, eager=False):
     """Fused 4-bit linear (nested state) at the page's shapes.  Each timed
     call uses a different weight set (rotated through > 400 MB, beyond the
@@ -852,6 +880,7 @@ def main(argv=None):
             "enc_a2": torch.empty(-(-nb // GROUP2), dtype=torch.float32, device=dev),
             "enc_off": torch.zeros(1, dtype=torch.float32, device=dev),
             "ws": torch.empty(kb.lib().kbit_nested_workspace_bytes(nb), dtype=torch.uint8, device=dev),
+            "qws": torch.empty(kb.lib().kbit_quantize_nested_workspace_bytes(), dtype=torch.uint8, device=dev),
         })
     torch.cuda.synchronize()
 
@@ -980,7 +1009,7 @@ def main(argv=None):
 
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
-    fp4 = warm = act = act_block = lin = sweep = cells = None
+    fp4 = warm = act = act_block = lin = sweep = cells = qnest = None
     if not args.headline_only:
         pair = {"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only}
         cb_nf = cb
@@ -1001,6 +1030,29 @@ def main(argv=None):
                 one = bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp)
                 one["prepared_tables"] = bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp, tables=True)
                 act_block.append(one)
+        # Quantize straight to the nested state (the sums inside quantize)
+        # against quantize followed by the encoder, as whole calls, on this
+        # weight and on a 4096x4096 one.
+        qnest = {"8192x8192": bench_quantize_nested(torch, kb, sets, cb, qmap, n, reps, round_robin, kstats)}
+        small = synth.weight(4096, 4096, "bf16", seed=synth.SEED_WEIGHT_SHAPES)
+        n_s = small.size
+        nb_s = -(-n_s // BLOCK)
+        x_s = torch.from_numpy(small.view(np.int16)).to(dev).view(torch.bfloat16)
+        sets_s = [{"A": x_s if i == 0 else x_s.clone(),
+                   "packed": torch.empty(kb.n_words(n_s, K), dtype=torch.int32, device=dev),
+                   "absmax": torch.empty(nb_s, dtype=torch.float32, device=dev),
+                   "enc_code": torch.empty(nb_s, dtype=torch.uint8, device=dev),
+                   "enc_a2": torch.empty(-(-nb_s // GROUP2), dtype=torch.float32, device=dev),
+                   "enc_off": torch.zeros(1, dtype=torch.float32, device=dev),
+                   "ws": torch.empty(kb.lib().kbit_nested_workspace_bytes(nb_s), dtype=torch.uint8, device=dev),
+                   "qws": torch.empty(kb.lib().kbit_quantize_nested_workspace_bytes(), dtype=torch.uint8,
+                                      device=dev)} for i in range(args.sets)]
+        qnest["4096x4096"] = bench_quantize_nested(torch, kb, sets_s, cb, qmap, n_s, reps, round_robin, kstats)
+        del sets_s, x_s
+        qnest["note"] = ("bf16 NF4 B=64 to the nested state (codes, absmax2, offset): quantize_4bit_nested_bf16 "
+                         "(two kernels; the quantize kernel also sums its block maxima exactly) against "
+                         "quantize_kbit_bf16_k4 then quantize_nested_absmax (three kernels); per call, "
+                         "bit-identical results")
         lin = bench_linear(torch, kb, synth, dev)
         sweep = bench_sweep(torch, kb, dev, reps)
         cells = bench_nested_cells(torch, kb, dev, max(4, reps // 2))
@@ -1111,6 +1163,7 @@ def main(argv=None):
         "nested_dequantize": kn,
         "e4m4_scales": e4,
         "nested_state_encoder": enc,
+        "quantize_to_nested_state": qnest,
         "fp4_codebook": fp4,
         "warm": warm,
         "act_fwht": act,

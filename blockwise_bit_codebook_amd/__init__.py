@@ -22,7 +22,7 @@ import numpy as np
 __all__ = [
     "KbitError", "lib", "codebook_nf", "codebook_fp4", "codebook_lloyd_max_normal",
     "dynamic_map8", "quantize_kbit", "dequantize_kbit", "dequantize_4bit_nested", "quantize_nested_absmax",
-    "quantize_nested_absmax_noalloc", "linear_4bit",
+    "quantize_nested_absmax_noalloc", "quantize_4bit_nested", "linear_4bit",
     "quantize_act_fwht_k4_bf16", "quantize_act_rpbh_k4_bf16", "act_tables_k4", "n_words", "n_blocks",
 ]
 
@@ -295,6 +295,44 @@ def quantize_nested_absmax_noalloc(absmax, qmap2, absmax_code, absmax2, offset):
     _check(name, lib().quantize_nested_absmax_noalloc(_ptr(absmax), nb, _ptr(qmap2), _ptr(absmax_code),
                                                       _ptr(absmax2), _ptr(offset), _stream(absmax.device)))
     return absmax_code, absmax2, offset
+
+
+def quantize_4bit_nested(A, codebook16, qmap2, blocksize, absmax=None, packed=None, absmax_code=None,
+                         absmax2=None, offset=None, workspace=None):
+    """Quantize A (fp32/fp16/bf16 CUDA tensor) straight to the nested 4-bit
+    state in two kernels -> (packed int32, absmax fp32, absmax_code u8,
+    absmax2 fp32, offset fp32[1]); the same bits as quantize_kbit(A, ..., 4)
+    followed by quantize_nested_absmax on its absmax.  The workspace
+    (scratch) is allocated here unless given."""
+    torch = _torch()
+    t = _dtype_name(A.dtype)
+    n = A.numel()
+    nb = _blocks(n, blocksize)
+    dev = A.device
+    if absmax is None:
+        absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+    if packed is None:
+        packed = torch.empty(n_words(n, 4), dtype=torch.int32, device=dev)
+    if absmax_code is None:
+        absmax_code = torch.empty(nb, dtype=torch.uint8, device=dev)
+    if absmax2 is None:
+        absmax2 = torch.empty(-(-nb // 256), dtype=torch.float32, device=dev)
+    if offset is None:
+        offset = torch.zeros(1, dtype=torch.float32, device=dev)
+    need = lib().kbit_quantize_nested_workspace_bytes()
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _buf(codebook16, "codebook16", torch.float32, 16)
+    _buf(absmax, "absmax", torch.float32, nb)
+    _buf(packed, "packed", torch.int32, n_words(n, 4))
+    _encode_args(absmax, qmap2, absmax_code, absmax2, offset)
+    _buf(workspace, "workspace", torch.uint8, need)
+    _same_device(A, codebook16=codebook16, absmax=absmax, packed=packed, qmap2=qmap2, workspace=workspace)
+    name = f"quantize_4bit_nested_{t}"
+    fn = getattr(lib(), name)
+    _check(name, fn(_ptr(codebook16), _ptr(A), _ptr(absmax), _ptr(packed), _ptr(qmap2), _ptr(absmax_code),
+                    _ptr(absmax2), _ptr(offset), n, blocksize, _ptr(workspace), workspace.numel(), _stream(dev)))
+    return packed, absmax, absmax_code, absmax2, offset
 
 
 def linear_4bit(X, packed, codebook16, N, blocksize, absmax=None, absmax_code=None, qmap2=None, absmax2=None,

@@ -41,6 +41,7 @@ def _signatures():
         ("quantize_nested_absmax", [_p, _i64, _p, _p, _p, _p, _p, _i64, _p]),
         ("kbit_nested_noalloc_scratch_bytes", []),
         ("quantize_nested_absmax_noalloc", [_p, _i64, _p, _p, _p, _p, _p]),
+        ("kbit_quantize_nested_workspace_bytes", []),
     ]
     for t in DTYPES:
         for k in KS:
@@ -50,6 +51,7 @@ def _signatures():
             sig.append((f"dequantize_kbit_e4m4_{t}_k{k}", [_p, _p, _p, _p, _i64, _i32, _p]))
         sig.append((f"dequantize_4bit_nested_{t}", [_p, _p, _p, _p, _p, _f32, _p, _i64, _i32, _p]))
         sig.append((f"dequantize_4bit_nested_{t}_offptr", [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _p]))
+        sig.append((f"quantize_4bit_nested_{t}", [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _p, _i64, _p]))
     return sig
 
 
@@ -67,6 +69,7 @@ def load(path=LIB_PATH):
         fn.argtypes = args
         fn.restype = {"kbit_strerror": ct.c_char_p, "kbit_nested_workspace_bytes": ct.c_int64,
                       "kbit_nested_noalloc_scratch_bytes": ct.c_int64,
+                      "kbit_quantize_nested_workspace_bytes": ct.c_int64,
                       "kbit_act_tables_bytes": ct.c_int64}.get(name, ct.c_int)
     return lib
 

@@ -238,6 +238,48 @@ int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2, 
         kbit::launch_nested_encode(absmax, nb, qmap2, absmax_code, absmax2, offset, workspace, stream));
 }
 
+int64_t kbit_quantize_nested_workspace_bytes(void) {
+    return static_cast<int64_t>(kbit::nested_max_records()) * kbit::nested_record_words() * 4;
+}
+
+namespace kbit {
+namespace {
+int do_quantize_nested(Dtype t, const float* codebook16, const void* A, float* absmax, uint32_t* packed,
+                       const float* qmap2, uint8_t* code, float* absmax2, float* offset, int64_t n,
+                       int32_t blocksize, void* workspace, int64_t workspace_bytes, void* stream) {
+    const int l2b = log2_block(blocksize);
+    if (l2b < 0) return KBIT_EBLOCK;
+    if (n < 0 || n > kMaxElems) return KBIT_EINVAL;
+    if (n == 0) return KBIT_OK;
+    if (!codebook16 || !A || !absmax || !packed || !qmap2 || !code || !absmax2 || !offset || !workspace)
+        return KBIT_EINVAL;
+    if (workspace_bytes < kbit_quantize_nested_workspace_bytes()) return KBIT_EINVAL;
+    if (!aligned(A, 16) || !aligned(codebook16, 4) || !aligned(absmax, 4) || !aligned(packed, 4) ||
+        !aligned(qmap2, 4) || !aligned(absmax2, 4) || !aligned(offset, 4) || !aligned(workspace, 4))
+        return KBIT_EALIGN;
+    if (current_device_cus() <= 0) return KBIT_EDEVICE;
+    const int64_t nb = (n + blocksize - 1) / blocksize;
+    uint32_t* records = static_cast<uint32_t*>(workspace);
+    int groups = 0;
+    const int q = launch_quantize_sums(t, codebook16, A, absmax, packed, n, l2b, records, &groups, stream);
+    if (q != 0) return KBIT_ELAUNCH;
+    return map_launch(launch_nested_encode_records(absmax, nb, qmap2, code, absmax2, offset, records, groups, stream));
+}
+}  // namespace
+}  // namespace kbit
+
+#define KBIT_DEFINE_QUANTIZE_NESTED(TNAME, CTYPE, DT)                                                          \
+    int quantize_4bit_nested_##TNAME(const float* codebook16, const CTYPE* A, float* absmax, uint32_t* packed, \
+                                     const float* qmap2, uint8_t* absmax_code, float* absmax2, float* offset,  \
+                                     int64_t n, int32_t blocksize, void* workspace, int64_t workspace_bytes,   \
+                                     void* stream) {                                                           \
+        return kbit::do_quantize_nested(kbit::Dtype::DT, codebook16, A, absmax, packed, qmap2, absmax_code,    \
+                                        absmax2, offset, n, blocksize, workspace, workspace_bytes, stream);    \
+    }
+KBIT_DEFINE_QUANTIZE_NESTED(fp32, float, fp32)
+KBIT_DEFINE_QUANTIZE_NESTED(fp16, uint16_t, fp16)
+KBIT_DEFINE_QUANTIZE_NESTED(bf16, uint16_t, bf16)
+
 int64_t kbit_nested_noalloc_scratch_bytes(void) { return kbit::nested_scratch_bytes(); }
 
 int quantize_nested_absmax_noalloc(const float* absmax, int64_t nb, const float* qmap2, uint8_t* absmax_code,

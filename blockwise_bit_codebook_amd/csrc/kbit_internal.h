@@ -16,6 +16,12 @@ enum class ScaleFmt : int { f32 = 0, e4m4 = 1 };
 int launch_quantize(Dtype t, ScaleFmt f, int K, const float* codebook, const void* A, void* absmax,
                     uint32_t* packed, int64_t n, int log2B, void* stream);
 
+// K = 4 quantize with fp32 absmax that also stores, per workgroup, the
+// record of the exact sum of its block maxima (word-major, *groups records
+// of nested_record_words() words, at most nested_max_records()).
+int launch_quantize_sums(Dtype t, const float* codebook16, const void* A, float* absmax, uint32_t* packed,
+                         int64_t n, int log2B, uint32_t* records, int* groups, void* stream);
+
 int launch_dequantize(Dtype t, ScaleFmt f, int K, const uint32_t* packed, const float* codebook,
                       const void* absmax, void* out, int64_t n, int log2B, void* stream);
 
@@ -29,6 +35,13 @@ int64_t nested_workspace_bytes(int64_t nb);
 
 int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
                          float* offset, void* workspace, void* stream);
+
+// The encoder's second launch alone, over `groups` records that a previous
+// launch on the stream stored (launch_quantize_sums).
+int launch_nested_encode_records(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code,
+                                 float* absmax2, float* offset, const void* records, int groups, void* stream);
+int nested_record_words();
+int nested_max_records();
 
 // The encoder's static device workspace: its size, and its device address
 // on the current device (null if it cannot be looked up).

@@ -38,6 +38,7 @@
 #include "device.h"
 #include "exact_mean.h"
 #include "kbit_internal.h"
+#include "nested_sums.h"
 
 #include <atomic>
 
@@ -47,102 +48,30 @@ namespace {
 constexpr int kBinThreads = 1024;
 constexpr int kBinWaves = kBinThreads / kWave;
 constexpr int kMaxBinGroups = 256;  // workgroups of launch 1 (the workspace holds one record each)
-constexpr int kLimbWords = kWideLimbs + 2;
-constexpr int kRecordWords = 2 * kLimbWords + 1;  // uint32: digits[sign][i], then the flags
 constexpr int kEncThreads = 1024;                       // launch 2: one group of 256 blocks per wave
 constexpr int kEncWaves = kEncThreads / kWave;
 constexpr int kEncMaxGrid = 512;                        // each workgroup of launch 2 re-reads the records
 constexpr int kOffsetParts = 32;                        // lanes per record word in the mean (a half wave)
-constexpr int kOffsetLoads = kMaxBinGroups / kOffsetParts;  // records per such lane
+static_assert(kMaxBinGroups <= kMaxSumGroups, "the second launch reads every first launch's records");
 static_assert(kRecordWords * kOffsetParts <= kEncThreads, "a half wave per record word");
 constexpr int kGroup2 = 256;
 constexpr float kEps2 = 1e-8f;
-constexpr uint32_t kFlagNan = 1, kFlagPosInf = 2, kFlagNegInf = 4;
 
-constexpr int kBinVecs = 1;      // 16-byte loads per lane per round (4 values)
-constexpr int kWindowBits = 24;  // binades below the wave's top one that the register sums take
-constexpr int64_t kRoundValues = static_cast<int64_t>(kBinThreads) * kBinVecs * 4;  // per workgroup
+constexpr int64_t kRoundValues = static_cast<int64_t>(kBinThreads) * 4;  // per workgroup
 
 int bin_groups(int64_t nb) {
     const int64_t g = (nb + kRoundValues - 1) / kRoundValues;
     return static_cast<int>(g < 1 ? 1 : (g > kMaxBinGroups ? kMaxBinGroups : g));
 }
 
-// Lane i of each row of 16 gets lane i - 1's value, lane 0 of a row gets 0
-// (DPP row_shr:1; with bound_ctrl set, a source lane outside the row reads
-// as zero).
-__device__ __forceinline__ uint32_t row_shr1_or_zero(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x111, 0xF, 0xF, true));
-}
-
-template <int CTRL>
-__device__ __forceinline__ int32_t dpp_i32(int32_t v) {
-    return static_cast<int32_t>(dpp_u32<CTRL>(static_cast<uint32_t>(v)));
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-    return (static_cast<uint64_t>(dpp_u32<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) |
-           dpp_u32<CTRL>(static_cast<uint32_t>(v));
-}
-
-__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
-    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
-}
-
-// Sum over the wave (every lane active), returned uniform: DPP within each
-// row of 16 lanes, then the four row totals read out.
-__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-    v += dpp_u64<kDppXor1>(v);
-    v += dpp_u64<kDppXor2>(v);
-    v += dpp_u64<kDppHalfMirror>(v);
-    v += dpp_u64<kDppMirror>(v);
-    uint64_t t = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        t += (static_cast<uint64_t>(readlane_u32(static_cast<uint32_t>(v >> 32), 16 * r)) << 32) |
-             readlane_u32(static_cast<uint32_t>(v), 16 * r);
-    }
-    return t;
-}
-
-// Maximum over the wave (every lane active), returned uniform.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, dpp_u32<kDppXor1>(v));
-    v = max(v, dpp_u32<kDppXor2>(v));
-    v = max(v, dpp_u32<kDppHalfMirror>(v));
-    v = max(v, dpp_u32<kDppMirror>(v));
-    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
-}
-
-// Launch 1.  Per round a wave holds 4 values per lane.  A finite nonzero
-// value with biased exponent e and integer significand m is m * 2^(e' - 1)
-// in units of 2^-149, e' = max(e, 1).  With E the wave's largest e' and
-// e0 = max(E - 24, 1), every value with e' >= e0 adds m << (e' - e0) (below
-// 2^48) to the register sum of its sign, in units of 2^(e0 - 1); the wave's
-// two sums (below 2^56) go into the wave's own limb accumulators in LDS
-// once per round, as three pieces below 2^33 (lane 0 alone writes them, so
-// no atomics).  Values further down (more than 24 binades below the wave's
-// top) add m to the workgroup's LDS bin of their sign and e, folded into
-// wave 0's limbs at the end (only if any exist).  NaN and infinities only
-// set flags.  Then wave 0 adds the waves' limbs (lane 16 s + i takes limb i
-// of sign s) and carries them into 32-bit digits.
-//
-// Bounds (nb <= 2^36, at most 2^28 values per workgroup): a wave's limb
-// takes at most one piece per round and sign, so all 16 waves' limbs of
-// one index add up to below 2^20 * 2^33 (2^20 wave rounds of 256 values),
-// plus at most 256 bin pieces; a bin stays below 2^28 * 2^24.  A
-// workgroup's sum is below 2^28 * 2^277, so its carried digits fit the 10
-// low limbs and each is below 2^32; launch 2 adds at most 256 of them per
+// Launch 1: each workgroup's exact sums of its values (nested_sums.h), one
+// round of 4 values per lane at a time, stored as its record.  With
+// nb <= 2^36 and at most 256 workgroups a workgroup holds at most 2^28
+// values, within the sums' bounds; launch 2 adds at most 256 digits per
 // limb.
-//
-// The record is word-major: word k of workgroup b at ws[k * groups + b],
-// so that launch 2 reads each word of all records with contiguous loads.
 __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* __restrict__ a, int64_t nb,
                                                                   uint32_t* __restrict__ ws) {
-    __shared__ unsigned long long bins[2][256];
-    __shared__ unsigned long long wlimbs[kBinWaves][2][kLimbWords];
-    __shared__ uint32_t flags, any_slow;
+    __shared__ SumsShared<kBinWaves> sh;
     const int wave = threadIdx.x / kWave;
     const int lane = __lane_id();
     uint32_t my_flags = 0;
@@ -153,145 +82,38 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kBinThreads;
     const u32x4* av = reinterpret_cast<const u32x4*>(a);
     const bool aligned16 = (reinterpret_cast<uintptr_t>(a) & 15u) == 0;
-    const auto load_round = [&](int64_t wb, u32x4 (&u)[kBinVecs]) {
+    const auto load_round = [&](int64_t wb, u32x4& u) {
+        const int64_t vi = wb + lane;
+        if (aligned16 && vi < nvec) {
+            u = av[vi];
+        } else {
 #pragma unroll
-        for (int k = 0; k < kBinVecs; ++k) {
-            const int64_t vi = wb + lane + k * stride;
-            if (aligned16 && vi < nvec) {
-                u[k] = av[vi];
-            } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) u[k][c] = 4 * vi + c < nb ? __float_as_uint(a[4 * vi + c]) : 0u;
-            }
+            for (int c = 0; c < 4; ++c) u[c] = 4 * vi + c < nb ? __float_as_uint(a[4 * vi + c]) : 0u;
         }
     };
     // the first round's loads are in flight while the LDS is cleared
     const int64_t wb0 = static_cast<int64_t>(blockIdx.x) * kBinThreads + wave * kWave;
     int64_t wb = wb0;
-    u32x4 u[kBinVecs];
+    u32x4 u;
     load_round(wb, u);
-    for (int i = threadIdx.x; i < 2 * 256; i += kBinThreads) (&bins[0][0])[i] = 0;
-    for (int i = threadIdx.x; i < kBinWaves * 2 * kLimbWords; i += kBinThreads) (&wlimbs[0][0][0])[i] = 0;
-    if (threadIdx.x == 0) flags = any_slow = 0;
+    sums_clear<kBinWaves, kBinThreads>(sh);
     __syncthreads();
-    unsigned long long* my_limbs = &wlimbs[wave][0][0];
-    for (; wb < nvec_all; wb += kBinVecs * stride) {
+    for (; wb < nvec_all; wb += stride) {
         if (wb != wb0) load_round(wb, u);
-        uint32_t top = 0;
-#pragma unroll
-        for (int k = 0; k < kBinVecs; ++k) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t e = (u[k][c] >> 23) & 0xFFu;
-                if (e != 0xFFu && (u[k][c] & 0x7FFFFFFFu) != 0) top = max(top, max(e, 1u));
-            }
-        }
-        top = wave_max_u32(top);
-        const uint32_t e0 = top > kWindowBits + 1 ? top - kWindowBits : 1u;
-        // branch-free for the values in the window; the rest (rare) after
-        uint64_t sum_pos = 0, sum_neg = 0;
-        uint32_t slow = 0;
-#pragma unroll
-        for (int k = 0; k < kBinVecs; ++k) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint32_t x = u[k][c];
-                const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
-                const bool neg = (x >> 31) != 0, special = e == 0xFFu;
-                my_flags |= special ? (f ? kFlagNan : (neg ? kFlagNegInf : kFlagPosInf)) : 0u;
-                const uint32_t ee = max(e, 1u), m = e ? (f | 0x800000u) : f;  // m = 0 for zeros
-                const bool fast = !special && ee >= e0;
-                const uint64_t t = static_cast<uint64_t>(fast ? m : 0u) << (fast ? ee - e0 : 0u);
-                sum_neg += neg ? t : 0ull;
-                sum_pos += neg ? 0ull : t;
-                slow |= (!special && !fast && m != 0) ? (1u << (4 * k + c)) : 0u;
-            }
-        }
-        if (slow != 0) {
-            atomicOr(&any_slow, 1u);
-#pragma unroll
-            for (int k = 0; k < kBinVecs; ++k) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (slow & (1u << (4 * k + c))) {
-                        const uint32_t x = u[k][c];
-                        const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
-                        atomicAdd(&bins[x >> 31][e], static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
-                    }
-                }
-            }
-        }
-        sum_pos = wave_sum_u64(sum_pos);
-        sum_neg = wave_sum_u64(sum_neg);
-        if (lane == 0) {
-#pragma unroll
-            for (int sg = 0; sg < 2; ++sg) {
-                const uint64_t v = sg ? sum_neg : sum_pos;
-                if (v != 0) {
-                    const WidePieces q = wide_pieces(v, static_cast<int>(e0) - 1);
-                    unsigned long long* l = my_limbs + sg * kLimbWords + q.w;
-                    l[0] += q.p0;
-                    l[1] += q.p1;
-                    l[2] += q.p2;
-                }
-            }
-        }
+        sums_round<kBinWaves>(sh, wave, lane, u, my_flags);
     }
-    if (my_flags) atomicOr(&flags, my_flags);
-    __syncthreads();
-    if (any_slow != 0) {  // workgroup-uniform: bins -> wave 0's limbs
-        for (int i = threadIdx.x; i < 2 * 256; i += kBinThreads) {
-            const uint64_t sum = (&bins[0][0])[i];
-            const int sg = i >> 8, e = i & 255;
-            if (sum != 0) {
-                const WidePieces q = wide_pieces(sum, (e > 0 ? e : 1) - 1);
-                atomicAdd(&wlimbs[0][sg][q.w], static_cast<unsigned long long>(q.p0));
-                atomicAdd(&wlimbs[0][sg][q.w + 1], static_cast<unsigned long long>(q.p1));
-                atomicAdd(&wlimbs[0][sg][q.w + 2], static_cast<unsigned long long>(q.p2));
-            }
-        }
-        __syncthreads();
-    }
-    if (wave == 0) {
-        // Lane 16 s + i (i < 12) adds limb i of sign s over all waves
-        // (t < 2^54), then the digits: each limb keeps its low 32 bits plus
-        // the high part of the limb below (one DPP row shift: each sign's
-        // limbs sit in one row of 16 lanes), which leaves sums below 2^33,
-        // i.e. carries of 0 or 1.  Those resolve as in a carry-lookahead
-        // adder: G marks the lanes whose sum reached 2^32, P those whose low
-        // 32 bits are all ones (they pass a carry on), and the carry into
-        // each lane is bit i of ((G | P) + G) ^ (G | P) ^ G.  Limbs 10 and 11
-        // never receive pieces (the top piece lands at limb 9), so no carry
-        // leaves a sign's row.
-        const int sg = lane >> 4, li = lane & 15;
-        const bool mine = lane < 32 && li < kLimbWords;
-        uint64_t t = 0;
-        if (mine) {
-#pragma unroll
-            for (int w = 0; w < kBinWaves; ++w) t += wlimbs[w][sg][li];
-        }
-        const uint32_t hi_below = row_shr1_or_zero(static_cast<uint32_t>(t >> 32));
-        const uint64_t sum = (t & 0xFFFFFFFFull) + hi_below;
-        const uint32_t low = static_cast<uint32_t>(sum);
-        const uint64_t G = __ballot(mine && (sum >> 32) != 0);
-        const uint64_t P = __ballot(mine && low == 0xFFFFFFFFu);
-        const uint64_t carries = ((G | P) + G) ^ (G | P) ^ G;
-        const uint32_t digit = low + static_cast<uint32_t>((carries >> lane) & 1ull);
-        const int64_t groups = gridDim.x;
-        if (mine) ws[(sg * kLimbWords + li) * groups + blockIdx.x] = digit;
-        if (lane == 0) ws[2 * kLimbWords * groups + blockIdx.x] = flags;
-    }
+    sums_record<kBinWaves, kBinThreads>(sh, my_flags, ws, gridDim.x, blockIdx.x);
 }
 
 // The records of launch 1 for the mean: half wave h of the workgroup
 // (kOffsetParts = 32 lanes) takes record word h (a digit of one sign, or
-// the flags) of every record, eight per lane, widened to 64 bits; halves
-// past the last word load nothing.
-__device__ __forceinline__ void load_records(const uint32_t* __restrict__ ws, int groups,
-                                             uint64_t (&v)[kOffsetLoads]) {
+// the flags) of every record, LOADS per lane (up to 32 * LOADS records),
+// widened to 64 bits; halves past the last word load nothing.
+template <int LOADS>
+__device__ __forceinline__ void load_records(const uint32_t* __restrict__ ws, int groups, uint64_t (&v)[LOADS]) {
     const int k = threadIdx.x / kOffsetParts, part = threadIdx.x % kOffsetParts;
 #pragma unroll
-    for (int j = 0; j < kOffsetLoads; ++j) {
+    for (int j = 0; j < LOADS; ++j) {
         const int g = part + j * kOffsetParts;
         v[j] = (k < kRecordWords && g < groups) ? ws[static_cast<int64_t>(k) * groups + g] : 0;
     }
@@ -304,14 +126,15 @@ __device__ __forceinline__ uint64_t dpp_or_u64(uint64_t v) {
 
 // The mean offset from the loaded records: each half wave sums (ORs, for
 // the flags) its word; thread 0 rounds the mean from the limb totals (each
-// below 2^40).  Every thread gets the offset (through LDS).  All threads of
-// the workgroup call it.
-__device__ inline float mean_offset(const uint64_t (&v)[kOffsetLoads], const NbDivider& div) {
+// below 2^41: at most 512 digits below 2^32).  Every thread gets the offset
+// (through LDS).  All threads of the workgroup call it.
+template <int LOADS>
+__device__ inline float mean_offset(const uint64_t (&v)[LOADS], const NbDivider& div) {
     __shared__ unsigned long long total[kRecordWords];
     __shared__ float off;
     uint64_t sum = 0, any = 0;
 #pragma unroll
-    for (int j = 0; j < kOffsetLoads; ++j) {
+    for (int j = 0; j < LOADS; ++j) {
         sum += v[j];
         any |= v[j];
     }
@@ -479,6 +302,9 @@ __device__ __forceinline__ void load_group(const float* __restrict__ a, int64_t 
     }
 }
 
+// LOADS: records per lane of the mean's half waves (up to 32 * LOADS
+// records in ws).
+template <int LOADS>
 __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float* __restrict__ a, int64_t nb,
                                                                     const float* __restrict__ qmap2,
                                                                     const uint32_t* __restrict__ ws, int groups,
@@ -487,7 +313,7 @@ __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float*
                                                                     float* __restrict__ absmax2, NbDivider div) {
     __shared__ float c[256];
     __shared__ int unsorted;
-    uint64_t rec[kOffsetLoads];
+    uint64_t rec[LOADS];
     load_records(ws, groups, rec);  // first: the mean waits on these
     if (threadIdx.x == 0) unsorted = 0;
     __syncthreads();
@@ -559,19 +385,43 @@ int64_t nested_workspace_bytes(int64_t nb) {
     return static_cast<int64_t>(bin_groups(nb)) * kRecordWords * 4;
 }
 
+namespace {
+// Launch 2 over `groups` records (LOADS = records per lane of the mean).
+template <int LOADS>
+void launch_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
+                   float* offset, const uint32_t* ws, int groups, hipStream_t st) {
+    const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
+    const int64_t want = (ngroups + kEncWaves - 1) / kEncWaves;
+    const int64_t grid = want < kEncMaxGrid ? want : kEncMaxGrid;
+    hipLaunchKernelGGL(nested_encode_kernel<LOADS>, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st,
+                       absmax, nb, qmap2, ws, groups, offset, code, absmax2,
+                       make_nb_divider(static_cast<uint64_t>(nb)));
+}
+}  // namespace
+
 int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
                          float* offset, void* workspace, void* stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const int groups = bin_groups(nb);
     uint32_t* ws = static_cast<uint32_t*>(workspace);
     hipLaunchKernelGGL(nested_bins_kernel, dim3(groups), dim3(kBinThreads), 0, st, absmax, nb, ws);
-    const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
-    const int64_t want = (ngroups + kEncWaves - 1) / kEncWaves;
-    const int64_t grid = want < kEncMaxGrid ? want : kEncMaxGrid;
-    hipLaunchKernelGGL(nested_encode_kernel, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st, absmax, nb,
-                       qmap2, ws, groups, offset, code, absmax2, make_nb_divider(static_cast<uint64_t>(nb)));
+    launch_encode<kMaxBinGroups / kOffsetParts>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
     return static_cast<int>(hipGetLastError());
 }
+
+int launch_nested_encode_records(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code,
+                                 float* absmax2, float* offset, const void* records, int groups, void* stream) {
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint32_t* ws = static_cast<const uint32_t*>(records);
+    if (groups <= kMaxBinGroups)
+        launch_encode<kMaxBinGroups / kOffsetParts>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
+    else
+        launch_encode<kMaxSumGroups / kOffsetParts>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
+    return static_cast<int>(hipGetLastError());
+}
+
+int nested_record_words() { return kRecordWords; }
+int nested_max_records() { return kMaxSumGroups; }
 
 // The encoder's workspace in device memory of this library, for callers
 // that cannot allocate: one copy per GPU, kept until the process ends.  Its

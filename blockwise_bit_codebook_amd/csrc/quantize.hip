@@ -66,10 +66,17 @@
 //     pass of the ring is the same straight-line code and the compiler
 //     waits for each row's own loads only.  The first ring loads go out
 //     before the table build.
+//   * A variant (K = 4, fp32 absmax) also sums the block maxima exactly for
+//     the nested state's mean: each maximum's integer significand goes into
+//     the workgroup's LDS bin of its exponent (one 64-bit LDS atomic by the
+//     lane that holds it), and at the end the bins are folded into 32-bit
+//     digits and stored as the workgroup's record (nested_sums.h), so that
+//     the encoder's second launch can follow directly.
 #include "device.h"
 #include "e4m4.h"
 #include "kbit_internal.h"
 #include "launch.h"
+#include "nested_sums.h"
 #include "threshold.h"
 
 #include <atomic>
@@ -318,13 +325,27 @@ struct E4m4Scale {
 template <class E>
 constexpr int kRing = E::kVec == 1 ? 4 : 2;
 
+// LDS of the variant that also sums the block maxima exactly for the
+// nested state's mean (nested_sums.h): each maximum's integer significand
+// goes into the workgroup's bin of its exponent (one LDS atomic), and the
+// bins are folded into the record at the end.  Only that variant's kernels
+// reference it, so only they allocate it.
+template <int WAVES>
+__device__ __forceinline__ SumsShared<WAVES>& quant_sums() {
+    __shared__ SumsShared<WAVES> s;
+    return s;
+}
+
 // LOG2B = log2(B) for B <= 512 (blocks inside a wave row); LOG2B = 0 for
-// B = 1024..4096 (blocks spanning rows; log2B from the argument).
-template <class E, class S, int K, int LOG2B, int THREADS>
-__global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restrict__ cb,
+// B = 1024..4096 (blocks spanning rows; log2B from the argument).  SUMS:
+// also store the workgroup's record of the exact sum of its block maxima
+// (word-major in ws, gridDim.x records) for the nested state's mean.
+template <class E, class S, int K, int LOG2B, int THREADS, bool SUMS>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(SUMS ? 8 : 1))) void quantize_kernel(const float* __restrict__ cb,
                                                              const typename E::storage* __restrict__ A,
                                                              typename S::type* __restrict__ absmax,
-                                                             uint32_t* __restrict__ packed, int64_t n, int log2B) {
+                                                             uint32_t* __restrict__ packed, int64_t n, int log2B,
+                                                             uint32_t* __restrict__ ws) {
     constexpr int C = 1 << K;
     constexpr int kV = E::kVec;
     constexpr int kWaves_ = THREADS / kWave;
@@ -371,6 +392,10 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     for (int i = 0; i < C; ++i) c[i] = cb[i];
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
+    if constexpr (SUMS) {
+        sums_clear<kWaves_, THREADS>(quant_sums<kWaves_>());
+        if (threadIdx.x == 0) quant_sums<kWaves_>().any_slow = 1;  // every value is in the bins
+    }
     if (threadIdx.x < C) T.code[threadIdx.x] = c[threadIdx.x];
     // One wave per threshold, or one half-wave where there are more
     // thresholds than waves (the search is cooperative); a failed search
@@ -405,6 +430,26 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
     const char* tab = reinterpret_cast<const char*>(T.row);
 
+    // SUMS: the block maxima of the wave (lane i * lpb holds block i's, 64 /
+    // lpb of them) into the workgroup's exponent bins; NaN and infinities
+    // only set flags, zeros add nothing.  A workgroup takes below 2^28
+    // maxima (n <= 2^40 spread over at least 256 workgroups, or at most one
+    // wave row per wave), so a bin stays below 2^52.
+    uint32_t sum_flags = 0;
+    auto sums_push = [&](float m, int lpb) {
+        if constexpr (SUMS) {
+            const uint32_t x = __float_as_uint(m);
+            const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
+            if ((lane & (lpb - 1)) == 0) {
+                if (e == 0xFFu)
+                    sum_flags |= f ? kFlagNan : ((x >> 31) ? kFlagNegInf : kFlagPosInf);
+                else if ((x & 0x7FFFFFFFu) != 0)
+                    atomicAdd(&quant_sums<kWaves_>().bins[x >> 31][e],
+                              static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
+            }
+        }
+    };
+
     if constexpr (LOG2B != 0) {
         static_assert(LOG2B >= 5 && LOG2B <= 9, "rows hold whole blocks of 32..512");
         constexpr int kLpb = (1 << LOG2B) / kElemsPerLane;  // lanes per block
@@ -430,6 +475,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
                 __builtin_amdgcn_raw_buffer_store_b8(S::encode(m), am_rs, scale_off, 0, 0);
             else
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), am_rs, scale_off, 0, 0);
+            sums_push(m, kLpb);  // rows past the end read as zeros: their maxima add nothing
             const Codes cd = classify_row<E, K>(fast, T, tab, lane_off, x, m);
             __builtin_amdgcn_raw_buffer_store_b32(quad_transpose_bytes(cd.acc, lane), pk_rs, word_off, 0, 0);
             if constexpr (K == 5)
@@ -464,6 +510,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
             const float m = block_max_abs<kLpb>(x);
             typename S::type* am = absmax + (base >> LOG2B);  // wave-uniform
             if ((lane & (kLpb - 1)) == 0 && base + lane_e < n) am[lane_e >> LOG2B] = S::encode(m);
+            sums_push(m, kLpb);  // blocks past n read as zeros: their maxima add nothing
             encode_partial_row<E, K>(fast, T, tab, lane_off, lane, x, m, base, n, packed);
         }
     } else {
@@ -484,6 +531,7 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
             }
             const float m = __uint_as_float(run_max_u32<kWave>(__float_as_uint(ml)));
             if (lane == 0) absmax[b] = S::encode(m);
+            sums_push(m, kWave);
             for (int u = 0; u < rows; ++u) {
                 const int64_t rb = base + u * kWaveTile;
                 if (rb >= n) break;
@@ -495,42 +543,47 @@ __global__ __launch_bounds__(THREADS) void quantize_kernel(const float* __restri
             }
         }
     }
+    if constexpr (SUMS) sums_record<kWaves_, THREADS>(quant_sums<kWaves_>(), sum_flags, ws, gridDim.x, blockIdx.x);
 }
 
 // Launch over a persistent grid: the resident workgroups of the device,
-// fewer when there are fewer wave rows (or blocks) than waves.
-template <class E, class S, int K, int LOG2B, int THREADS>
+// fewer when there are fewer wave rows (or blocks) than waves.  With ws
+// (the nested-state variant) the grid also stays within kMaxSumGroups, the
+// records that ws holds; *groups gets the grid size.
+template <class E, class S, int K, int LOG2B, int THREADS, bool SUMS>
 int launch_cfg(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
-               void* stream) {
-    auto kern = quantize_kernel<E, S, K, LOG2B, THREADS>;
+               uint32_t* ws, int* groups, void* stream) {
+    auto kern = quantize_kernel<E, S, K, LOG2B, THREADS, SUMS>;
     static std::atomic<int> occupancy[kMaxDevices];
     const int blocks_per_cu = cached_blocks_per_cu(kern, THREADS, occupancy);
     const int64_t units = LOG2B == 0 ? ((n + (1LL << log2B) - 1) >> log2B) : (n + kWaveTile - 1) / kWaveTile;
     constexpr int waves = THREADS / kWave;
     int64_t grid = (units + waves - 1) / waves;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
+    int64_t cap = static_cast<int64_t>(device_cu_count()) * blocks_per_cu;
+    if (SUMS && cap > kMaxSumGroups) cap = kMaxSumGroups;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
+    if (groups) *groups = static_cast<int>(grid);
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(THREADS), 0,
                        static_cast<hipStream_t>(stream), cb,
                        static_cast<const typename E::storage*>(A), static_cast<typename S::type*>(absmax),
-                       packed, n, log2B);
+                       packed, n, log2B, ws);
     return static_cast<int>(hipGetLastError());
 }
 
-template <class E, class S, int K>
+template <class E, class S, int K, bool SUMS = false>
 int launch_k(const float* cb, const void* A, void* absmax, uint32_t* packed, int64_t n, int log2B,
-             void* stream) {
+             void* stream, uint32_t* ws = nullptr, int* groups = nullptr) {
     // K = 5 runs 512-thread groups (52-54 VGPRs, 8 waves per SIMD either
     // way); 1024-thread groups measured the same within noise.
     constexpr int TH = K == 5 ? 512 : kQThreads;
     switch (log2B) {
-        case 5: return launch_cfg<E, S, K, 5, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 6: return launch_cfg<E, S, K, 6, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 7: return launch_cfg<E, S, K, 7, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 8: return launch_cfg<E, S, K, 8, TH>(cb, A, absmax, packed, n, log2B, stream);
-        case 9: return launch_cfg<E, S, K, 9, TH>(cb, A, absmax, packed, n, log2B, stream);
-        default: return launch_cfg<E, S, K, 0, TH>(cb, A, absmax, packed, n, log2B, stream);
+        case 5: return launch_cfg<E, S, K, 5, TH, SUMS>(cb, A, absmax, packed, n, log2B, ws, groups, stream);
+        case 6: return launch_cfg<E, S, K, 6, TH, SUMS>(cb, A, absmax, packed, n, log2B, ws, groups, stream);
+        case 7: return launch_cfg<E, S, K, 7, TH, SUMS>(cb, A, absmax, packed, n, log2B, ws, groups, stream);
+        case 8: return launch_cfg<E, S, K, 8, TH, SUMS>(cb, A, absmax, packed, n, log2B, ws, groups, stream);
+        case 9: return launch_cfg<E, S, K, 9, TH, SUMS>(cb, A, absmax, packed, n, log2B, ws, groups, stream);
+        default: return launch_cfg<E, S, K, 0, TH, SUMS>(cb, A, absmax, packed, n, log2B, ws, groups, stream);
     }
 }
 
@@ -561,6 +614,18 @@ int launch_quantize(Dtype t, ScaleFmt f, int K, const float* codebook, const voi
                     uint32_t* packed, int64_t n, int log2B, void* stream) {
     if (f == ScaleFmt::e4m4) return launch_s<E4m4Scale>(t, K, codebook, A, absmax, packed, n, log2B, stream);
     return launch_s<F32Scale>(t, K, codebook, A, absmax, packed, n, log2B, stream);
+}
+
+int launch_quantize_sums(Dtype t, const float* codebook16, const void* A, float* absmax, uint32_t* packed,
+                         int64_t n, int log2B, uint32_t* records, int* groups, void* stream) {
+    switch (t) {
+        case Dtype::fp32:
+            return launch_k<Fp32, F32Scale, 4, true>(codebook16, A, absmax, packed, n, log2B, stream, records, groups);
+        case Dtype::fp16:
+            return launch_k<Fp16, F32Scale, 4, true>(codebook16, A, absmax, packed, n, log2B, stream, records, groups);
+        default:
+            return launch_k<Bf16, F32Scale, 4, true>(codebook16, A, absmax, packed, n, log2B, stream, records, groups);
+    }
 }
 
 }  // namespace kbit

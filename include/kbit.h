@@ -286,6 +286,36 @@ int quantize_nested_absmax(const float* absmax, int64_t nb, const float* qmap2,
                            uint8_t* absmax_code, float* absmax2, float* offset,
                            void* workspace, int64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Quantize straight to the nested 4-bit state: quantize_kbit_*_k4 (fp32
+ * absmax) and then quantize_nested_absmax on that absmax, in two kernels
+ * instead of three.  The quantize kernel also sums its own block maxima
+ * exactly (one record per workgroup in the workspace), so the encoder's
+ * pass over the absmax for the mean is not needed; the second kernel rounds
+ * the mean and encodes.  Results (absmax, packed, absmax_code, absmax2,
+ * offset) are bit-identical to those two calls'.  ([PR2051] Summary: the
+ * state the fused nested dequantize reads; the encoder itself is this
+ * library's reading, as quantize_nested_absmax.)
+ * codebook16, A, absmax, packed : as quantize_kbit_*_k4 (absmax is written
+ *               and then read by the second kernel).
+ * qmap2, absmax_code, absmax2, offset : as quantize_nested_absmax.
+ * workspace   : device, >= kbit_quantize_nested_workspace_bytes() bytes
+ *               (51,200), 4-byte aligned, owned by the caller; scratch (no
+ *               initialisation needed).  Calls that share a workspace must
+ *               not overlap.
+ * n == 0 is a no-op.  Two kernels run in order on the stream.
+ * --------------------------------------------------------------------- */
+int64_t kbit_quantize_nested_workspace_bytes(void);
+#define KBIT_DECLARE_QUANTIZE_NESTED(TNAME, CTYPE)                                           \
+    int quantize_4bit_nested_##TNAME(const float* codebook16, const CTYPE* A, float* absmax, \
+                                     uint32_t* packed, const float* qmap2,                   \
+                                     uint8_t* absmax_code, float* absmax2, float* offset,    \
+                                     int64_t n, int32_t blocksize, void* workspace,          \
+                                     int64_t workspace_bytes, void* stream);
+KBIT_DECLARE_QUANTIZE_NESTED(fp32, float)
+KBIT_DECLARE_QUANTIZE_NESTED(fp16, uint16_t)
+KBIT_DECLARE_QUANTIZE_NESTED(bf16, uint16_t)
+
 /* quantize_nested_absmax without a workspace argument and without any
  * allocation, for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid it).  The

@@ -37,7 +37,7 @@ def test_header_compiles_as_c_and_cpp():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 4 + 2 + 24 + 24 + 3 + 3 + 2 + 2 + 2 + 2 + 1 + 4, names
+    assert len(names) == 4 + 2 + 24 + 24 + 3 + 3 + 2 + 2 + 2 + 2 + 1 + 4 + 4, names
     nm = subprocess.run(["nm", "-D", "--defined-only", os.path.join(ROOT, "blockwise_bit_codebook_amd", "libkbit.so")],
                         capture_output=True, text=True, check=True).stdout
     exported = set(l.split()[-1] for l in nm.splitlines() if " T " in l)
@@ -128,6 +128,19 @@ def test_validation_codes_before_any_device_access():
     assert ne(_A16, 1000, _A16, _A16, _A16, _A16, ct.c_void_p(0x40004), wsb, None) == -3
     assert ne(_A16, 1000, _A16, None, _A16, _A16, _W8, wsb, None) == -1
     assert ne(_A16, 1000, ct.c_void_p(0x20002), _A16, _A16, _A16, _W8, wsb, None) == -3
+    qn = lib.quantize_4bit_nested_bf16
+    qwb = lib.kbit_quantize_nested_workspace_bytes()
+    assert qwb == 512 * 25 * 4                                    # one record per quantize workgroup
+    assert qn(None, None, None, None, None, None, None, None, 0, 64, None, 0, None) == 0   # empty: no-op
+    assert qn(_A16, _A16, _A16, _A16, _A16, _A16, _A16, _A16, 100, 48, _A16, qwb, None) == -2
+    assert qn(_A16, _A16, _A16, _A16, _A16, _A16, _A16, _A16, -1, 64, _A16, qwb, None) == -1
+    assert qn(_A16, _A16, _A16, _A16, _A16, _A16, _A16, _A16, 100, 64, None, qwb, None) == -1        # no workspace
+    assert qn(_A16, _A16, _A16, _A16, _A16, _A16, _A16, _A16, 100, 64, _A16, qwb - 1, None) == -1    # too small
+    assert qn(_A16, _A16, _A16, _A16, None, _A16, _A16, _A16, 100, 64, _A16, qwb, None) == -1        # no qmap2
+    assert qn(_A16, _A16, _A16, _A16, _A16, _A16, _A16, None, 100, 64, _A16, qwb, None) == -1        # no offset
+    assert qn(_A16, _A4, _A16, _A16, _A16, _A16, _A16, _A16, 100, 64, _A16, qwb, None) == -3         # A misaligned
+    assert qn(_A16, _A16, ct.c_void_p(0x20002), _A16, _A16, _A16, _A16, _A16, 100, 64, _A16, qwb, None) == -3
+    assert qn(_A16, _A16, _A16, _A16, _A16, _A16, _A16, _A16, 100, 64, ct.c_void_p(0x40002), qwb, None) == -3
     na = lib.quantize_nested_absmax_noalloc
     assert lib.kbit_nested_noalloc_scratch_bytes() >= lib.kbit_nested_workspace_bytes(1 << 36)
     assert na(None, 0, None, None, None, None, None) == 0                           # empty: no-op

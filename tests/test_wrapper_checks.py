@@ -90,6 +90,18 @@ def test_nested_encode():
     bad(ValueError, "offset", kb.quantize_nested_absmax_noalloc, a, z(256, f32), z(nb, u8), z(4, f32), z(0, f32))
 
 
+def test_quantize_4bit_nested():
+    A, q = z(N, bf16), z(256, f32)
+    placement_only(kb.quantize_4bit_nested, A, z(16, f32), q, B)
+    bad(ValueError, "codebook16", kb.quantize_4bit_nested, A, z(8, f32), q, B)
+    bad(ValueError, "qmap2", kb.quantize_4bit_nested, A, z(16, f32), z(255, f32), B)
+    bad(ValueError, "absmax", kb.quantize_4bit_nested, A, z(16, f32), q, B, absmax=z(NB - 1, f32))
+    bad(TypeError, "packed", kb.quantize_4bit_nested, A, z(16, f32), q, B, packed=z(NW, f32))
+    bad(ValueError, "absmax_code", kb.quantize_4bit_nested, A, z(16, f32), q, B, absmax_code=z(NB - 1, u8))
+    bad(ValueError, "workspace", kb.quantize_4bit_nested, A, z(16, f32), q, B, workspace=z(8, u8))
+    bad(TypeError, "element", kb.quantize_4bit_nested, z(N, torch.int16), z(16, f32), q, B)
+
+
 def test_linear_4bit():
     M, Kd, Nn = 4, 128, 64
     X = z(M * Kd, bf16).view(M, Kd)
