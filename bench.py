@@ -72,6 +72,16 @@ def kernel_bytes(n):
         # nested-state encoder: absmax read twice (the mean comes first),
         # codes, group absmax, offset and the map
         "quantize_nested_absmax": 8 * nb + nb + 4 * (-(-nb // GROUP2)) + 4 + 4 * 256,
+        # the encoder's two launches: the absmax read for the sums (records
+        # of 100 bytes per workgroup aside), then read again for the codes
+        "nested_bins_kernel": 4 * nb,
+        "nested_encode_kernel": 4 * nb + nb + 4 * (-(-nb // GROUP2)) + 4 + 4 * 256,
+        # quantize_4bit_nested_bf16's two kernels: the quantize variant (the
+        # plain kernel's bytes; its records are a few tens of KB) and the
+        # encoder's second launch (absmax read once, codes, group absmax,
+        # offset, map)
+        "quantize_kbit_bf16_k4 (nested sums)": 2 * n + planes + 4 * nb + tables,
+        "nested_encode_kernel (512 records)": 4 * nb + nb + 4 * (-(-nb // GROUP2)) + 4 + 4 * 256,
     }
 
 
@@ -133,6 +143,10 @@ KERNELS = {
     # the nested-state encoder's two launches
     "nested_bins_kernel": (("::nested_bins_kernel",), _E_SRC),
     "nested_encode_kernel": (("::nested_encode_kernel<8>",), _E_SRC),
+    # quantize_4bit_nested_bf16's two launches
+    "quantize_kbit_bf16_k4 (nested sums)": (("::quantize_kernel<kbit::Bf16,", "F32Scale, 4,", ", true>"),
+                                            _Q_SRC),
+    "nested_encode_kernel (512 records)": (("::nested_encode_kernel<16>",), _E_SRC),
 }
 
 
@@ -267,7 +281,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
     header = ["# rocprofv3 summary: k-bit quantize / dequantize kernels, 8192x8192 bf16, NF4, blocksize 64", "",
               "The bench step is quantize_kbit_bf16_k4 + dequantize_4bit_nested_bf16; the E4M4-scale pair, "
               "the plain fp32-scale dequantize and the nested-state encoder (quantize_nested_absmax: "
-              "nested_bins_kernel + nested_encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements."]
+              "nested_bins_kernel + nested_encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements, "
+              "and so does quantize_4bit_nested_bf16 (the quantize kernel's nested-sums variant + "
+              "nested_encode_kernel over its 512 records)."]
     return _summarize_into(table, trace_dir, fetch_dir, write_dir, header, PROFILE_COMMANDS,
                            "kbit_kernels_8192sq_bf16_nf4_b64.md",
                            timed_last={"quantize_kbit_bf16_k4": PROFILE_ROUND_LAUNCHES,
@@ -1007,9 +1023,18 @@ def main(argv=None):
     enc["note"] = ("nested-state encoder on the 1,048,576 fp32 block absmax of the same tensor: two launches "
                    "(exact significand sums; mean and codes); elements_per_s counts blocks")
 
+    # Quantize straight to the nested state (quantize_4bit_nested_bf16, two
+    # kernels) against quantize then quantize_nested_absmax (three), whole
+    # calls in a round robin of their own.
+    qnest = {"8192x8192": bench_quantize_nested(torch, kb, sets, cb, qmap, n, reps, round_robin, kstats),
+             "note": ("bf16 NF4 B=64 to the nested state (codes, absmax2, offset): quantize_4bit_nested_bf16 "
+                      "(two kernels; the quantize kernel also sums its block maxima exactly) against "
+                      "quantize_kbit_bf16_k4 then quantize_nested_absmax (three kernels); per call, "
+                      "bit-identical results")}
+
     # The same two kernels with the FP4 codebook, and warm numbers (one
     # buffer set over and over, so the last-level cache holds most of it).
-    fp4 = warm = act = act_block = lin = sweep = cells = qnest = None
+    fp4 = warm = act = act_block = lin = sweep = cells = None
     if not args.headline_only:
         pair = {"quantize_kbit_bf16_k4": quant_only, "dequantize_4bit_nested_bf16": nested_only}
         cb_nf = cb
@@ -1030,10 +1055,7 @@ def main(argv=None):
                 one = bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp)
                 one["prepared_tables"] = bench_act(torch, kb, synth, dev, reps, rows=r, d=dd, perm=pp, tables=True)
                 act_block.append(one)
-        # Quantize straight to the nested state (the sums inside quantize)
-        # against quantize followed by the encoder, as whole calls, on this
-        # weight and on a 4096x4096 one.
-        qnest = {"8192x8192": bench_quantize_nested(torch, kb, sets, cb, qmap, n, reps, round_robin, kstats)}
+        # The same comparison on a 4096x4096 weight.
         small = synth.weight(4096, 4096, "bf16", seed=synth.SEED_WEIGHT_SHAPES)
         n_s = small.size
         nb_s = -(-n_s // BLOCK)
@@ -1049,10 +1071,6 @@ def main(argv=None):
                                       device=dev)} for i in range(args.sets)]
         qnest["4096x4096"] = bench_quantize_nested(torch, kb, sets_s, cb, qmap, n_s, reps, round_robin, kstats)
         del sets_s, x_s
-        qnest["note"] = ("bf16 NF4 B=64 to the nested state (codes, absmax2, offset): quantize_4bit_nested_bf16 "
-                         "(two kernels; the quantize kernel also sums its block maxima exactly) against "
-                         "quantize_kbit_bf16_k4 then quantize_nested_absmax (three kernels); per call, "
-                         "bit-identical results")
         lin = bench_linear(torch, kb, synth, dev)
         sweep = bench_sweep(torch, kb, dev, reps)
         cells = bench_nested_cells(torch, kb, dev, max(4, reps // 2))

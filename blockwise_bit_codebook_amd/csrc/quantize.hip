@@ -67,11 +67,12 @@
 //     waits for each row's own loads only.  The first ring loads go out
 //     before the table build.
 //   * A variant (K = 4, fp32 absmax) also sums the block maxima exactly for
-//     the nested state's mean: each maximum's integer significand goes into
-//     the workgroup's LDS bin of its exponent (one 64-bit LDS atomic by the
-//     lane that holds it), and at the end the bins are folded into 32-bit
-//     digits and stored as the workgroup's record (nested_sums.h), so that
-//     the encoder's second launch can follow directly.
+//     the nested state's mean: each wave stages its maxima in LDS and empties
+//     a full stage into the workgroup's bins by exponent (64-bit LDS
+//     atomics of the integer significands); at the end the bins are folded
+//     into 32-bit digits and stored as the workgroup's record
+//     (nested_sums.h), so that the encoder's second launch can follow
+//     directly.
 #include "device.h"
 #include "e4m4.h"
 #include "kbit_internal.h"
@@ -326,13 +327,26 @@ template <class E>
 constexpr int kRing = E::kVec == 1 ? 4 : 2;
 
 // LDS of the variant that also sums the block maxima exactly for the
-// nested state's mean (nested_sums.h): each maximum's integer significand
-// goes into the workgroup's bin of its exponent (one LDS atomic), and the
-// bins are folded into the record at the end.  Only that variant's kernels
-// reference it, so only they allocate it.
+// nested state's mean (nested_sums.h).  Each wave stages its maxima (one
+// LDS write per row by the lanes that hold them); a full stage is emptied
+// into bins by exponent, each lane adding the integer significands of 4
+// staged values with 64-bit LDS atomics (lane l into copy l mod 8 of the
+// bins, so that fewer lanes of one instruction meet at an address; each
+// copy is one bin longer than 256, so that copies of a bin sit in different
+// banks).  At the end the bins are folded into the workgroup's record.  The
+// maxima are magnitudes (sign bit 0), so one sign suffices.  Only that
+// variant's kernels reference this, so only they allocate it.
+constexpr int kBinCopies = 8;
+constexpr int kBinStride = 257;
 template <int WAVES>
-__device__ __forceinline__ SumsShared<WAVES>& quant_sums() {
-    __shared__ SumsShared<WAVES> s;
+struct QuantSums {
+    alignas(16) uint32_t stage[WAVES][256];  // read 16 bytes per lane
+    unsigned long long bins[kBinCopies * kBinStride];
+    SumsShared<WAVES> sh;
+};
+template <int WAVES>
+__device__ __forceinline__ QuantSums<WAVES>& quant_sums() {
+    __shared__ QuantSums<WAVES> s;
     return s;
 }
 
@@ -393,8 +407,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(SUMS ? 
     bool fast = codebook_is_sorted_unit(c);
     if (threadIdx.x == 0) T.fail = 0;
     if constexpr (SUMS) {
-        sums_clear<kWaves_, THREADS>(quant_sums<kWaves_>());
-        if (threadIdx.x == 0) quant_sums<kWaves_>().any_slow = 1;  // every value is in the bins
+        QuantSums<kWaves_>& qs = quant_sums<kWaves_>();
+        sums_clear<kWaves_, THREADS>(qs.sh);
+        for (int i = threadIdx.x; i < kBinCopies * kBinStride; i += THREADS) qs.bins[i] = 0;
+        if (threadIdx.x == 0) qs.sh.any_slow = 1;  // every value goes through the bins
     }
     if (threadIdx.x < C) T.code[threadIdx.x] = c[threadIdx.x];
     // One wave per threshold, or one half-wave where there are more
@@ -430,23 +446,41 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(SUMS ? 
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kCopies - 1)) * 16u;
     const char* tab = reinterpret_cast<const char*>(T.row);
 
-    // SUMS: the block maxima of the wave (lane i * lpb holds block i's, 64 /
-    // lpb of them) into the workgroup's exponent bins; NaN and infinities
-    // only set flags, zeros add nothing.  A workgroup takes below 2^28
-    // maxima (n <= 2^40 spread over at least 256 workgroups, or at most one
-    // wave row per wave), so a bin stays below 2^52.
+    // SUMS: the wave's block maxima are staged (staged is wave-uniform;
+    // entries past it count as 0) and emptied into the bins; NaN and
+    // infinities only set flags, zeros add nothing.  A workgroup takes
+    // below 2^28 maxima (n <= 2^40 spread over at least 256 workgroups, or
+    // at most one wave row per wave), so a bin stays below 2^52 and a sum
+    // over the copies below 2^55.  Pushes and flushes run in uniform
+    // control flow; each flush point keeps the stage within its 256
+    // entries until the next.
     uint32_t sum_flags = 0;
+    int staged = 0;
+    auto sums_flush = [&]() {
+        if constexpr (SUMS) {
+            QuantSums<kWaves_>& qs = quant_sums<kWaves_>();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const u32x4 u = *reinterpret_cast<const u32x4*>(&qs.stage[wave][lane * 4]);
+            unsigned long long* bins = qs.bins + (lane & (kBinCopies - 1)) * kBinStride;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t x = lane * 4 + c < staged ? u[c] : 0u;  // a magnitude: sign bit 0
+                const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
+                sum_flags |= e == 0xFFu ? (f ? kFlagNan : kFlagPosInf) : 0u;
+                if (e != 0xFFu && x != 0) atomicAdd(bins + e, static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
+            }
+            staged = 0;
+        }
+    };
+    // the wave's maxima of blocks of `lpb` lanes each (lane i * lpb holds
+    // block i's), 64 / lpb of them
     auto sums_push = [&](float m, int lpb) {
         if constexpr (SUMS) {
-            const uint32_t x = __float_as_uint(m);
-            const uint32_t e = (x >> 23) & 0xFFu, f = x & 0x7FFFFFu;
-            if ((lane & (lpb - 1)) == 0) {
-                if (e == 0xFFu)
-                    sum_flags |= f ? kFlagNan : ((x >> 31) ? kFlagNegInf : kFlagPosInf);
-                else if ((x & 0x7FFFFFFFu) != 0)
-                    atomicAdd(&quant_sums<kWaves_>().bins[x >> 31][e],
-                              static_cast<unsigned long long>(e ? (f | 0x800000u) : f));
-            }
+            QuantSums<kWaves_>& qs = quant_sums<kWaves_>();
+            if ((lane & (lpb - 1)) == 0) qs.stage[wave][staged + lane / lpb] = __float_as_uint(m);
+            staged += kWave / lpb;
         }
     };
 
@@ -487,17 +521,26 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(SUMS ? 
         // operations outstanding from both sides and the compiler's wait
         // counts stay exact (a merge of differing states makes it wait for
         // nearly every load).
-        auto ring_pass = [&]() {
+        // SUMS: every row of a pass (past the end or not) stages
+        // kBlocksPerRow maxima, D * kBlocksPerRow per pass (a divisor of
+        // 256), so the stage is emptied once the pass's last row is staged if
+        // less room than that is left, i.e. exactly when it is full (before
+        // that slot is reloaded, so that its registers are free); the peeled
+        // first pass never fills it.
+        auto ring_pass = [&](bool may_flush) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
                 do_row(row[d], buf[d]);
                 row[d] += D * nwaves;
+                if constexpr (SUMS) {
+                    if (d == D - 1 && may_flush && staged > 256 - D * kBlocksPerRow) sums_flush();
+                }
                 load_full_row(row[d], buf[d]);
             }
         };
         if (row[0] < nfull) {
-            ring_pass();
-            while (row[0] < nfull) ring_pass();
+            ring_pass(false);
+            while (row[0] < nfull) ring_pass(true);
         }
         // The one partial row, if any, goes to the wave whose sequence
         // reaches it.
@@ -519,6 +562,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(SUMS ? 
         const int rows = 1 << (log2B - 9);
         const int64_t nblocks = (n + (1LL << log2B) - 1) >> log2B;
         for (int64_t b = vwave; b < nblocks; b += nwaves) {
+            if constexpr (SUMS) {
+                if (staged == 256) sums_flush();  // one maximum per block
+            }
             const int64_t base = b << log2B;
             float ml = 0.0f;
             for (int u = 0; u < rows; ++u) {
@@ -543,7 +589,20 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(SUMS ? 
             }
         }
     }
-    if constexpr (SUMS) sums_record<kWaves_, THREADS>(quant_sums<kWaves_>(), sum_flags, ws, gridDim.x, blockIdx.x);
+    if constexpr (SUMS) {
+        // the last staged maxima, the copies' totals into the positive bins,
+        // then the record
+        QuantSums<kWaves_>& qs = quant_sums<kWaves_>();
+        if (staged != 0) sums_flush();
+        __syncthreads();
+        for (int e = threadIdx.x; e < 256; e += THREADS) {
+            unsigned long long t = 0;
+#pragma unroll
+            for (int c = 0; c < kBinCopies; ++c) t += qs.bins[c * kBinStride + e];
+            qs.sh.bins[0][e] = t;
+        }
+        sums_record<kWaves_, THREADS>(qs.sh, sum_flags, ws, gridDim.x, blockIdx.x);
+    }
 }
 
 // Launch over a persistent grid: the resident workgroups of the device,
