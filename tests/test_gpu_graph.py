@@ -118,11 +118,14 @@ def test_graph_replays_other_types(dtype, K):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_graph_whole_chain_with_device_offset(dtype):
+@pytest.mark.parametrize("state", ["three_kernels", "quantize_to_nested"])
+def test_graph_whole_chain_with_device_offset(dtype, state):
     # quantize -> nested encode -> nested dequantize (offset read on the
     # device) and the fused linear on the same state, captured as one graph
     # with no host read-back; every replay equals the eager run, and the
-    # eager run equals the oracle's chain from the input alone
+    # eager run equals the oracle's chain from the input alone.  The state
+    # comes from quantize then quantize_nested_absmax, or from
+    # quantize_4bit_nested (two kernels).
     import torch
     from oracle import numerics
     from tests.test_gpu_dequantize import _tdt
@@ -142,16 +145,21 @@ def test_graph_whole_chain_with_device_offset(dtype):
     a2 = torch.empty(-(-nb // 256), dtype=torch.float32, device="cuda")
     off = torch.empty(1, dtype=torch.float32, device="cuda")
     ws = torch.empty(kb.lib().kbit_nested_workspace_bytes(nb), dtype=torch.uint8, device="cuda")
+    qws = torch.empty(kb.lib().kbit_quantize_nested_workspace_bytes(), dtype=torch.uint8, device="cuda")
     out = torch.empty(n, dtype=_tdt(dtype), device="cuda")
     y = torch.empty((16, rows), dtype=torch.bfloat16, device="cuda")
 
     def chain():
-        kb.quantize_kbit(A, cb, K, B, absmax=absmax, packed=packed)
-        kb.quantize_nested_absmax(absmax, qmap, absmax_code=code, absmax2=a2, offset=off, workspace=ws)
+        if state == "quantize_to_nested":
+            kb.quantize_4bit_nested(A, cb, qmap, B, absmax=absmax, packed=packed, absmax_code=code, absmax2=a2,
+                                    offset=off, workspace=qws)
+        else:
+            kb.quantize_kbit(A, cb, K, B, absmax=absmax, packed=packed)
+            kb.quantize_nested_absmax(absmax, qmap, absmax_code=code, absmax2=a2, offset=off, workspace=ws)
         kb.dequantize_4bit_nested(packed, cb, code, qmap, a2, off, n, _tdt(dtype), B, out=out)
         kb.linear_4bit(X, packed, cb, rows, B, absmax_code=code, qmap2=qmap, absmax2=a2, offset=off, out=y)
 
-    case(f"graph chain {dtype}: eager")
+    case(f"graph chain {dtype} {state}: eager")
     chain()
     torch.cuda.synchronize()
     ref = [bits(t) for t in (packed, absmax, code, a2, off, out, y)]
@@ -174,7 +182,7 @@ def test_graph_whole_chain_with_device_offset(dtype):
         chain()
     torch.cuda.synchronize()
     for r in range(4):
-        case(f"graph chain {dtype}: replay {r}")
+        case(f"graph chain {dtype} {state}: replay {r}")
         for t in (packed, absmax, code, a2, off, out, y):
             t.zero_()
         kb.quantize_kbit(A, cb, K, B)                       # unrelated eager work between replays

@@ -3,7 +3,8 @@ ragged length, magnitude and codebook kind (NF, random sorted, sorted with a
 repeated entry, unsorted) drawn per seed.  Quantize (words and absmax) and
 the dequantize of the kernel's own words are compared bit for bit with the
 oracle, with fp32 and with E4M4 block scales; the nested chain (quantize,
-nested-state encode, fused nested dequantize) and the activation
+nested-state encode, fused nested dequantize), quantize straight to the
+nested state (quantize_4bit_nested) and the activation
 assignment (random width, rows, codebook scale, permutation) likewise; the
 fused 4-bit linear (random M, N, K, blocksize) within its fp32-sum bound."""
 
@@ -107,6 +108,28 @@ def test_random_config_nested(seed):
     torch.cuda.synchronize()
     want = nested.dequantize_packed(want_w, wc, wa2, np.float32(woff), q, cb, n, B, dtype)
     assert_bits_equal(bits(out), np_bits(want), "nested dequantize")
+
+
+@pytest.mark.parametrize("seed", range(2100, 2124))
+def test_random_config_quantize_to_nested(seed):
+    # quantize_4bit_nested (the quantize kernel's exact sums, then the
+    # encoder's second launch) against the oracle run from the input alone
+    import torch
+    from oracle import nested
+    rng, dtype, _, B, n, kind, sigma = _config(seed)
+    cb = codebooks.nf(4) if kind in ("nf", "unsorted") else _codebook(rng, "sorted", 4)
+    q = codebooks.dynamic_map8()
+    x = synth.normal(n, seed=9000 + seed, dtype=dtype, sigma=sigma)
+    case(f"random config quantize to nested seed={seed} dtype={dtype} B={B} n={n} sigma={sigma:.3g}")
+    packed, absmax, code, a2, off = kb.quantize_4bit_nested(to_dev(x, dtype), to_dev(cb), to_dev(q), B)
+    torch.cuda.synchronize()
+    want_w, want_a = kbit.quantize_packed(numerics.widen(x, dtype), cb, 4, B)
+    assert_bits_equal(bits(packed), want_w, "words")
+    assert_bits_equal(bits(absmax), np_bits(want_a), "absmax")
+    wc, wa2, woff = nested.encode(want_a, q)
+    assert bits(off)[0] == np.float32(woff).view(np.uint32), "offset"
+    assert_bits_equal(bits(a2), np_bits(wa2), "absmax2")
+    assert_bits_equal(bits(code), wc, "codes")
 
 
 @pytest.mark.parametrize("seed", range(3000, 3040))
