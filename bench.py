@@ -81,7 +81,7 @@ def kernel_bytes(n):
         # encoder's second launch (absmax read once, codes, group absmax,
         # offset, map)
         "quantize_kbit_bf16_k4 (nested sums)": 2 * n + planes + 4 * nb + tables,
-        "nested_encode_kernel (512 records)": 4 * nb + nb + 4 * (-(-nb // GROUP2)) + 4 + 4 * 256,
+        "nested_encode_kernel (quantize records)": 4 * nb + nb + 4 * (-(-nb // GROUP2)) + 4 + 4 * 256,
     }
 
 
@@ -142,11 +142,11 @@ KERNELS = {
     "dequantize_kbit_bf16_k4": (("::dequantize_kernel<kbit::Bf16, 4,", "PlainScale>"), _D_SRC),
     # the nested-state encoder's two launches
     "nested_bins_kernel": (("::nested_bins_kernel",), _E_SRC),
-    "nested_encode_kernel": (("::nested_encode_kernel<8>",), _E_SRC),
+    "nested_encode_kernel": (("::nested_encode_kernel<8, false>",), _E_SRC),
     # quantize_4bit_nested_bf16's two launches
     "quantize_kbit_bf16_k4 (nested sums)": (("::quantize_kernel<kbit::Bf16,", "F32Scale, 4,", ", true>"),
                                             _Q_SRC),
-    "nested_encode_kernel (512 records)": (("::nested_encode_kernel<16>",), _E_SRC),
+    "nested_encode_kernel (quantize records)": (("::nested_encode_kernel<8, true>",), _E_SRC),
 }
 
 
@@ -283,7 +283,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
               "the plain fp32-scale dequantize and the nested-state encoder (quantize_nested_absmax: "
               "nested_bins_kernel + nested_encode_kernel, 1,048,576 blocks) run on the same tensor as side measurements, "
               "and so does quantize_4bit_nested_bf16 (the quantize kernel's nested-sums variant + "
-              "nested_encode_kernel over its 512 records)."]
+              "nested_encode_kernel over its 512 records of non-negative sums)."]
     return _summarize_into(table, trace_dir, fetch_dir, write_dir, header, PROFILE_COMMANDS,
                            "kbit_kernels_8192sq_bf16_nf4_b64.md",
                            timed_last={"quantize_kbit_bf16_k4": PROFILE_ROUND_LAUNCHES,

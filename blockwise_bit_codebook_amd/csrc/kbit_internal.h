@@ -36,8 +36,8 @@ int64_t nested_workspace_bytes(int64_t nb);
 int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
                          float* offset, void* workspace, void* stream);
 
-// The encoder's second launch alone, over `groups` records that a previous
-// launch on the stream stored (launch_quantize_sums).
+// The encoder's second launch alone, over `groups` records of non-negative
+// values that a previous launch on the stream stored (launch_quantize_sums).
 int launch_nested_encode_records(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code,
                                  float* absmax2, float* offset, const void* records, int groups, void* stream);
 int nested_record_words();

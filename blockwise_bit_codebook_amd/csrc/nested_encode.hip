@@ -105,17 +105,33 @@ __global__ __launch_bounds__(kBinThreads) void nested_bins_kernel(const float* _
     sums_record<kBinWaves, kBinThreads>(sh, my_flags, ws, gridDim.x, blockIdx.x);
 }
 
-// The records of launch 1 for the mean: half wave h of the workgroup
-// (kOffsetParts = 32 lanes) takes record word h (a digit of one sign, or
-// the flags) of every record, LOADS per lane (up to 32 * LOADS records),
-// widened to 64 bits; halves past the last word load nothing.
-template <int LOADS>
+// Which record words a workgroup of launch 2 reads: all 25, or, for
+// records of non-negative values only (POS: the quantize kernel's, whose
+// negative digits are zero), the 12 positive digits and the flags.  Each
+// word (slot) is read by PARTS half waves (kOffsetParts = 32 lanes), part p
+// taking records 32 p + lane, 32 (p + PARTS) + lane, ...: LOADS per lane
+// cover up to 32 * PARTS * LOADS records.
+template <bool POS>
+struct RecordPlan {
+    static constexpr int kSlots = POS ? kLimbWords + 1 : kRecordWords;
+    static constexpr int kParts = POS ? 2 : 1;
+    static constexpr int kFlagSlot = kSlots - 1;
+    __device__ static int word(int slot) { return POS && slot == kFlagSlot ? 2 * kLimbWords : slot; }
+};
+static_assert(RecordPlan<false>::kSlots * RecordPlan<false>::kParts * kOffsetParts <= kEncThreads &&
+                  RecordPlan<true>::kSlots * RecordPlan<true>::kParts * kOffsetParts <= kEncThreads,
+              "a half wave per part of a record word");
+
+template <int LOADS, bool POS>
 __device__ __forceinline__ void load_records(const uint32_t* __restrict__ ws, int groups, uint64_t (&v)[LOADS]) {
-    const int k = threadIdx.x / kOffsetParts, part = threadIdx.x % kOffsetParts;
+    using P = RecordPlan<POS>;
+    const int h = threadIdx.x / kOffsetParts, lane_h = threadIdx.x % kOffsetParts;
+    const int slot = h / P::kParts, part = h % P::kParts;
+    const int k = slot < P::kSlots ? P::word(slot) : -1;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-        const int g = part + j * kOffsetParts;
-        v[j] = (k < kRecordWords && g < groups) ? ws[static_cast<int64_t>(k) * groups + g] : 0;
+        const int g = lane_h + kOffsetParts * (part + P::kParts * j);
+        v[j] = (k >= 0 && g < groups) ? ws[static_cast<int64_t>(k) * groups + g] : 0;
     }
 }
 
@@ -125,12 +141,14 @@ __device__ __forceinline__ uint64_t dpp_or_u64(uint64_t v) {
 }
 
 // The mean offset from the loaded records: each half wave sums (ORs, for
-// the flags) its word; thread 0 rounds the mean from the limb totals (each
-// below 2^41: at most 512 digits below 2^32).  Every thread gets the offset
-// (through LDS).  All threads of the workgroup call it.
-template <int LOADS>
+// the flags) its part of a word; thread 0 adds the parts and rounds the
+// mean from the limb totals (each below 2^41: at most 512 digits below
+// 2^32).  Every thread gets the offset (through LDS).  All threads of the
+// workgroup call it.
+template <int LOADS, bool POS>
 __device__ inline float mean_offset(const uint64_t (&v)[LOADS], const NbDivider& div) {
-    __shared__ unsigned long long total[kRecordWords];
+    using P = RecordPlan<POS>;
+    __shared__ unsigned long long part_total[kEncThreads / kOffsetParts];
     __shared__ float off;
     uint64_t sum = 0, any = 0;
 #pragma unroll
@@ -153,16 +171,26 @@ __device__ inline float mean_offset(const uint64_t (&v)[LOADS], const NbDivider&
     // The read-outs stay in uniform control flow (a cross-lane read inside
     // a lane-0 branch lets the compiler move the sums' last step into that
     // branch, where the other lanes do not run it).
-    const int k0 = 2 * (threadIdx.x / kWave);  // word of the wave's first half; k0 + 1 is odd: never the flags
-    const uint64_t t0 = k0 == 2 * kLimbWords ? (row(any, 0) | row(any, 16)) : row(sum, 0) + row(sum, 16);
-    const uint64_t t1 = row(sum, 32) + row(sum, 48);
+    const int h0 = 2 * (threadIdx.x / kWave);  // the wave's first half; h0 + 1 its second
+    const bool fl0 = h0 / P::kParts == P::kFlagSlot, fl1 = (h0 + 1) / P::kParts == P::kFlagSlot;
+    const uint64_t t0 = fl0 ? (row(any, 0) | row(any, 16)) : row(sum, 0) + row(sum, 16);
+    const uint64_t t1 = fl1 ? (row(any, 32) | row(any, 48)) : row(sum, 32) + row(sum, 48);
     if (__lane_id() == 0) {
-        if (k0 < kRecordWords) total[k0] = t0;
-        if (k0 + 1 < kRecordWords) total[k0 + 1] = t1;
+        part_total[h0] = t0;
+        part_total[h0 + 1] = t1;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t fl = static_cast<uint32_t>(total[2 * kLimbWords]);
+        const auto slot_total = [](int slot) {
+            uint64_t t = 0;
+#pragma unroll
+            for (int p = 0; p < P::kParts; ++p) {
+                const uint64_t x = part_total[slot * P::kParts + p];
+                t = slot == P::kFlagSlot ? (t | x) : t + x;
+            }
+            return t;
+        };
+        const uint32_t fl = static_cast<uint32_t>(slot_total(P::kFlagSlot));
         uint32_t bits;
         if ((fl & kFlagNan) || ((fl & kFlagPosInf) && (fl & kFlagNegInf))) {
             bits = 0x7FC00000u;
@@ -174,8 +202,8 @@ __device__ inline float mean_offset(const uint64_t (&v)[LOADS], const NbDivider&
             uint64_t pos[kLimbWords], neg[kLimbWords];
 #pragma unroll
             for (int i = 0; i < kLimbWords; ++i) {
-                pos[i] = total[i];
-                neg[i] = total[kLimbWords + i];
+                pos[i] = slot_total(i);
+                neg[i] = POS ? 0 : slot_total(kLimbWords + i);
             }
             bits = mean_from_limbs(pos, neg, div);
         }
@@ -302,9 +330,8 @@ __device__ __forceinline__ void load_group(const float* __restrict__ a, int64_t 
     }
 }
 
-// LOADS: records per lane of the mean's half waves (up to 32 * LOADS
-// records in ws).
-template <int LOADS>
+// LOADS, POS: which records the mean reads, and how (RecordPlan).
+template <int LOADS, bool POS>
 __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float* __restrict__ a, int64_t nb,
                                                                     const float* __restrict__ qmap2,
                                                                     const uint32_t* __restrict__ ws, int groups,
@@ -314,7 +341,7 @@ __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float*
     __shared__ float c[256];
     __shared__ int unsorted;
     uint64_t rec[LOADS];
-    load_records(ws, groups, rec);  // first: the mean waits on these
+    load_records<LOADS, POS>(ws, groups, rec);  // first: the mean waits on these
     if (threadIdx.x == 0) unsorted = 0;
     __syncthreads();
     if (threadIdx.x < 256) {
@@ -339,7 +366,7 @@ __global__ __launch_bounds__(kEncThreads) void nested_encode_kernel(const float*
 #pragma unroll
     for (int t = 0; t < 15; ++t) sep[t] = qmap2[16 * t + 15];
     GroupRange range = group_range(x, g * kGroup2 + lane * 4, nb);
-    const float offset = mean_offset(rec, div);  // has barriers: c[] and unsorted are set
+    const float offset = mean_offset<LOADS, POS>(rec, div);  // has barriers: c[] and unsorted are set
     const bool sorted = unsorted == 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) *offset_out = offset;
     for (; g < ngroups; g += step) {
@@ -386,14 +413,15 @@ int64_t nested_workspace_bytes(int64_t nb) {
 }
 
 namespace {
-// Launch 2 over `groups` records (LOADS = records per lane of the mean).
-template <int LOADS>
+// Launch 2 over `groups` records (LOADS, POS: RecordPlan).
+template <int LOADS, bool POS>
 void launch_encode(const float* absmax, int64_t nb, const float* qmap2, uint8_t* code, float* absmax2,
                    float* offset, const uint32_t* ws, int groups, hipStream_t st) {
     const int64_t ngroups = (nb + kGroup2 - 1) / kGroup2;
     const int64_t want = (ngroups + kEncWaves - 1) / kEncWaves;
     const int64_t grid = want < kEncMaxGrid ? want : kEncMaxGrid;
-    hipLaunchKernelGGL(nested_encode_kernel<LOADS>, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st,
+    auto kern = nested_encode_kernel<LOADS, POS>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kEncThreads), 0, st,
                        absmax, nb, qmap2, ws, groups, offset, code, absmax2,
                        make_nb_divider(static_cast<uint64_t>(nb)));
 }
@@ -405,7 +433,7 @@ int launch_nested_encode(const float* absmax, int64_t nb, const float* qmap2, ui
     const int groups = bin_groups(nb);
     uint32_t* ws = static_cast<uint32_t*>(workspace);
     hipLaunchKernelGGL(nested_bins_kernel, dim3(groups), dim3(kBinThreads), 0, st, absmax, nb, ws);
-    launch_encode<kMaxBinGroups / kOffsetParts>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
+    launch_encode<kMaxBinGroups / kOffsetParts, false>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
     return static_cast<int>(hipGetLastError());
 }
 
@@ -413,10 +441,9 @@ int launch_nested_encode_records(const float* absmax, int64_t nb, const float* q
                                  float* absmax2, float* offset, const void* records, int groups, void* stream) {
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const uint32_t* ws = static_cast<const uint32_t*>(records);
-    if (groups <= kMaxBinGroups)
-        launch_encode<kMaxBinGroups / kOffsetParts>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
-    else
-        launch_encode<kMaxSumGroups / kOffsetParts>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
+    // the quantize kernel's records: block maxima, never negative
+    constexpr int kLoads = kMaxSumGroups / (kOffsetParts * RecordPlan<true>::kParts);
+    launch_encode<kLoads, true>(absmax, nb, qmap2, code, absmax2, offset, ws, groups, st);
     return static_cast<int>(hipGetLastError());
 }
 
