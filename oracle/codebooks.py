@@ -38,8 +38,8 @@ All values are computed in float64 and rounded once to float32.
     quantization (Dettmers et al., "8-bit Optimizers via Block-wise
     Quantization", 2021): a sign, a decimal exponent 10^-z coded by z leading
     zero bits, then a linear fraction in (0.1, 1) taken at the midpoints of
-    2^(6-z) equal slots; plus 0 and 1.  Parity unpinned for the individual
-    values (the GPU path only reads the map as data); its structure is pinned.
+    2^(6-z) equal slots; plus 0 and 1.  Pinned against a bit-by-bit decoding
+    of the 256 codes in exact rationals (the GPU path reads the map as data).
 """
 
 import math

@@ -123,3 +123,45 @@ def test_dynamic_map_structure():
     for z in range(7):                                  # 2^(6-z) levels per decade
         lo, hi = 10.0 ** (-z - 1), 10.0 ** (-z)
         assert np.count_nonzero((pos > lo) & (pos < hi)) == 1 << (6 - z)
+
+
+def _decode_dynamic_code(c):
+    """Value of one 8-bit dynamic-tree code, read bit by bit.
+
+    Bit 7 is the sign.  Of the other seven bits, the leading zeros count the
+    decimal exponent z (value scale 10^-z), the first one bit marks where the
+    fraction starts, and the 6 - z bits after it index one of 2^(6-z) equal
+    slots of the linear fraction range (0.1, 1); the slot's midpoint is taken.
+    Seven zero bits code 0.  Returns an exact Fraction.
+    """
+    sign = -1 if c & 0x80 else 1
+    m = c & 0x7F
+    if m == 0:
+        return Fraction(0)
+    z = 7 - m.bit_length()                  # leading zeros of the 7-bit field
+    nbits = 6 - z                           # fraction bits after the marker
+    f = m & ((1 << nbits) - 1)
+    slot = Fraction(9, 10) / (1 << nbits)
+    frac_part = Fraction(1, 10) + slot * f + slot / 2
+    return sign * frac_part / Fraction(10) ** z
+
+
+def test_dynamic_map_matches_bitwise_decoding():
+    """Every entry equals a code of the published dynamic-tree layout, decoded
+    bit by bit and rounded once to fp32 by exact rational arithmetic; the
+    code with sign bit set and zero magnitude (a second zero) stands for +1.
+    """
+    want = set()
+    for c in range(256):
+        if c == 0x80:
+            want.add(1.0)
+            continue
+        want.add(exact.f32(_decode_dynamic_code(c)))
+    q = codebooks.dynamic_map8()
+    assert len(want) == 256
+    assert sorted(want) == [float(v) for v in q]
+    # hand-derived landmarks: the finest level 10^-6 * 0.55, the coarsest
+    # slot midpoint below 1, 0.1 + 0.9 * 63.5 / 64 = 1271/1280
+    assert float(q[127]) == 0.0
+    assert float(q[128]) == exact.f32(Fraction(55, 10 ** 8))
+    assert float(q[254]) == exact.f32(Fraction(1271, 1280))
