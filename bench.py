@@ -48,6 +48,7 @@ BLOCK = 64
 K = 4
 GROUP2 = 256
 KERNEL_ROUNDS_MIN = 50  # rounds of back-to-back launches per step kernel for its launch duration
+ROUND_PASSES = 4        # passes over the rotated buffer sets inside one round (one event pair)
 
 
 def algorithmic_bytes(n):
@@ -155,7 +156,7 @@ def _matches(pat, name):
 PROFILE_STEPS = 200  # --steps of the trace command below
 PROFILE_SETS = 4     # its --sets (the default)
 # launches of each step kernel in the rounds after its timed steps
-PROFILE_ROUND_LAUNCHES = max(KERNEL_ROUNDS_MIN, PROFILE_STEPS // PROFILE_SETS) * PROFILE_SETS
+PROFILE_ROUND_LAUNCHES = max(KERNEL_ROUNDS_MIN, PROFILE_STEPS // PROFILE_SETS) * PROFILE_SETS * ROUND_PASSES
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o trace -- "
@@ -1082,7 +1083,10 @@ def main(argv=None):
     # step by 1-2.5 us (measured), so the per-kernel launch durations of the
     # roofline come from the rounds right after the timed region: each step
     # kernel alone, back to back over the rotated buffer sets, with an event
-    # at each round's ends (max(KERNEL_ROUNDS_MIN, steps / sets) rounds).
+    # at each round's ends (max(KERNEL_ROUNDS_MIN, steps / sets) rounds of
+    # ROUND_PASSES passes over the sets: an event costs about 1-2.5 us of GPU
+    # time inside back-to-back work, which a round of one pass, 4 launches,
+    # put at about 0.8 us on each launch's figure).
     # The events are created without the system-scope fence
     # (hipEventDisableSystemFence): default events add a cache flush per
     # record.  All launches call the two C entry points directly (qfn,
@@ -1118,13 +1122,14 @@ def main(argv=None):
         code = 0
         hev.record(rm[0])
         for r in range(rounds):
-            for a in argsets:
-                code |= fn(*a)
+            for _ in range(ROUND_PASSES):
+                for a in argsets:
+                    code |= fn(*a)
             hev.record(rm[r + 1])
         torch.cuda.synchronize()
         if code:
             raise RuntimeError(f"a timed launch failed: {kb.lib().kbit_strerror(code)}")
-        ts = [hev.elapsed_ms(rm[r], rm[r + 1]) / len(argsets) for r in range(rounds)]
+        ts = [hev.elapsed_ms(rm[r], rm[r + 1]) / (ROUND_PASSES * len(argsets)) for r in range(rounds)]
         hev.destroy(rm)
         return ts
 
