@@ -143,35 +143,76 @@ __device__ __forceinline__ void decode_tile(const TileIn<K, Scale>& in, float s,
     }
 }
 
+// The wave's first full step of U wave tiles (step blockIdx.x * waves +
+// wave), loaded before the kernel stages its tables in LDS, so that the
+// latency of these loads overlaps that of the table loads and the barrier.
+template <int K, class Scale, int U>
+struct FirstStep {
+    TileIn<K, Scale> in[U];
+};
+
+// a step's U tiles (2048 elements) lie in one group of 256 blocks (B >= 8)
+template <int U>
+__device__ __forceinline__ int64_t step_group(int64_t step, int log2B) {
+    return (step * U * kWaveTile) >> (log2B + 8);
+}
+
+// The loads are unconditional (a branch around them would make the
+// compiler wait for all of them at the barrier): a wave without a full step
+// reads group 0's words and block 0's scale inputs, which exist for every
+// n >= 1, and never uses them.
+template <int K, class Scale, int U>
+__device__ __forceinline__ void dequant_prefetch(const uint32_t* __restrict__ packed, const Scale& scale, int64_t n,
+                                                 int log2B, FirstStep<K, Scale, U>& first) {
+    const int lane = __lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nfull = n / (static_cast<int64_t>(kWaveTile) * U);
+    const int64_t st = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave;
+    const bool live = st < nfull;  // wave-uniform
+    const int64_t g0 = live ? step_group<U>(st, log2B) : 0;
+    const int l = lane & 3;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t base = (st * U + u) * kWaveTile;
+        const int64_t g = live ? base / kGroup + (lane >> 2) : 0;
+        const int64_t e0 = live ? base + static_cast<int64_t>(lane) * kElemsPerLane : 0;
+        TileIn<K, Scale>& in = first.in[u];
+        // lanes l >= K (K < 4) read their group's last word and keep 0
+        const uint32_t w = packed[g * K + (K >= 4 ? l : min(l, K - 1))];
+        in.w = (K >= 4 || l < K) ? w : 0u;
+        if constexpr (K == 5) in.w4 = packed[g * K + 4];  // lane 0 of the quad's is used
+        in.sc = scale.load(e0 >> log2B, g0);
+    }
+}
+
 // Steps of U wave tiles: the step's plane words and scale inputs are loaded
 // together, the next step's loads are issued before this step's stores, and
 // full steps run without branches (so the store queue never has to drain
 // before the next loads are used).  Remaining tiles go one at a time.
+// `first` holds the wave's first step (dequant_prefetch).
 template <class E, int K, class Scale, int U, bool NTS>
 __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packed, const float* cb_lds,
                                               const float2* pair_lds, const Scale& scale,
-                                              typename E::storage* __restrict__ out, int64_t n, int log2B) {
+                                              typename E::storage* __restrict__ out, int64_t n, int log2B,
+                                              const FirstStep<K, Scale, U>& first) {
     const int lane = __lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kWavesPerGroup;
     const int64_t nfull = n / (static_cast<int64_t>(kWaveTile) * U);  // full steps
     int64_t st = static_cast<int64_t>(blockIdx.x) * kWavesPerGroup + wave;
-    // a step's U tiles (2048 elements) lie in one group of 256 blocks (B >= 8)
-    auto step_group = [&](int64_t step) { return (step * U * kWaveTile) >> (log2B + 8); };
     // Each step's block scales are built right after the previous step's
     // stores go out, so that their lookups (the nested map in LDS) are off
     // the next step's critical path.
     if (st < nfull) {
         TileIn<K, Scale> cur[U];
         float cs[U];
-        const int64_t g0 = step_group(st);
 #pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = load_tile<K, Scale, true>(packed, scale, st * U + u, g0, n, log2B, lane);
+        for (int u = 0; u < U; ++u) cur[u] = first.in[u];
 #pragma unroll
         for (int u = 0; u < U; ++u) cs[u] = scale.finish(cur[u].sc);
         for (; st < nfull; st += nwaves) {
             const int64_t sn = min(st + nwaves, nfull - 1);
-            const int64_t gn = step_group(sn);
+            const int64_t gn = step_group<U>(sn, log2B);
             TileIn<K, Scale> nxt[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) nxt[u] = load_tile<K, Scale, true>(packed, scale, sn * U + u, gn, n, log2B, lane);
@@ -195,16 +236,31 @@ __device__ __forceinline__ void dequant_tiles(const uint32_t* __restrict__ packe
     }
 }
 
-// Stages the codebook (and the pair table for K <= 4) in LDS.
+// The codebook (and the pair table for K <= 4) for LDS, in two steps so that
+// the loads go out first: load_codebook reads this thread's entries,
+// store_codebook writes them.
+struct CbEntries {
+    float c = 0.0f;
+    float2 pair = {0.0f, 0.0f};
+};
 template <int K>
-__device__ __forceinline__ void stage_codebook(const float* __restrict__ cb, float* cb_lds, float2* pair_lds) {
+__device__ __forceinline__ CbEntries load_codebook(const float* __restrict__ cb) {
     constexpr int C = 1 << K;
     const int tid = threadIdx.x;
-    if (tid < C) cb_lds[tid] = cb[tid];
+    CbEntries e;
+    if (tid < C) e.c = cb[tid];
     if constexpr (K <= 4) {
         // a pair byte (planes_to_pairs); indices >= 2^K never occur
-        pair_lds[tid] = make_float2(cb[pair_index(tid, 0) & (C - 1)], cb[pair_index(tid, 1) & (C - 1)]);
+        e.pair = make_float2(cb[pair_index(tid, 0) & (C - 1)], cb[pair_index(tid, 1) & (C - 1)]);
     }
+    return e;
+}
+template <int K>
+__device__ __forceinline__ void store_codebook(const CbEntries& e, float* cb_lds, float2* pair_lds) {
+    constexpr int C = 1 << K;
+    const int tid = threadIdx.x;
+    if (tid < C) cb_lds[tid] = e.c;
+    if constexpr (K <= 4) pair_lds[tid] = e.pair;
 }
 
 constexpr int kSteps = 4;      // wave tiles per step
@@ -217,9 +273,14 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint32_t* __
                                                               int log2B) {
     __shared__ float cb_lds[32];
     __shared__ float2 pair_lds[256];
-    stage_codebook<K>(cb, cb_lds, pair_lds);
+    // the table loads first, then the first step's: the barrier waits for
+    // the former only
+    const CbEntries ce = load_codebook<K>(cb);
+    FirstStep<K, Scale, kSteps> first;
+    dequant_prefetch<K, Scale, kSteps>(packed, scale, n, log2B, first);
+    store_codebook<K>(ce, cb_lds, pair_lds);
     __syncthreads();
-    dequant_tiles<E, K, Scale, kSteps, kNtStore>(packed, cb_lds, pair_lds, scale, out, n, log2B);
+    dequant_tiles<E, K, Scale, kSteps, kNtStore>(packed, cb_lds, pair_lds, scale, out, n, log2B, first);
 }
 
 template <class E, int U = kSteps, bool NTS = kNtStore>
@@ -230,19 +291,25 @@ __global__ __launch_bounds__(kThreads) void dequantize_nested_kernel(
     __shared__ float cb_lds[32];
     __shared__ float2 pair_lds[256];
     __shared__ float qmap_lds[256];
-    // the offset from device memory when given (a uniform load, in flight
-    // with the table staging), else the argument
-    if (offset_ptr != nullptr) offset = *offset_ptr;
-    stage_codebook<4>(cb, cb_lds, pair_lds);
-    qmap_lds[threadIdx.x] = qmap2[threadIdx.x];
-    __syncthreads();
     // buffer descriptor over the ceil(ceil(n / B) / 256) group scales
     const int64_t ng = (((n + (int64_t(1) << log2B) - 1) >> log2B) + 255) >> 8;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(absmax2), 0, static_cast<int>(ng * 4), 0x00020000);
+    // the table loads first, then the first step's: the barrier waits for
+    // the former only
+    const CbEntries ce = load_codebook<4>(cb);
+    const float qv = qmap2[threadIdx.x];
+    FirstStep<4, NestedScale, U> first;
+    dequant_prefetch<4, NestedScale, U>(packed, NestedScale{code, absmax2, offset, qmap_lds, rsrc}, n, log2B, first);
+    // the offset from device memory when given (a uniform load, in flight
+    // with the table staging), else the argument
+    if (offset_ptr != nullptr) offset = *offset_ptr;
+    store_codebook<4>(ce, cb_lds, pair_lds);
+    qmap_lds[threadIdx.x] = qv;
+    __syncthreads();
     dequant_tiles<E, 4, NestedScale, U, NTS>(packed, cb_lds, pair_lds,
                                                         NestedScale{code, absmax2, offset, qmap_lds, rsrc}, out, n,
-                                                        log2B);
+                                                        log2B, first);
 }
 
 template <class E, int K, class Scale>
