@@ -192,10 +192,30 @@ __device__ __forceinline__ void store_act_tables(const ActTables& T, const ActPl
 // Fills T's bank-spread rows and codebook from the prepared form and
 // returns the plan.  Every thread of the workgroup calls it; a workgroup
 // barrier must separate it from the first use of T.
+// Every load goes out before the first LDS write, so that the copy costs one
+// load latency: item i (of kBuckets * 4) is bucket i / 4's entry, which its
+// thread writes to copies 4(i % 4) .. 4(i % 4) + 3.  A thread takes items
+// threadIdx.x and threadIdx.x + nthreads (nthreads >= 256 covers all of
+// them; the loop after it takes any left for smaller groups).
 __device__ __forceinline__ ActPlan load_act_tables(ActTables& T, const u32x4* __restrict__ prep, int nthreads) {
-    for (int i = threadIdx.x; i < kBuckets * kCopies; i += nthreads) T.row[i] = prep[i / kCopies];
-    if (threadIdx.x < 16) T.code[threadIdx.x] = __uint_as_float(prep[kBuckets + 1 + threadIdx.x / 4][threadIdx.x % 4]);
+    static_assert(kCopies == 16, "four copies per item");
+    constexpr int kItems = kBuckets * 4;
+    const int i0 = threadIdx.x, i1 = threadIdx.x + nthreads;
+    u32x4 e0 = {0u, 0u, 0u, 0u}, e1 = {0u, 0u, 0u, 0u};
+    if (i0 < kItems) e0 = prep[i0 >> 2];
+    if (i1 < kItems) e1 = prep[i1 >> 2];
+    const bool has_code = threadIdx.x < 16;
+    const uint32_t cw = has_code ? prep[kBuckets + 1 + threadIdx.x / 4][threadIdx.x % 4] : 0u;
     const u32x4 pl = prep[kBuckets];
+    auto put = [&](int i, const u32x4& e) {
+        u32x4* dst = T.row + (i >> 2) * kCopies + (i & 3) * 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[c] = e;
+    };
+    if (i0 < kItems) put(i0, e0);
+    if (i1 < kItems) put(i1, e1);
+    for (int i = threadIdx.x + 2 * nthreads; i < kItems; i += nthreads) put(i, prep[i >> 2]);
+    if (has_code) T.code[threadIdx.x] = __uint_as_float(cw);
     return ActPlan{pl[0] != 0u, __uint_as_float(pl[1])};
 }
 

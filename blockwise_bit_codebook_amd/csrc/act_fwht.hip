@@ -80,6 +80,8 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
             b = *reinterpret_cast<const uint4*>(xr + 8);
         }
     };
+    // the sign word goes out first, then the first row, then the tables
+    const uint32_t signs = (sign_bits[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
     uint4 cur_a, cur_b;
     load_raw(static_cast<int64_t>(blockIdx.x) * kSlots + slot, cur_a, cur_b);
 
@@ -96,7 +98,6 @@ __global__ __launch_bounds__(kRowThreads * kSlots) void act_fwht_kernel(const ui
 
     // Sign flips as XOR masks on the raw bf16 words: element 2i is the low
     // half of word i (sign bit 15), element 2i+1 the high half (bit 31).
-    const uint32_t signs = (sign_bits[t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
     uint32_t flip[kPer / 2];
 #pragma unroll
     for (int i = 0; i < kPer / 2; ++i)

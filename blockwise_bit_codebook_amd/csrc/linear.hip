@@ -152,14 +152,20 @@ __global__ __launch_bounds__(kLinThreads) void linear4_kernel(const uint16_t* __
         }
     };
 
+    // The table entries are loaded first and the first chunk after them, so
+    // that both latencies overlap; the LDS writes follow.
+    const int t = threadIdx.x;
+    float2 pair_e = make_float2(0.0f, 0.0f);
+    float qmap_e = 0.0f;
+    if (t < 256) {
+        pair_e = make_float2(cb[pair_index(t, 0)], cb[pair_index(t, 1)]);
+        if (qmap2) qmap_e = qmap2[t];
+    }
     C ca, cb2;
     if (s_begin < s_end) load_chunk(s_begin, 0, ca);
-    {
-        const int t = threadIdx.x;
-        if (t < 256) {
-            pair_lds[t] = make_float2(cb[pair_index(t, 0)], cb[pair_index(t, 1)]);
-            qmap_lds[t] = qmap2 ? qmap2[t] : 0.0f;
-        }
+    if (t < 256) {
+        pair_lds[t] = pair_e;
+        qmap_lds[t] = qmap_e;
     }
     __syncthreads();
 
